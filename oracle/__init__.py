@@ -1,0 +1,125 @@
+"""fp64 CPU oracle of the selective-scan forward pass (wrapper over ``scan_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU-baseline leg may use
+it; the product path never does. It shares no code with the HIP library. Which passage of the
+pages each step follows is stated in ``scan_oracle.c``.
+
+Every function of the oracle is pinned by CPU tests against things other than itself
+(brute-force sums, a closed form, the delta -> 0 limit, hand-computed L=1/L=2 cases, scipy's
+``lfilter`` and numpy's ``cumsum`` special cases, invariants, and the pages' own einsum loop run
+in torch fp64). One reading is not pinned by any page value: the exp branch taken when
+``delta_softplus`` is false ("parity unpinned" beyond the text of the page that defines it).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "scan_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True, source: str = SOURCE, out: str = _LIB) -> str:
+    """Compile the oracle with plain gcc: -O2, no fast-math, host libm."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", tmp, source, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, out)
+    return out
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    f = lib.oracle_selective_scan
+    f.restype = ctypes.c_int
+    P = ctypes.c_void_p
+    f.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int] + [P] * 5 + [P] * 4 + [ctypes.c_int] + [
+        P, ctypes.c_int64, P, P, ctypes.c_int]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        _lib = _bind(_LIB)
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _as(arr, kind):
+    if arr is None:
+        return None
+    if kind == "in":
+        a = np.ascontiguousarray(arr)
+        if a.dtype not in (np.float32, np.uint16):
+            raise TypeError(f"oracle inputs are fp32 or bf16 bit patterns (uint16), got {a.dtype}")
+        return a
+    a = np.ascontiguousarray(arr, dtype=np.float32)
+    return a
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                   h0=None, rows=None, nthreads=None, lib_path=None):
+    """Reference scan in fp64.
+
+    u, delta, z: (batch, dim, L); B, C: (batch, N, L), all fp32 or all bf16 bit patterns
+    (numpy uint16). A: (dim, N) fp32; D, delta_bias: (dim,) fp32; h0: (batch, dim, N), widened to fp64.
+    rows: optional flat row indices b*dim + d to compute (default: all, in order).
+    Returns (y, last_state) as fp64 arrays of shape (nrows, L) and (nrows, N), reshaped to
+    (batch, dim, L) / (batch, dim, N) when all rows are computed.
+    """
+    lib = _bind(lib_path) if lib_path else _load()
+    u, delta, B, C = (_as(x, "in") for x in (u, delta, B, C))
+    z = _as(z, "in")
+    kinds = {x.dtype for x in (u, delta, B, C) + ((z,) if z is not None else ())}
+    if len(kinds) != 1:
+        raise TypeError("u, delta, z, B, C must share one storage dtype")
+    in_dtype = 1 if kinds.pop() == np.uint16 else 0
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("u, delta, z shapes differ")
+    if B.shape != (batch, N, L) or C.shape != (batch, N, L):
+        raise ValueError("B, C must be (batch, N, L)")
+    A = _as(A, "p")
+    D = _as(D, "p")
+    delta_bias = _as(delta_bias, "p")
+    h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+    if rows is None:
+        nrows, rows_arr = batch * dim, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.size
+    y = np.empty((nrows, L), dtype=np.float64)
+    ls = np.empty((nrows, N), dtype=np.float64)
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data
+
+    rc = lib.oracle_selective_scan(
+        batch, dim, L, N, in_dtype, ptr(u), ptr(delta), ptr(z), ptr(B), ptr(C), ptr(A), ptr(D),
+        ptr(delta_bias), ptr(h0), int(bool(delta_softplus)), ptr(rows_arr), nrows, ptr(y), ptr(ls),
+        int(nthreads or default_threads()),
+    )
+    if rc != 0:
+        raise RuntimeError(f"oracle_selective_scan failed with {rc}")
+    if rows is None:
+        return y.reshape(batch, dim, L), ls.reshape(batch, dim, N)
+    return y, ls

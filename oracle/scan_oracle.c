@@ -1,0 +1,154 @@
+/*
+ * fp64 CPU oracle of the Mamba selective-scan forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call this file:
+ * only the tests, the smoke check and the bench's CPU-baseline leg use it. It shares no code,
+ * header, table or helper with the HIP library.
+ *
+ * It is the plain sequential recurrence, in the order and notation of the pages:
+ *   - "Mamba代码实战：手把手教你用PyTorch复现选择性扫描核心逻辑（附避坑指南）"
+ *       §2.1 layouts: u, delta, z (batch, D, L); A (D, N); B, C (batch, N, L); D, delta_bias (D);
+ *       §2.2 / §6 delta preprocessing: delta + delta_bias[d], then softplus (flag set) or exp;
+ *       §3.1 discretisation: dA = exp(delta * A[d, n]),  dB = delta * B[b, n, t];
+ *       §3.2 recurrence from a zero state: h = dA * h + dB * u, per step, with an output per step;
+ *       §3.3 skip and gate: y += u * D[d], then y *= silu(z);
+ *       §6 return value: (y, state after the last step).
+ *   - "Mamba-minimal项目解析：深入理解Mamba模型的极简实现", "关键技术点 1. 选择性扫描算法": the output
+ *       contraction y[b, d, t] = sum_n h[b, d, n] * C[b, n, t] (the subscripts there are right;
+ *       the first page's 'bdn,bdn->bd' label on C is a slip).
+ *   - The initial state h0 (NULL = zeros) follows the scan of "手把手用PyTorch实现Mamba的SSM层
+ *       从HiPPO矩阵到选择性扫描算法", §3.1, which takes the state h as an argument.
+ * softplus(x) = ln(1 + e^x) exactly (beta 1, no linearisation threshold), evaluated as
+ * max(x, 0) + log1p(exp(-|x|)), which is the same function. silu(z) = z / (1 + e^-z).
+ * No clamp of delta, no special handling of overflow: fp64 libm exp/log1p throughout.
+ *
+ * Inputs are contiguous. bf16 inputs arrive as their 16-bit patterns and are widened here
+ * (exactly: the pattern is the high half of an fp32), fp32 inputs are widened to fp64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+typedef struct {
+    int64_t batch, dim, len, dstate;
+    int in_dtype;
+    const void *u, *delta, *z, *B, *C;
+    const float *A, *Dvec, *delta_bias;
+    const double* h0;
+    int delta_softplus;
+    const int64_t* rows;
+    int64_t nrows;
+    double *y, *last_state;
+} orc_args;
+
+static double widen(const void* p, int in_dtype, int64_t i) {
+    if (in_dtype == ORC_F32) return (double)((const float*)p)[i];
+    uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+}
+
+static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One row (b, d): writes y[out_row, 0..L) and last_state[out_row, 0..N). */
+static void scan_row(const orc_args* a, int64_t b, int64_t d, int64_t out_row, double* h) {
+    const int64_t L = a->len, N = a->dstate, D = a->dim;
+    const int64_t row_off = (b * D + d) * L;  /* u, delta, z (batch, D, L) */
+    const int64_t bc_off = b * N * L;         /* B, C (batch, N, L) */
+    for (int64_t n = 0; n < N; ++n) h[n] = a->h0 ? a->h0[(b * D + d) * N + n] : 0.0;
+    const double bias = a->delta_bias ? (double)a->delta_bias[d] : 0.0;
+    const double dskip = a->Dvec ? (double)a->Dvec[d] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const double x = widen(a->delta, a->in_dtype, row_off + t) + bias;
+        const double dt = a->delta_softplus ? softplus(x) : exp(x);
+        const double ut = widen(a->u, a->in_dtype, row_off + t);
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double Bt = widen(a->B, a->in_dtype, bc_off + n * L + t);
+            const double Ct = widen(a->C, a->in_dtype, bc_off + n * L + t);
+            const double dA = exp(dt * (double)a->A[d * N + n]);
+            h[n] = dA * h[n] + dt * Bt * ut;
+            acc += Ct * h[n];
+        }
+        double v = acc + dskip * ut;
+        if (a->z) v *= silu(widen(a->z, a->in_dtype, row_off + t));
+        a->y[out_row * L + t] = v;
+    }
+    if (a->last_state)
+        for (int64_t n = 0; n < N; ++n) a->last_state[out_row * N + n] = h[n];
+}
+
+typedef struct {
+    const orc_args* a;
+    int64_t begin, end;
+} orc_job;
+
+static void* orc_worker(void* p) {
+    const orc_job* j = (const orc_job*)p;
+    double* h = (double*)malloc(sizeof(double) * (size_t)(j->a->dstate > 0 ? j->a->dstate : 1));
+    if (!h) return (void*)1;
+    for (int64_t k = j->begin; k < j->end; ++k) {
+        const int64_t flat = j->a->rows ? j->a->rows[k] : k;
+        scan_row(j->a, flat / j->a->dim, flat % j->a->dim, k, h);
+    }
+    free(h);
+    return NULL;
+}
+
+#define ORC_MAX_THREADS 256
+
+/*
+ * Compute rows of the scan.  rows == NULL: all batch*dim rows in order (nrows ignored);
+ * otherwise the listed flat rows b*dim + d.  y is (nrows, L) fp64, last_state (nrows, N) fp64 or
+ * NULL.  z, Dvec, delta_bias, h0 may be NULL (absent).  h0 is (batch, dim, N) fp64, so that a
+ * scan split at any step continues exactly from the fp64 state of its first part.
+ * Returns 0, or a negative value on a bad argument or allocation failure.
+ */
+int oracle_selective_scan(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int in_dtype,
+                          const void* u, const void* delta, const void* z, const void* B,
+                          const void* C, const float* A, const float* Dvec,
+                          const float* delta_bias, const double* h0, int delta_softplus,
+                          const int64_t* rows, int64_t nrows, double* y, double* last_state,
+                          int nthreads) {
+    if (batch <= 0 || dim <= 0 || len <= 0 || dstate <= 0) return -2;
+    if (in_dtype != ORC_F32 && in_dtype != ORC_BF16) return -4;
+    if (!u || !delta || !B || !C || !A || !y) return -1;
+    orc_args a = {batch, dim, len, dstate, in_dtype, u, delta, z, B, C, A, Dvec, delta_bias, h0,
+                  delta_softplus, rows, rows ? nrows : batch * dim, y, last_state};
+    if (rows)
+        for (int64_t k = 0; k < nrows; ++k)
+            if (rows[k] < 0 || rows[k] >= batch * dim) return -2;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > ORC_MAX_THREADS) nthreads = ORC_MAX_THREADS;
+    if (nthreads > a.nrows) nthreads = (int)a.nrows;
+    orc_job jobs[ORC_MAX_THREADS];
+    pthread_t tids[ORC_MAX_THREADS];
+    const int64_t per = (a.nrows + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].a = &a;
+        jobs[t].begin = per * t < a.nrows ? per * t : a.nrows;
+        jobs[t].end = per * (t + 1) < a.nrows ? per * (t + 1) : a.nrows;
+    }
+    int ok = 1;
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, orc_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    if (orc_worker(&jobs[0]) != NULL) ok = 0;
+    for (int t = 1; t <= started; ++t) {
+        void* r = NULL;
+        pthread_join(tids[t], &r);
+        if (r != NULL) ok = 0;
+    }
+    for (int t = started + 1; t < nthreads; ++t)
+        if (orc_worker(&jobs[t]) != NULL) ok = 0;
+    return ok ? 0 : -8;
+}
