@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Selective-scan forward benchmark on one MI355X.
+
+One step = one full forward pass (mamba_scan_fwd) over the Mamba-130m layer workload: batch 8,
+channels 1536 (d_model 768, expand 2), d_state 16, L 2048, bf16 u/delta/z/B/C, fp32 y and last
+state, softplus, silu gate. Inputs are generated once, resident in HBM before timing starts;
+three buffer sets are rotated so that no launch finds its inputs in the 256 MB last-level cache
+from the previous one.
+
+Prints one JSON line: Gelem/s (batch*D*L*N per second), the roofline of the scan kernel
+(algorithmic bytes or VALU work per launch / its mean HIP-event duration), and the fp64 CPU
+oracle timed on the host's cores over the same workload (cpu_baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--kernel", choices=["auto", "generic", "tiled"], default="auto")
+    ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--copy-mb", type=float, default=0.0,
+                    help="instead of the scan, time a plain device copy of this many MB "
+                         "(calibrates the HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copy_calibration(mb, steps, warmup):
+    import torch
+
+    n = int(mb * 1e6) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
+                      "ms_per_copy": dt * 1e3, "GBps": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
+def cpu_baseline(w, inputs):
+    """fp64 oracle over the whole workload on every core this process may use."""
+    import oracle
+
+    cores = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.selective_scan(inputs["u"], inputs["delta"], inputs["A"], inputs["B"], inputs["C"],
+                          D=inputs["D"], z=inputs["z"], delta_bias=inputs["delta_bias"],
+                          delta_softplus=w.softplus, nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.elements / dt / 1e9, 4), "unit": "Gelem/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"the whole workload ({w.rows} rows x {w.seqlen} steps x {w.dstate} states), "
+                      f"fp64, {dt:.2f} s wall on {cores} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the scan shards over (batch, channel) rows with no communication, so N GPUs run "
+              "N independent copies of this measurement).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from selective_state_space_29_amd import scan, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_mb > 0:
+        copy_calibration(args.copy_mb, args.steps, args.warmup)
+        return
+
+    w = workloads.WORKLOADS[args.workload]
+    log(f"workload {w.wid} {w.name}: batch {w.batch} dim {w.dim} N {w.dstate} L {w.seqlen} {w.dtype}")
+    t0 = time.perf_counter()
+    x = workloads.make_inputs(w)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    base = {k: to_dev(v) for k, v in x.items()}
+    sets = []
+    for i in range(max(1, args.sets)):
+        s = {k: (v.clone() if (v is not None and i > 0) else v) for k, v in base.items()}
+        s["y"] = torch.empty((w.batch, w.dim, w.seqlen), dtype=torch.float32, device=dev)
+        s["ls"] = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+        sets.append(s)
+    kernel = None if args.kernel == "auto" else args.kernel
+
+    def step(i):
+        s = sets[i % len(sets)]
+        scan.selective_scan_fn(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                               delta_bias=s["delta_bias"], delta_softplus=w.softplus,
+                               return_last_state=w.last_state, kernel=kernel, out=s["y"],
+                               last_state_out=s["ls"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    span_ms = ev[0][0].elapsed_time(ev[-1][1])
+    mean_launch_ms = float(np.mean(per_launch_ms))
+    log(f"{args.steps} steps: span {span_ms:.3f} ms, wall {wall * 1e3:.3f} ms, launch mean "
+        f"{mean_launch_ms * 1e3:.1f} us min {min(per_launch_ms) * 1e3:.1f} us")
+
+    ms_per_step = span_ms / args.steps
+    value = w.elements / (ms_per_step * 1e-3) / 1e9
+    alg_bytes = w.algorithmic_bytes()
+    achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
+
+    check = None
+    if not args.no_check:
+        import oracle
+
+        rows = sorted({0, 63, 64, w.rows // 2, w.rows - 1} |
+                      {int(r) for r in np.random.default_rng(3).integers(0, w.rows, 11)})
+        s = sets[(args.steps - 1) % len(sets)]
+        idx = torch.tensor(rows, device=dev)
+        yg = s["y"].reshape(w.rows, w.seqlen).index_select(0, idx).cpu().numpy()
+        lg = s["ls"].reshape(w.rows, w.dstate).index_select(0, idx).cpu().numpy()
+        xr = workloads.make_row_inputs(w, rows)
+        yr, lr = oracle.selective_scan(xr["u"], xr["delta"], xr["A"], xr["B"], xr["C"], D=xr["D"],
+                                       z=xr["z"], delta_bias=xr["delta_bias"],
+                                       delta_softplus=w.softplus)
+        yr, lr = yr.reshape(len(rows), -1), lr.reshape(len(rows), -1)
+        check = {"rows": len(rows),
+                 "max_rel_err_y": float(np.max(np.abs(yg - yr) / (1 + np.abs(yr)))),
+                 "max_rel_err_last_state": float(np.max(np.abs(lg - lr) / (1 + np.abs(lr))))}
+        log(f"sampled parity: {check}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on the whole workload")
+        cpu = cpu_baseline(w, x)
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": "scan Gelem/s (B*D*L*N) + % HBM roofline, Mamba-130m layer shape, L=2048",
+        "value": round(value, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 arithmetic, bf16 storage" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded counter-based generator)",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
+                   "seq_len": w.seqlen, "storage": w.dtype, "z_gate": w.has_z,
+                   "last_state": w.last_state, "kernel": args.kernel, "buffer_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": alg_bytes,
+                     "mean_launch_us": round(mean_launch_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "parity_sample": check,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

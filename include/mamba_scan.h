@@ -1,0 +1,131 @@
+/*
+ * mamba_scan.h - C ABI of the MI355X (gfx950) selective-scan forward library.
+ *
+ * The operation (one call = the whole forward pass):
+ *
+ *   for every batch b, channel d, step t, state n (diagonal A):
+ *     dt      = softplus(delta[b,d,t] + delta_bias[d])      if MAMBA_SCAN_DELTA_SOFTPLUS
+ *             = exp(delta[b,d,t] + delta_bias[d])           otherwise
+ *     h[n]    = exp(dt * A[d,n]) * h[n] + dt * B[b,n,t] * u[b,d,t]      (h starts at h0 or 0)
+ *     y[b,d,t]= (sum_n C[b,n,t] * h[n] + D[d] * u[b,d,t]) * silu(z[b,d,t])
+ *   last_state[b,d,n] = h[n] after the last step.
+ *
+ * Sources: "Mamba代码实战：手把手教你用PyTorch复现选择性扫描核心逻辑（附避坑指南）" - §2.1 (tensor
+ * layouts), §2.2 and §6 (delta + delta_bias, then softplus or exp; the argument list
+ * u, delta, A, B, C, D, delta_bias, delta_softplus, return_last_state; the returned state),
+ * §3.1 (dA = exp(delta*A), dB = delta*B), §3.2 (the per-step recurrence from a zero state),
+ * §3.3 (skip y + u*D, then the gate y * silu(z)), §4.1 (unit stride along L);
+ * "Mamba-minimal项目解析：深入理解Mamba模型的极简实现", 关键技术点 1 (y = sum_n h[n] * C[n]) and 5
+ * (A = -exp(A_log) and D in fp32, softplus on delta); "手把手用PyTorch实现Mamba的SSM层从HiPPO矩阵到
+ * 选择性扫描算法" §3.1 (a scan that starts from a given state: the optional h0).
+ *
+ * Conventions
+ *  - All pointers are DEVICE pointers (memory of the GPU that is current when the call is made).
+ *    The caller owns every buffer; the library never allocates, frees or synchronises.
+ *  - u, delta, z: (batch, dim, len); B, C: (batch, dstate, len); all in `dtype`.
+ *    A: (dim, dstate), D: (dim), delta_bias: (dim), h0: (batch, dim, dstate): fp32.
+ *    y: (batch, dim, len) fp32; last_state: (batch, dim, dstate) fp32.
+ *  - Strides are in elements. The innermost stride (len for u/delta/z/B/C/y, dstate for
+ *    A/h0/last_state) must be 1; the other strides are free (slices are fine) but must be >= 0.
+ *    A NULL strides argument means every tensor is contiguous.
+ *  - z, D, delta_bias, h0 may be NULL (absent: no gate, no skip, no bias, zero initial state).
+ *    last_state must be non-NULL exactly when MAMBA_SCAN_RETURN_LAST_STATE is set.
+ *  - Outputs must not overlap any input or each other.
+ *  - The work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *    returns without waiting. Calls on different streams may run concurrently.
+ *  - Errors are returned before anything is enqueued (codes below); the library never aborts.
+ *    mamba_scan_strerror() turns a code into a message.
+ *  - Thread-safe: no mutable global state.
+ */
+#ifndef MAMBA_SCAN_H
+#define MAMBA_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAMBA_SCAN_ABI_VERSION 1
+
+/* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
+typedef enum mamba_scan_dtype {
+    MAMBA_SCAN_F32 = 0,
+    MAMBA_SCAN_BF16 = 1
+} mamba_scan_dtype;
+
+/* flags */
+#define MAMBA_SCAN_DELTA_SOFTPLUS (1u << 0)    /* dt = softplus(.) ; clear: dt = exp(.) */
+#define MAMBA_SCAN_RETURN_LAST_STATE (1u << 1) /* write last_state */
+/* Kernel selection, for testing and tuning. Default (neither bit): the library picks. */
+#define MAMBA_SCAN_FORCE_GENERIC (1u << 8) /* one lane per row, any shape and alignment */
+#define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
+#define MAMBA_SCAN_KNOWN_FLAGS 0x303u
+
+/* error codes */
+#define MAMBA_SCAN_OK 0
+#define MAMBA_SCAN_ERR_NULL (-1)      /* a required pointer is NULL */
+#define MAMBA_SCAN_ERR_SHAPE (-2)     /* a dimension <= 0, or a stride < 0 */
+#define MAMBA_SCAN_ERR_STRIDE (-3)    /* an innermost stride is not 1 */
+#define MAMBA_SCAN_ERR_DTYPE (-4)     /* unknown dtype */
+#define MAMBA_SCAN_ERR_DSTATE (-5)    /* dstate above MAMBA_SCAN_MAX_DSTATE */
+#define MAMBA_SCAN_ERR_ARGS (-6)      /* flags/pointer mismatch, unknown flag, overlapping buffers */
+#define MAMBA_SCAN_ERR_LAUNCH (-7)    /* the HIP runtime refused the launch */
+#define MAMBA_SCAN_ERR_UNSUPPORTED (-8) /* a forced kernel cannot run this shape/alignment */
+#define MAMBA_SCAN_ERR_WORKSPACE (-9) /* workspace too small for the requested plan */
+
+#define MAMBA_SCAN_MAX_DSTATE 256
+
+typedef struct mamba_scan_ptrs {
+    const void* u;           /* (batch, dim, len) dtype, required */
+    const void* delta;       /* (batch, dim, len) dtype, required */
+    const void* z;           /* (batch, dim, len) dtype, or NULL */
+    const void* B;           /* (batch, dstate, len) dtype, required */
+    const void* C;           /* (batch, dstate, len) dtype, required */
+    const float* A;          /* (dim, dstate) fp32, required */
+    const float* D;          /* (dim) fp32, or NULL */
+    const float* delta_bias; /* (dim) fp32, or NULL */
+    const float* h0;         /* (batch, dim, dstate) fp32, or NULL (zero initial state) */
+    float* y;                /* (batch, dim, len) fp32, required, written */
+    float* last_state;       /* (batch, dim, dstate) fp32, written iff RETURN_LAST_STATE */
+    void* workspace;         /* device scratch, or NULL; see mamba_scan_workspace_bytes */
+    int64_t workspace_bytes; /* its size in bytes */
+} mamba_scan_ptrs;
+
+typedef struct mamba_scan_shape {
+    int64_t batch, dim, len, dstate;
+} mamba_scan_shape;
+
+/* Element strides: [0] batch, [1] dim or state, [2] len (must be 1) for the 3-d tensors;
+ * A: [0] dim, [1] state (must be 1); D, delta_bias: stride along dim. */
+typedef struct mamba_scan_strides {
+    int64_t u[3], delta[3], z[3];
+    int64_t B[3], C[3];
+    int64_t y[3];
+    int64_t h0[3], last_state[3];
+    int64_t A[2];
+    int64_t D, delta_bias;
+} mamba_scan_strides;
+
+/* Enqueue the selective-scan forward pass on `stream`. Returns MAMBA_SCAN_OK or an error code. */
+int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s,
+                   const mamba_scan_strides* st, mamba_scan_dtype dtype, uint32_t flags,
+                   void* stream);
+
+/* Bytes of device workspace that let mamba_scan_fwd split long sequences across workgroups
+ * (an exact two-pass carry of the state between segments of L). 0 when the plan needs none.
+ * A call given less workspace than this still runs, unsplit. Negative on invalid arguments. */
+int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype,
+                                   uint32_t flags);
+
+/* Static message for an error code; never NULL. */
+const char* mamba_scan_strerror(int code);
+
+/* MAMBA_SCAN_ABI_VERSION of the built library. */
+int mamba_scan_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H */

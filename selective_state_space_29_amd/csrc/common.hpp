@@ -1,0 +1,65 @@
+// Device-side helpers shared by the selective-scan kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mscan {
+
+// Everything a kernel needs, passed by value. Strides are in elements.
+struct ScanParams {
+    const void* u;
+    const void* delta;
+    const void* z;
+    const void* B;
+    const void* C;
+    const float* A;
+    const float* D;
+    const float* bias;
+    const float* h0;
+    float* y;
+    float* last_state;
+    int64_t batch, dim, len, dstate;
+    int64_t su_b, su_d, sdt_b, sdt_d, sz_b, sz_d;
+    int64_t sB_b, sB_n, sC_b, sC_n;
+    int64_t sy_b, sy_d;
+    int64_t sh0_b, sh0_d, sls_b, sls_d;
+    int64_t sA_d, sD, sbias;
+    int softplus;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Storage types: fp32, or bf16 held as its 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v.bits << 16); }
+
+// Hardware transcendentals: v_exp_f32 is 2^x, v_log_f32 is log2(x), v_rcp_f32 is 1/x.
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = ln(1 + e^x) = max(x, 0) + log1p(e^-|x|). log1p(e) uses Goldberg's correction
+// ("What every computer scientist should know about floating-point arithmetic", 1991,
+// Theorem 4): with w = 1 + e rounded, log1p(e) = e when w == 1, else ln(w) * e / (w - 1).
+__device__ __forceinline__ float softplus_f(float x) {
+    const float e = hw_exp2(-__builtin_fabsf(x) * kLog2e);
+    const float w = 1.0f + e;
+    const float l1p = (w == 1.0f) ? e : (hw_log2(w) * kLn2) * (e * hw_rcp(w - 1.0f));
+    return __builtin_fmaxf(x, 0.0f) + l1p;
+}
+
+// dt from the biased delta: softplus, or exp when the softplus flag is clear.
+__device__ __forceinline__ float delta_to_dt(float x, int softplus) {
+    return softplus ? softplus_f(x) : hw_exp2(x * kLog2e);
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z).
+__device__ __forceinline__ float silu_f(float z) { return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e)); }
+
+}  // namespace mscan

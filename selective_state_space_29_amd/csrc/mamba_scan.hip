@@ -1,0 +1,216 @@
+// C-ABI entry points of the selective-scan library: argument validation, kernel choice and the
+// launch on the caller's stream. The contract is in include/mamba_scan.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mamba_scan.h"
+#include "common.hpp"
+#include "scan_generic.hpp"
+#include "scan_tiled.hpp"
+
+using namespace mscan;
+
+namespace {
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi) bytes
+    bool valid;
+};
+
+// Byte range touched by a tensor with the given sizes and element strides.
+Span span_of(const void* ptr, int64_t esize, const int64_t* sizes, const int64_t* strides, int nd) {
+    Span s{0, 0, false};
+    if (!ptr) return s;
+    int64_t maxoff = 0;
+    for (int i = 0; i < nd; ++i) maxoff += (sizes[i] - 1) * strides[i];
+    s.lo = reinterpret_cast<uintptr_t>(ptr);
+    s.hi = s.lo + (uintptr_t)((maxoff + 1) * esize);
+    s.valid = true;
+    return s;
+}
+
+const int64_t kUnit[1] = {1};
+
+bool overlaps(const Span& a, const Span& b) { return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi; }
+
+void contiguous_strides(const mamba_scan_shape& s, mamba_scan_strides* st) {
+    const int64_t DL = s.dim * s.len, NL = s.dstate * s.len, DN = s.dim * s.dstate;
+    const int64_t t3[3] = {DL, s.len, 1};
+    memcpy(st->u, t3, sizeof t3);
+    memcpy(st->delta, t3, sizeof t3);
+    memcpy(st->z, t3, sizeof t3);
+    memcpy(st->y, t3, sizeof t3);
+    const int64_t bc[3] = {NL, s.len, 1};
+    memcpy(st->B, bc, sizeof bc);
+    memcpy(st->C, bc, sizeof bc);
+    const int64_t hs[3] = {DN, s.dstate, 1};
+    memcpy(st->h0, hs, sizeof hs);
+    memcpy(st->last_state, hs, sizeof hs);
+    st->A[0] = s.dstate;
+    st->A[1] = 1;
+    st->D = 1;
+    st->delta_bias = 1;
+}
+
+int validate(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_scan_strides* st,
+             mamba_scan_dtype dtype, uint32_t flags) {
+    if (!p || !s || !st) return MAMBA_SCAN_ERR_NULL;
+    if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
+    if (flags & ~MAMBA_SCAN_KNOWN_FLAGS) return MAMBA_SCAN_ERR_ARGS;
+    if ((flags & MAMBA_SCAN_FORCE_GENERIC) && (flags & MAMBA_SCAN_FORCE_TILED)) return MAMBA_SCAN_ERR_ARGS;
+    if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+    if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
+    if (!p->u || !p->delta || !p->B || !p->C || !p->A || !p->y) return MAMBA_SCAN_ERR_NULL;
+    const bool want_ls = (flags & MAMBA_SCAN_RETURN_LAST_STATE) != 0;
+    if (want_ls != (p->last_state != nullptr)) return MAMBA_SCAN_ERR_ARGS;
+    if (p->workspace_bytes < 0 || (p->workspace_bytes > 0 && !p->workspace)) return MAMBA_SCAN_ERR_ARGS;
+
+    const int64_t* inner3[] = {st->u, st->delta, st->z, st->B, st->C, st->y, st->h0, st->last_state};
+    for (const int64_t* v : inner3) {
+        if (v[2] != 1) return MAMBA_SCAN_ERR_STRIDE;
+        if (v[0] < 0 || v[1] < 0) return MAMBA_SCAN_ERR_SHAPE;
+    }
+    if (st->A[1] != 1) return MAMBA_SCAN_ERR_STRIDE;
+    if (st->A[0] < 0 || st->D < 0 || st->delta_bias < 0) return MAMBA_SCAN_ERR_SHAPE;
+
+    // Outputs may not overlap inputs or each other.
+    const int64_t es = dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+    const int64_t bdl[3] = {s->batch, s->dim, s->len};
+    const int64_t bnl[3] = {s->batch, s->dstate, s->len};
+    const int64_t bdn[3] = {s->batch, s->dim, s->dstate};
+    const int64_t dn[2] = {s->dim, s->dstate};
+    const int64_t d1[1] = {s->dim};
+    const Span ins[] = {
+        span_of(p->u, es, bdl, st->u, 3),         span_of(p->delta, es, bdl, st->delta, 3),
+        span_of(p->z, es, bdl, st->z, 3),         span_of(p->B, es, bnl, st->B, 3),
+        span_of(p->C, es, bnl, st->C, 3),         span_of(p->A, 4, dn, st->A, 2),
+        span_of(p->D, 4, d1, &st->D, 1),          span_of(p->delta_bias, 4, d1, &st->delta_bias, 1),
+        span_of(p->h0, 4, bdn, st->h0, 3),
+        span_of(p->workspace, 1, &p->workspace_bytes, kUnit, p->workspace_bytes > 0 ? 1 : 0),
+    };
+    const Span y = span_of(p->y, 4, bdl, st->y, 3);
+    const Span ls = span_of(p->last_state, 4, bdn, st->last_state, 3);
+    for (const Span& in : ins)
+        if (overlaps(y, in) || overlaps(ls, in)) return MAMBA_SCAN_ERR_ARGS;
+    if (overlaps(y, ls)) return MAMBA_SCAN_ERR_ARGS;
+    return MAMBA_SCAN_OK;
+}
+
+ScanParams make_params(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_scan_strides* st,
+                       uint32_t flags) {
+    ScanParams q;
+    q.u = p->u;
+    q.delta = p->delta;
+    q.z = p->z;
+    q.B = p->B;
+    q.C = p->C;
+    q.A = p->A;
+    q.D = p->D;
+    q.bias = p->delta_bias;
+    q.h0 = p->h0;
+    q.y = p->y;
+    q.last_state = (flags & MAMBA_SCAN_RETURN_LAST_STATE) ? p->last_state : nullptr;
+    q.batch = s->batch;
+    q.dim = s->dim;
+    q.len = s->len;
+    q.dstate = s->dstate;
+    q.su_b = st->u[0];
+    q.su_d = st->u[1];
+    q.sdt_b = st->delta[0];
+    q.sdt_d = st->delta[1];
+    q.sz_b = st->z[0];
+    q.sz_d = st->z[1];
+    q.sB_b = st->B[0];
+    q.sB_n = st->B[1];
+    q.sC_b = st->C[0];
+    q.sC_n = st->C[1];
+    q.sy_b = st->y[0];
+    q.sy_d = st->y[1];
+    q.sh0_b = st->h0[0];
+    q.sh0_d = st->h0[1];
+    q.sls_b = st->last_state[0];
+    q.sls_d = st->last_state[1];
+    q.sA_d = st->A[0];
+    q.sD = st->D;
+    q.sbias = st->delta_bias;
+    q.softplus = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) ? 1 : 0;
+    return q;
+}
+
+template <typename T>
+int launch_generic(const ScanParams& q, hipStream_t stream) {
+    const int64_t rows = q.batch * q.dim;
+    const dim3 grid((unsigned)((rows + 63) / 64));
+    const dim3 block(64);
+    void* args[] = {const_cast<ScanParams*>(&q)};
+    const void* fn;
+    if (q.dstate <= 16)
+        fn = reinterpret_cast<const void*>(&scan_generic_kernel<T, 16>);
+    else if (q.dstate <= 32)
+        fn = reinterpret_cast<const void*>(&scan_generic_kernel<T, 32>);
+    else
+        fn = reinterpret_cast<const void*>(&scan_generic_kernel<T, 64>);
+    return hipLaunchKernel(fn, grid, block, args, 0, stream) == hipSuccess ? MAMBA_SCAN_OK
+                                                                           : MAMBA_SCAN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba_scan_abi_version(void) { return MAMBA_SCAN_ABI_VERSION; }
+
+const char* mamba_scan_strerror(int code) {
+    switch (code) {
+        case MAMBA_SCAN_OK: return "success";
+        case MAMBA_SCAN_ERR_NULL: return "a required pointer is NULL";
+        case MAMBA_SCAN_ERR_SHAPE: return "a dimension is <= 0 or a stride is negative";
+        case MAMBA_SCAN_ERR_STRIDE: return "an innermost stride (along len, or along dstate) is not 1";
+        case MAMBA_SCAN_ERR_DTYPE: return "unknown dtype (expected MAMBA_SCAN_F32 or MAMBA_SCAN_BF16)";
+        case MAMBA_SCAN_ERR_DSTATE: return "dstate exceeds MAMBA_SCAN_MAX_DSTATE";
+        case MAMBA_SCAN_ERR_ARGS:
+            return "inconsistent flags/pointers (unknown flag, last_state vs RETURN_LAST_STATE, "
+                   "workspace) or overlapping buffers";
+        case MAMBA_SCAN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+        case MAMBA_SCAN_ERR_UNSUPPORTED: return "the forced kernel cannot handle this shape or alignment";
+        case MAMBA_SCAN_ERR_WORKSPACE: return "workspace too small";
+        default: return "unknown error code";
+    }
+}
+
+int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype, uint32_t flags) {
+    if (!s) return MAMBA_SCAN_ERR_NULL;
+    if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
+    if (flags & ~MAMBA_SCAN_KNOWN_FLAGS) return MAMBA_SCAN_ERR_ARGS;
+    if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+    if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
+    return tiled_workspace_bytes(*s, flags);
+}
+
+int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_scan_strides* st_in,
+                   mamba_scan_dtype dtype, uint32_t flags, void* stream) {
+    if (!p || !s) return MAMBA_SCAN_ERR_NULL;
+    mamba_scan_strides st;
+    if (st_in) {
+        st = *st_in;
+    } else {
+        if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+        contiguous_strides(*s, &st);
+    }
+    const int rc = validate(p, s, &st, dtype, flags);
+    if (rc != MAMBA_SCAN_OK) return rc;
+    const ScanParams q = make_params(p, s, &st, flags);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool bf16 = dtype == MAMBA_SCAN_BF16;
+
+    if (!(flags & MAMBA_SCAN_FORCE_GENERIC)) {
+        const int trc = bf16 ? launch_tiled<bf16_t>(q, p, flags, hs) : launch_tiled<float>(q, p, flags, hs);
+        if (trc != MAMBA_SCAN_ERR_UNSUPPORTED) return trc;
+        if (flags & MAMBA_SCAN_FORCE_TILED) return trc;
+    }
+    return bf16 ? launch_generic<bf16_t>(q, hs) : launch_generic<float>(q, hs);
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+"""Python binding of the selective-scan C ABI (argument marshalling only).
+
+Every step of the scan runs in ``libmamba_scan.so``; this module only turns torch tensors into
+device pointers, strides and flags, allocates the outputs with torch, and calls
+``mamba_scan_fwd`` on torch's current HIP stream. There is no CPU fallback: without the built
+library, or without a GPU, calls raise.
+
+Signature and defaults follow ``selective_scan_ref(u, delta, A, B, C, D=None, delta_bias=None,
+delta_softplus=False, return_last_state=False)`` of "Mamba代码实战…" §6, with the gate ``z`` of
+§3.3 and an initial state ``h0`` (the state argument of the scan in "手把手用PyTorch实现Mamba的SSM层…"
+§3.1). Inputs whose last stride is not 1 are made contiguous first (§4.1).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmamba_scan.so")
+
+F32, BF16 = 0, 1
+DELTA_SOFTPLUS = 1 << 0
+RETURN_LAST_STATE = 1 << 1
+FORCE_GENERIC = 1 << 8
+FORCE_TILED = 1 << 9
+
+_I64 = ctypes.c_int64
+_P = ctypes.c_void_p
+
+
+class Ptrs(ctypes.Structure):
+    _fields_ = [("u", _P), ("delta", _P), ("z", _P), ("B", _P), ("C", _P), ("A", _P), ("D", _P),
+                ("delta_bias", _P), ("h0", _P), ("y", _P), ("last_state", _P),
+                ("workspace", _P), ("workspace_bytes", _I64)]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", _I64), ("dim", _I64), ("len", _I64), ("dstate", _I64)]
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("u", _I64 * 3), ("delta", _I64 * 3), ("z", _I64 * 3), ("B", _I64 * 3),
+                ("C", _I64 * 3), ("y", _I64 * 3), ("h0", _I64 * 3), ("last_state", _I64 * 3),
+                ("A", _I64 * 2), ("D", _I64), ("delta_bias", _I64)]
+
+
+class MambaScanError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mamba_scan_fwd failed ({code}): {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: the HIP extension is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.mamba_scan_fwd.restype = ctypes.c_int
+    lib.mamba_scan_fwd.argtypes = [ctypes.POINTER(Ptrs), ctypes.POINTER(Shape),
+                                   ctypes.POINTER(Strides), ctypes.c_int, ctypes.c_uint32, _P]
+    lib.mamba_scan_workspace_bytes.restype = _I64
+    lib.mamba_scan_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, ctypes.c_uint32]
+    lib.mamba_scan_strerror.restype = ctypes.c_char_p
+    lib.mamba_scan_strerror.argtypes = [ctypes.c_int]
+    lib.mamba_scan_abi_version.restype = ctypes.c_int
+    lib.mamba_scan_abi_version.argtypes = []
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().mamba_scan_strerror(code).decode()
+
+
+def _inner_contig(x):
+    if x is not None and x.stride(-1) != 1:
+        x = x.contiguous()
+    return x
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def _s3(x, fallback=(0, 0, 1)):
+    return (_I64 * 3)(*(x.stride() if x is not None else fallback))
+
+
+def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                      return_last_state=False, h0=None, *, kernel=None, out=None,
+                      last_state_out=None):
+    """y = selective_scan(...), fp32 (batch, dim, L); with ``return_last_state`` also the final
+    state (batch, dim, N) fp32.
+
+    u, delta, z: (batch, dim, L); B, C: (batch, N, L); one storage dtype for all five
+    (torch.float32 or torch.bfloat16). A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N);
+    these are taken in fp32. ``kernel``: None (library picks), "generic" or "tiled".
+    """
+    lib = load_library()
+    if u.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"u must be float32 or bfloat16, got {u.dtype}")
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("selective_scan_fn runs on the GPU only: inputs must be device tensors")
+    for name, x in (("delta", delta), ("z", z), ("B", B), ("C", C)):
+        if x is not None and (x.dtype != u.dtype or x.device != dev):
+            raise TypeError(f"{name} must have u's dtype and device")
+    for name, x in (("A", A), ("D", D), ("delta_bias", delta_bias), ("h0", h0)):
+        if x is not None and x.device != dev:
+            raise TypeError(f"{name} must be on u's device")
+    u, delta, z, B, C = (_inner_contig(x) for x in (u, delta, z, B, C))
+    A = _inner_contig(A.float())
+    D = None if D is None else D.float()
+    delta_bias = None if delta_bias is None else delta_bias.float()
+    h0 = None if h0 is None else _inner_contig(h0.float())
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("u, delta and z must have the same shape")
+    if B.shape != (batch, N, L) or C.shape != (batch, N, L):
+        raise ValueError(f"B and C must be (batch, N, L) = {(batch, N, L)}")
+    if A.shape != (dim, N):
+        raise ValueError(f"A must be (dim, N) = {(dim, N)}")
+    for name, x in (("D", D), ("delta_bias", delta_bias)):
+        if x is not None and x.shape != (dim,):
+            raise ValueError(f"{name} must be (dim,)")
+    if h0 is not None and h0.shape != (batch, dim, N):
+        raise ValueError("h0 must be (batch, dim, N)")
+
+    y = out if out is not None else torch.empty((batch, dim, L), dtype=torch.float32, device=dev)
+    ls = None
+    flags = (DELTA_SOFTPLUS if delta_softplus else 0)
+    if return_last_state:
+        ls = last_state_out if last_state_out is not None else torch.empty(
+            (batch, dim, N), dtype=torch.float32, device=dev)
+        flags |= RETURN_LAST_STATE
+    if kernel == "generic":
+        flags |= FORCE_GENERIC
+    elif kernel == "tiled":
+        flags |= FORCE_TILED
+    elif kernel is not None:
+        raise ValueError("kernel must be None, 'generic' or 'tiled'")
+
+    shape = Shape(batch, dim, L, N)
+    dtype = BF16 if u.dtype == torch.bfloat16 else F32
+    ws_bytes = lib.mamba_scan_workspace_bytes(ctypes.byref(shape), dtype, flags)
+    if ws_bytes < 0:
+        raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
+    ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+
+    st = Strides()
+    st.u, st.delta, st.z = _s3(u), _s3(delta), _s3(z)
+    st.B, st.C, st.y = _s3(B), _s3(C), _s3(y)
+    st.h0, st.last_state = _s3(h0), _s3(ls)
+    st.A = (_I64 * 2)(*A.stride())
+    st.D = D.stride(0) if D is not None else 1
+    st.delta_bias = delta_bias.stride(0) if delta_bias is not None else 1
+    ptrs = Ptrs(_ptr(u), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
+                _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls), _ptr(ws), int(ws_bytes))
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.mamba_scan_fwd(ctypes.byref(ptrs), ctypes.byref(shape), ctypes.byref(st),
+                                dtype, flags, stream)
+    if rc != 0:
+        err = MambaScanError(rc, strerror(rc))
+        if rc in (-1, -2, -3, -4, -5, -6, -8):
+            raise ValueError(str(err)) from err
+        raise err
+    if ws is not None:
+        ws.record_stream(torch.cuda.current_stream(dev))
+    return (y, ls) if return_last_state else y
