@@ -165,10 +165,16 @@ def main():
         yg = s["y"].reshape(w.rows, w.seqlen).index_select(0, idx).cpu().numpy()
         lg = s["ls"].reshape(w.rows, w.dstate).index_select(0, idx).cpu().numpy()
         xr = workloads.make_row_inputs(w, rows)
-        yr, lr = oracle.selective_scan(xr["u"], xr["delta"], xr["A"], xr["B"], xr["C"], D=xr["D"],
-                                       z=xr["z"], delta_bias=xr["delta_bias"],
-                                       delta_softplus=w.softplus)
-        yr, lr = yr.reshape(len(rows), -1), lr.reshape(len(rows), -1)
+        yr, lr = [], []
+        for i in range(len(rows)):  # each sampled row is its own single-channel problem
+            s1 = slice(i, i + 1)
+            a, c = oracle.selective_scan(
+                xr["u"][s1], xr["delta"][s1], xr["A"][s1], xr["B"][s1], xr["C"][s1], D=xr["D"][s1],
+                z=None if xr["z"] is None else xr["z"][s1], delta_bias=xr["delta_bias"][s1],
+                delta_softplus=w.softplus)
+            yr.append(a.reshape(-1))
+            lr.append(c.reshape(-1))
+        yr, lr = np.stack(yr), np.stack(lr)
         check = {"rows": len(rows),
                  "max_rel_err_y": float(np.max(np.abs(yg - yr) / (1 + np.abs(yr)))),
                  "max_rel_err_last_state": float(np.max(np.abs(lg - lr) / (1 + np.abs(lr))))}

@@ -129,8 +129,9 @@ def make_inputs(w: Workload) -> dict:
 
 
 def make_row_inputs(w: Workload, rows) -> dict:
-    """Inputs restricted to the listed flat rows ``b * dim + d``: u/delta/z as (nrows, 1, L),
-    B/C for the rows' batches as (nrows, N, L), and per-row A/D/delta_bias. The slices are
+    """Inputs restricted to the listed flat rows ``b * dim + d``, one independent single-channel
+    problem per row: entry ``i`` of u/delta/z (nrows, 1, L), of B/C (nrows, N, L) and of
+    A (nrows, N), D and delta_bias (nrows,) is row ``rows[i]``'s data. The slices are
     bit-identical to the same rows of :func:`make_inputs` (the generator is counter-based)."""
     rows = [int(r) for r in rows]
     L = w.seqlen

@@ -42,6 +42,24 @@ def gpu_scan(x, softplus=True, last_state=True, kernel=None, h0=None, dev="cuda:
     return out.cpu().numpy(), None
 
 
+def oracle_rows(xr, softplus=True):
+    """Oracle over the single-channel problems of workloads.make_row_inputs (one per row)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = xr["u"].shape[0]
+
+    def one(i):
+        s = slice(i, i + 1)
+        return oracle.selective_scan(
+            xr["u"][s], xr["delta"][s], xr["A"][s], xr["B"][s], xr["C"][s], D=xr["D"][s],
+            z=None if xr["z"] is None else xr["z"][s], delta_bias=xr["delta_bias"][s],
+            delta_softplus=softplus, nthreads=1)
+
+    with ThreadPoolExecutor(max_workers=min(16, oracle.default_threads())) as ex:
+        res = list(ex.map(one, range(n)))
+    return (np.stack([r[0].reshape(-1) for r in res]), np.stack([r[1].reshape(-1) for r in res]))
+
+
 def oracle_scan(x, softplus=True, h0=None, rows=None):
     return oracle.selective_scan(
         x["u"], x["delta"], x["A"], x["B"], x["C"], D=x.get("D"), z=x.get("z"),

@@ -94,3 +94,16 @@ def test_workload_inputs_follow_their_recipes():
     assert p["delta_bias"].min() >= -4.0 and p["delta_bias"].max() < -1.0
     assert workloads.WORKLOADS[3].elements == 8 * 1536 * 2048 * 16
     assert abs(workloads.WORKLOADS[3].algorithmic_bytes() / 1e6 - 253.60) < 0.01
+
+
+def test_row_problems_reproduce_full_oracle_rows():
+    """Each sampled row, run as its own single-channel problem, equals that row of the full run."""
+    import gpu_util as gu
+
+    w = workloads.WORKLOADS[1]
+    full = workloads.make_inputs(w)
+    yf, lf = gu.oracle_scan(full, softplus=w.softplus)
+    rows = [0, 17, 63]
+    yr, lr = gu.oracle_rows(workloads.make_row_inputs(w, rows), softplus=w.softplus)
+    assert np.array_equal(yr, yf.reshape(w.rows, -1)[rows])
+    assert np.array_equal(lr, lf.reshape(w.rows, -1)[rows])
