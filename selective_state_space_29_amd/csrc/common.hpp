@@ -44,14 +44,15 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(x) = ln(1 + e^x) = max(x, 0) + log1p(e^-|x|). log1p(e) uses Goldberg's correction
-// ("What every computer scientist should know about floating-point arithmetic", 1991,
-// Theorem 4): with w = 1 + e rounded, log1p(e) = e when w == 1, else ln(w) * e / (w - 1).
+// softplus(x) = ln(1 + e^x) = max(x, 0) + log1p(e) with e = e^-|x| in (0, 1].
+// log1p(e): w = 1 + e is rounded, and r = e - (w - 1) is that rounding error exactly (w - 1 is
+// exact for w in [1, 2]). Then log1p(e) = ln(w) + ln(1 + r/w) = ln(w) + r to within |r|*e + r^2,
+// i.e. below 2^-24 relative: no division and no special case for w == 1 (then r = e).
 __device__ __forceinline__ float softplus_f(float x) {
     const float e = hw_exp2(-__builtin_fabsf(x) * kLog2e);
     const float w = 1.0f + e;
-    const float l1p = (w == 1.0f) ? e : (hw_log2(w) * kLn2) * (e * hw_rcp(w - 1.0f));
-    return __builtin_fmaxf(x, 0.0f) + l1p;
+    const float r = e - (w - 1.0f);
+    return __builtin_fmaf(hw_log2(w), kLn2, r + __builtin_fmaxf(x, 0.0f));
 }
 
 // dt from the biased delta: softplus, or exp when the softplus flag is clear.

@@ -93,8 +93,16 @@ def _ptr(x):
     return None if x is None else x.data_ptr()
 
 
+def _strides(x):
+    """Element strides. A size-1 dimension's stride is never used and torch reports arbitrary
+    values for it: report 1 for the innermost dimension and 0 for the others."""
+    nd = len(x.shape)
+    return [(1 if i == nd - 1 else 0) if n == 1 else s
+            for i, (n, s) in enumerate(zip(x.shape, x.stride()))]
+
+
 def _s3(x, fallback=(0, 0, 1)):
-    return (_I64 * 3)(*(x.stride() if x is not None else fallback))
+    return (_I64 * 3)(*(_strides(x) if x is not None else fallback))
 
 
 def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
@@ -163,9 +171,9 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     st.u, st.delta, st.z = _s3(u), _s3(delta), _s3(z)
     st.B, st.C, st.y = _s3(B), _s3(C), _s3(y)
     st.h0, st.last_state = _s3(h0), _s3(ls)
-    st.A = (_I64 * 2)(*A.stride())
-    st.D = D.stride(0) if D is not None else 1
-    st.delta_bias = delta_bias.stride(0) if delta_bias is not None else 1
+    st.A = (_I64 * 2)(*_strides(A))
+    st.D = _strides(D)[0] if D is not None else 1
+    st.delta_bias = _strides(delta_bias)[0] if delta_bias is not None else 1
     ptrs = Ptrs(_ptr(u), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
                 _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls), _ptr(ws), int(ws_bytes))
     with torch.cuda.device(dev):
