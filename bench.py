@@ -24,6 +24,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# VALU peak: 256 CUs x 128 fp32 lanes/clk x 2.4 GHz = 78.6 T lane-slots/s, i.e. the published
+# 157.3 TFLOP/s fp32 vector figure with one FMA = 2 flops. Work is counted in issue slots (one
+# lane-op = 1 slot, a transcendental = 4 slots at quarter rate) and reported as 2 flops per slot.
+VALU_PEAK_TFLOPS = 157.3
+SLOTS_PER_ELEMENT = 8      # mul (dt*A), exp, mul (dt*u*B), fma (h), fma (y)
+SLOTS_PER_ROW_STEP = 30    # softplus, dt*u, bias, skip, silu gate
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "scan_tiled_mamba130m_traffic.json")
 
 
 def parse():
@@ -62,6 +69,30 @@ def copy_calibration(mb, steps, warmup):
     dt = (time.perf_counter() - t0) / steps
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
                       "ms_per_copy": dt * 1e3, "GBps": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
+def kernel_source_hash():
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_29_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(w, kernel):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record, or None
+    when that record was taken on other kernel sources or another workload."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if w.wid != 3 or kernel not in ("auto", "tiled") or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(w, inputs):
@@ -153,6 +184,8 @@ def main():
     value = w.elements / (ms_per_step * 1e-3) / 1e9
     alg_bytes = w.algorithmic_bytes()
     achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
+    slots = w.elements * SLOTS_PER_ELEMENT + w.rows * w.seqlen * SLOTS_PER_ROW_STEP
+    achieved_tflops = 2 * slots / (mean_launch_ms * 1e-3) / 1e12
 
     check = None
     if not args.no_check:
@@ -202,9 +235,13 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seq_len": w.seqlen, "storage": w.dtype, "z_gate": w.has_z,
                    "last_state": w.last_state, "kernel": args.kernel, "buffer_sets": len(sets)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": alg_bytes,
+        "roofline": {"bound": "alu", "achieved": round(achieved_tflops, 2),
+                     "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved_tflops / VALU_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(w, args.kernel),
+                     "valu_slots_per_launch": slots, "algorithmic_bytes": alg_bytes,
+                     "hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)},
                      "mean_launch_us": round(mean_launch_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "parity_sample": check,

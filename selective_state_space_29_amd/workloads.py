@@ -76,7 +76,7 @@ WORKLOADS = {
 
 def a_matrix(dim: int, dstate: int) -> np.ndarray:
     """A[d, n] = -(n + 1), fp32, exactly."""
-    return np.array(np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), (dim, dstate)))
+    return np.tile(-(np.arange(dstate, dtype=np.float32) + 1.0), (dim, 1))  # C-contiguous
 
 
 def _vec(w: Workload, which: str, dist: str) -> np.ndarray:

@@ -77,7 +77,7 @@ def case(seed, batch, dim, N, L, dtype="f32", z=True, D=True, bias=True, a_kind=
         return v
 
     if a_kind == "mamba":
-        A = np.array(np.broadcast_to(-(np.arange(N, dtype=np.float32) + 1), (dim, N)))
+        A = np.tile(-(np.arange(N, dtype=np.float32) + 1), (dim, 1))
     else:
         A = (-rng.uniform(0.05, 4.0, (dim, N))).astype(np.float32)
     return dict(

@@ -1,0 +1,27 @@
+"""Host-side checks of bench.py: the one-GPU contract and the traffic record."""
+
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "8"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_traffic_is_reported_only_for_the_profiled_sources():
+    import bench
+    from selective_state_space_29_amd import workloads
+
+    rec = json.load(open(bench.TRAFFIC_RECORD))
+    w3 = workloads.WORKLOADS[3]
+    expect = rec["traffic_bytes_per_launch"] if rec["source_sha256"] == bench.kernel_source_hash() else None
+    assert bench.measured_traffic(w3, "auto") == expect
+    assert bench.measured_traffic(w3, "generic") is None
+    assert bench.measured_traffic(workloads.WORKLOADS[4], "auto") is None

@@ -107,3 +107,10 @@ def test_row_problems_reproduce_full_oracle_rows():
     yr, lr = gu.oracle_rows(workloads.make_row_inputs(w, rows), softplus=w.softplus)
     assert np.array_equal(yr, yf.reshape(w.rows, -1)[rows])
     assert np.array_equal(lr, lf.reshape(w.rows, -1)[rows])
+
+
+def test_parameter_arrays_are_c_contiguous():
+    for w in workloads.WORKLOADS.values():
+        if w.dim * w.dstate > 1:
+            p = workloads.make_params(w)
+            assert p["A"].flags["C_CONTIGUOUS"] and p["A"].strides == (4 * w.dstate, 4)
