@@ -31,6 +31,7 @@ VALU_PEAK_TFLOPS = 157.3
 SLOTS_PER_ELEMENT = 8      # mul (dt*A), exp, mul (dt*u*B), fma (h), fma (y)
 SLOTS_PER_ROW_STEP = 30    # softplus, dt*u, bias, skip, silu gate
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "scan_tiled_mamba130m_traffic.json")
+RATES_LIB = os.path.join(ROOT, "selective_state_space_29_amd", "probe", "libmscan_rates.so")
 
 
 def parse():
@@ -93,6 +94,45 @@ def measured_traffic(w, kernel):
     if w.wid != 3 or kernel not in ("auto", "tiled") or rec.get("source_sha256") != kernel_source_hash():
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def measured_rates():
+    """Whole-GPU fp32 FMA and v_exp_f32 issue rates (lane-ops/s) from the microkernels, or None
+    when their library is not built."""
+    import ctypes
+
+    if not os.path.exists(RATES_LIB):
+        return None
+    lib = ctypes.CDLL(RATES_LIB)
+    lib.mscan_measure_rates.restype = ctypes.c_int
+    lib.mscan_measure_rates.argtypes = [ctypes.POINTER(ctypes.c_double)]
+    r = (ctypes.c_double * 2)()
+    if lib.mscan_measure_rates(r) != 0:
+        return None
+    return {"fma_T_lane_ops_per_s": round(r[0] / 1e12, 2), "exp_T_lane_ops_per_s": round(r[1] / 1e12, 2)}
+
+
+def transcendentals_per_launch(w):
+    """One exp per element; per (b, d, t) softplus (exp, log) or exp, and silu (exp, rcp)."""
+    per_row_step = (2 if w.softplus else 1) + (2 if w.has_z else 0)
+    return w.elements + w.rows * w.seqlen * per_row_step
+
+
+def cpu_baseline_one_thread(w, inputs):
+    """fp64 oracle on one thread over batch 0 of the workload (all its channels)."""
+    import oracle
+
+    one = {k: (None if v is None else (v[:1] if k in ("u", "delta", "z", "B", "C") else v))
+           for k, v in inputs.items()}
+    t0 = time.perf_counter()
+    oracle.selective_scan(one["u"], one["delta"], one["A"], one["B"], one["C"], D=one["D"],
+                          z=one["z"], delta_bias=one["delta_bias"], delta_softplus=w.softplus,
+                          nthreads=1)
+    dt = time.perf_counter() - t0
+    n = w.dim * w.seqlen * w.dstate
+    return {"value": round(n / dt / 1e9, 4), "unit": "Gelem/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch 0 of the workload ({w.dim} rows x {w.seqlen} steps x {w.dstate} "
+                      f"states), fp64, {dt:.2f} s on one thread"}
 
 
 def cpu_baseline(w, inputs):
@@ -213,11 +253,21 @@ def main():
                  "max_rel_err_last_state": float(np.max(np.abs(lg - lr) / (1 + np.abs(lr))))}
         log(f"sampled parity: {check}")
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on the whole workload")
         cpu = cpu_baseline(w, x)
         log(f"cpu baseline: {cpu}")
+        cpu1 = cpu_baseline_one_thread(w, x)
+        log(f"cpu baseline, one thread: {cpu1}")
+
+    rates = measured_rates()
+    log(f"measured issue rates: {rates}")
+    n_trans = transcendentals_per_launch(w)
+    trans_rate = n_trans / (mean_launch_ms * 1e-3) / 1e12
+    trans = {"ops_per_launch": n_trans, "achieved_T_per_s": round(trans_rate, 3),
+             "measured_peak_T_per_s": None if rates is None else rates["exp_T_lane_ops_per_s"],
+             "frac": None if rates is None else round(trans_rate / rates["exp_T_lane_ops_per_s"], 4)}
 
     out = {
         "metric": "scan Gelem/s (B*D*L*N) + % HBM roofline, Mamba-130m layer shape, L=2048",
@@ -230,7 +280,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32 arithmetic, bf16 storage" if w.dtype == "bf16" else "f32",
+        "dtype": "f32",
         "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seq_len": w.seqlen, "storage": w.dtype, "z_gate": w.has_z,
@@ -242,8 +292,11 @@ def main():
                      "valu_slots_per_launch": slots, "algorithmic_bytes": alg_bytes,
                      "hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)},
+                     "transcendental": trans,
+                     "measured_rates": rates,
                      "mean_launch_us": round(mean_launch_ms * 1e3, 2)},
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
         "parity_sample": check,
     }
     print(json.dumps(out), flush=True)

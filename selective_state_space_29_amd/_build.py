@@ -4,6 +4,8 @@
   instructions are disabled (``-target-feature -packed-fp32-ops``): the kernels' arithmetic is
   plain fp32 FMA/MUL plus the hardware transcendentals.
 * ``gen/libssm_gen.so``: the seeded input generator (plain gcc).
+* ``probe/libmscan_rates.so``: FMA and exp issue-rate microkernels the benchmark reports its
+  rooflines against (not part of the scan library).
 """
 
 from __future__ import annotations
@@ -45,6 +47,19 @@ def build_hip(out: str = LIB, extra=()) -> str:
     return out
 
 
+RATES_SRC = os.path.join(HERE, "probe", "rates.hip")
+RATES_LIB = os.path.join(HERE, "probe", "libmscan_rates.so")
+
+
+def build_rates(out: str = RATES_LIB) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = out + ".tmp"
+    subprocess.run([hipcc, *HIPCC_FLAGS, "-o", tmp, RATES_SRC], check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def build_all() -> None:
     build_hip()
+    build_rates()
     _gen.build(force=True)
