@@ -44,6 +44,11 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--decode", action="store_true",
+                    help="instead of the one-shot scan, time recurrent decode: each call advances "
+                         "the state by --chunk steps from the previous call's last_state")
+    ap.add_argument("--chunk", type=int, default=1, help="steps per decode call")
+    ap.add_argument("--decode-calls", type=int, default=256, help="timed decode calls")
     ap.add_argument("--copy-mb", type=float, default=0.0,
                     help="instead of the scan, time a plain device copy of this many MB "
                          "(calibrates the HBM byte counters)")
@@ -151,6 +156,131 @@ def cpu_baseline(w, inputs):
                       f"fp64, {dt:.2f} s wall on {cores} threads"}
 
 
+def decode_bench(args):
+    """Recurrent decode / streaming continuation at the workload's channel shape: call i scans
+    steps [i*chunk, (i+1)*chunk) of the workload's sequence starting from call i-1's last_state
+    (two state buffers in turn). Per call the library reads u, delta, z (chunk steps), B, C, A, D,
+    delta_bias and h0 and writes y and last_state. `value` is the GPU time per call with the calls
+    captured in one HIP graph (median of 5 replays, each checked against the eager state); the
+    eager per-call times, which include Python argument marshalling, are reported beside it."""
+    import numpy as np
+    import torch
+
+    from selective_state_space_29_amd import scan, workloads
+    import oracle
+
+    w = workloads.WORKLOADS[args.workload]
+    C = args.chunk
+    calls = args.decode_calls
+    if C < 1 or calls < 1 or calls * C > w.seqlen:
+        print(f"--chunk {C} x --decode-calls {calls} must fit in L = {w.seqlen}", file=sys.stderr)
+        sys.exit(2)
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    seq = ("u", "delta", "z", "B", "C")
+    full = {k: (None if v is None else to_dev(v)) for k, v in x.items()}
+    pieces = [{k: (full[k][..., i * C:(i + 1) * C].contiguous() if (k in seq and full[k] is not None)
+                   else full[k]) for k in full} for i in range(calls)]
+    ys = [torch.empty((w.batch, w.dim, C), dtype=torch.float32, device=dev) for _ in range(calls)]
+    hs = [torch.zeros((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def call(i, h0):
+        p = pieces[i]
+        scan.selective_scan_fn(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
+                               delta_bias=p["delta_bias"], delta_softplus=w.softplus,
+                               return_last_state=True, h0=h0, out=ys[i],
+                               last_state_out=hs[(i + 1) % 2])
+
+    def run_all():
+        for i in range(calls):
+            call(i, None if i == 0 else hs[i % 2])
+
+    for i in range(min(args.warmup, calls)):
+        call(i, hs[i % 2])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    # eager: one event pair per call (host-side argument marshalling included when the GPU waits)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for i in range(calls):
+        ev[i][0].record(stream)
+        call(i, None if i == 0 else hs[i % 2])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    eager_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    eager_state = hs[calls % 2].clone()
+    # the same calls captured once in a HIP graph and replayed: the GPU-side cost per call
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_all()
+    reps = 5
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    replay_ok = True
+    for r in range(reps):
+        hs[0].fill_(float("nan"))
+        hs[1].fill_(float("nan"))
+        gev[r][0].record(stream)
+        graph.replay()
+        gev[r][1].record(stream)
+        torch.cuda.synchronize()
+        replay_ok &= bool(torch.equal(hs[calls % 2], eager_state))
+    per_call_us = np.array([a.elapsed_time(b) * 1e3 / calls for a, b in gev])
+    mean_us = float(np.median(per_call_us))
+    es = 2 if w.dtype == "bf16" else 4
+    nbytes = (3 * w.rows * C * es + 2 * w.batch * w.dstate * C * es + w.dim * (w.dstate + 2) * 4
+              + 2 * w.rows * w.dstate * 4 + w.rows * C * 4)
+    gbs = nbytes / (mean_us * 1e-6) / 1e9
+
+    # the state after `calls` calls against the oracle over the same steps, on sampled rows
+    rows = sorted({0, 1535 % w.rows, w.rows // 2, w.rows - 1} |
+                  {int(r) for r in np.random.default_rng(5).integers(0, w.rows, 12)})
+    xr = workloads.make_row_inputs(w, rows)
+    lr = []
+    for i in range(len(rows)):
+        s1 = slice(i, i + 1)
+        cut = {k: (None if xr[k] is None else
+                   (np.ascontiguousarray(xr[k][s1][..., :calls * C]) if k in seq else xr[k][s1]))
+               for k in xr}
+        _, l1 = oracle.selective_scan(cut["u"], cut["delta"], cut["A"], cut["B"], cut["C"],
+                                      D=cut["D"], z=cut["z"], delta_bias=cut["delta_bias"],
+                                      delta_softplus=w.softplus)
+        lr.append(l1.reshape(-1))
+    lg = hs[calls % 2].reshape(w.rows, w.dstate)[torch.tensor(rows, device=dev)].cpu().numpy()
+    lr = np.stack(lr)
+    err = float(np.max(np.abs(lg - lr) / (1 + np.abs(lr))))
+
+    out = {
+        "metric": f"recurrent decode, {C} step(s) per call from the previous call's state",
+        "value": round(mean_us, 3),
+        "unit": "us per call",
+        "n_gpus": 1,
+        "steps": calls,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator)",
+        "config": {"workload": w.name + "-decode", "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
+                   "steps_per_call": C, "storage": w.dtype},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                     "algorithmic_bytes_per_call": nbytes},
+        "timing": {"graph_replay_us_per_call": [round(float(v), 3) for v in per_call_us],
+                   "eager_us_per_call_mean": round(float(eager_us.mean()), 3),
+                   "eager_us_per_call_min": round(float(eager_us.min()), 3)},
+        "parity_sample": {"rows": len(rows), "steps": calls * C, "max_rel_err_last_state": err,
+                          "graph_replays_equal_eager": replay_ok},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -166,6 +296,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.decode:
+        decode_bench(args)
+        return
     if args.copy_mb > 0:
         copy_calibration(args.copy_mb, args.steps, args.warmup)
         return

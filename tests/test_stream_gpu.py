@@ -1,0 +1,133 @@
+"""Recurrent decode and streaming continuation on the GPU: the sequence fed in pieces (one step
+at a time, or chunks of any length), each call starting from the previous call's last_state as
+h0, must reproduce the one-shot scan.
+
+* With the same kernel for every call the result is bit-identical: the carried state is the exact
+  fp32 state and each step runs the same fp32 operations in the same order.
+* Across kernels (the library picks the generic kernel for pieces whose rows are not 4-step
+  aligned) last_state stays bit-identical; y may differ in the order the states' contributions are
+  summed, so it is held to the oracle's bar instead.
+* Against the fp64 oracle (the recurrence of "Mamba代码实战…" §3.2 started from the given state,
+  "手把手用PyTorch实现Mamba的SSM层…" §3.1) the pieces meet the same bar as the one-shot scan.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from selective_state_space_29_amd import scan
+
+pytestmark = pytest.mark.gpu
+
+SEQ = ("u", "delta", "z", "B", "C")
+
+
+def _dev_case(x):
+    return {k: gu.to_dev(v) if isinstance(v, np.ndarray) else v for k, v in x.items()}
+
+
+def _call(g, t0, t1, h0, kernel):
+    piece = {k: (g[k][..., t0:t1].contiguous() if (k in SEQ and g[k] is not None) else g[k]) for k in g}
+    return scan.selective_scan_fn(
+        piece["u"], piece["delta"], piece["A"], piece["B"], piece["C"], D=piece["D"], z=piece["z"],
+        delta_bias=piece["delta_bias"], delta_softplus=True, return_last_state=True, h0=h0,
+        kernel=kernel)
+
+
+def _stream(g, cuts, kernel, h0=None):
+    ys = []
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        y, h0 = _call(g, t0, t1, h0, kernel)
+        ys.append(y)
+    torch.cuda.synchronize()
+    return torch.cat(ys, -1).cpu().numpy(), h0.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_step_decode_reproduces_the_scan(dtype):
+    x = gu.case(61, 2, 80, 16, 40, dtype=dtype)
+    g = _dev_case(x)
+    L = x["u"].shape[-1]
+    y_full, ls_full = _call(g, 0, L, None, "generic")
+    y_dec, ls_dec = _stream(g, list(range(L + 1)), "generic")
+    assert np.array_equal(y_dec, y_full.cpu().numpy())
+    assert np.array_equal(ls_dec, ls_full.cpu().numpy())
+    # the library's own choice for the one-shot call
+    y_auto, ls_auto = _call(g, 0, L, None, None)
+    assert np.array_equal(ls_dec, ls_auto.cpu().numpy())
+    tol = gu.BF16_TOL if dtype == "bf16" else gu.FP32_TOL
+    assert gu.rel_err(y_dec, y_auto.cpu().numpy()) <= 1e-6
+    yr, lr = gu.oracle_scan(x)
+    assert gu.rel_err(y_dec, yr) <= tol and gu.rel_err(ls_dec, lr) <= tol
+
+
+@pytest.mark.parametrize("kernel", [None, "generic"], ids=lambda k: k or "auto")
+def test_irregular_chunks_reproduce_the_scan(kernel):
+    x = gu.case(62, 3, 130, 16, 512, dtype="bf16")
+    g = _dev_case(x)
+    cuts = [0, 1, 8, 72, 172, 175, 256, 288, 511, 512]
+    y_s, ls_s = _stream(g, cuts, kernel)
+    y_full, ls_full = _call(g, 0, 512, None, kernel)
+    y_full, ls_full = y_full.cpu().numpy(), ls_full.cpu().numpy()
+    assert np.array_equal(ls_s, ls_full)
+    if kernel == "generic":
+        assert np.array_equal(y_s, y_full)
+    else:
+        assert gu.rel_err(y_s, y_full) <= 1e-6
+    yr, lr = gu.oracle_scan(x)
+    assert gu.rel_err(y_s, yr) <= gu.BF16_TOL and gu.rel_err(ls_s, lr) <= gu.BF16_TOL
+
+
+def test_decode_from_a_given_state_at_the_mamba130m_width():
+    """Decode steps of the full channel count (1536) from a nonzero state, against the oracle
+    started from the same state."""
+    x = gu.case(63, 2, 1536, 16, 6, dtype="bf16")
+    rng = np.random.default_rng(64)
+    h0 = rng.standard_normal((2, 1536, 16)).astype(np.float32)
+    g = _dev_case(x)
+    y_dec, ls_dec = _stream(g, list(range(7)), None, h0=gu.to_dev(h0))
+    yr, lr = gu.oracle_scan(x, h0=h0)
+    assert np.all(np.isfinite(y_dec)) and np.all(np.isfinite(ls_dec))
+    assert gu.rel_err(y_dec, yr) <= gu.BF16_TOL and gu.rel_err(ls_dec, lr) <= gu.BF16_TOL
+
+
+def test_decode_calls_captured_in_a_graph_replay_exactly():
+    """The library launches on the caller's stream and allocates nothing, so a decode loop can be
+    captured in a HIP graph; every replay (with eager library work in between) equals the eager
+    result."""
+    x = gu.case(65, 2, 96, 16, 12, dtype="bf16")
+    g = _dev_case(x)
+    L = x["u"].shape[-1]
+    dev = g["u"].device
+    pieces = [{k: (g[k][..., t:t + 1].contiguous() if (k in SEQ and g[k] is not None) else g[k]) for k in g}
+              for t in range(L)]
+    ys = [torch.empty((2, 96, 1), dtype=torch.float32, device=dev) for _ in range(L)]
+    hs = [torch.zeros((2, 96, 16), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def run():
+        for t in range(L):
+            p = pieces[t]
+            scan.selective_scan_fn(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
+                                   delta_bias=p["delta_bias"], delta_softplus=True,
+                                   return_last_state=True, h0=None if t == 0 else hs[t % 2],
+                                   out=ys[t], last_state_out=hs[(t + 1) % 2])
+
+    run()
+    torch.cuda.synchronize()
+    y_eager = torch.cat(ys, -1).clone()
+    ls_eager = hs[L % 2].clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        hs[0].fill_(float("nan"))
+        hs[1].fill_(float("nan"))
+        gu.gpu_scan(gu.case(66 + rep, 1, 70, 16, 33), kernel=None)  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(ys, -1), y_eager), f"replay {rep}"
+        assert torch.equal(hs[L % 2], ls_eager), f"replay {rep}"
