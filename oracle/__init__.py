@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the selective-scan forward pass (wrapper over ``scan_oracle.c``).
+"""fp64 CPU oracle of the selective-scan forward and backward passes (wrapper over ``scan_oracle.c``).
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU-baseline leg may use
 it; the product path never does. It shares no code with the HIP library. Which passage of the
@@ -9,6 +9,9 @@ Every function of the oracle is pinned by CPU tests against things other than it
 ``lfilter`` and numpy's ``cumsum`` special cases, invariants, and the pages' own einsum loop run
 in torch fp64). One reading is not pinned by any page value: the exp branch taken when
 ``delta_softplus`` is false ("parity unpinned" beyond the text of the page that defines it).
+
+The backward pass (``selective_scan_bwd``) is pinned by central finite differences of the forward
+oracle and by torch's fp64 CPU autograd through an independent step-by-step formulation.
 """
 
 from __future__ import annotations
@@ -47,12 +50,21 @@ def _bind(path: str):
     return lib
 
 
+def _bind_bwd(lib):
+    f = lib.oracle_selective_scan_bwd
+    f.restype = ctypes.c_int
+    P = ctypes.c_void_p
+    f.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int] + [P] * 5 + [P] * 4 + [ctypes.c_int] + [
+        P] * 11 + [ctypes.c_int]
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
             build(force=False)
-        _lib = _bind(_LIB)
+        _lib = _bind_bwd(_bind(_LIB))
     return _lib
 
 
@@ -123,3 +135,49 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     if rows is None:
         return y.reshape(batch, dim, L), ls.reshape(batch, dim, N)
     return y, ls
+
+
+def selective_scan_bwd(u, delta, A, B, C, gy, D=None, z=None, delta_bias=None,
+                       delta_softplus=False, h0=None, glast=None, nthreads=None, lib_path=None):
+    """Gradients of a loss with dLoss/dy = gy (batch, dim, L) and dLoss/dlast_state = glast
+    (batch, dim, N) or None, in fp64. Inputs as for ``selective_scan``.
+
+    Returns a dict: u, delta, z (batch, dim, L; z only when given), B, C (batch, N, L), A (dim, N),
+    D, delta_bias (dim,) and h0 (batch, dim, N), all fp64.
+    """
+    lib = _bind_bwd(_bind(lib_path)) if lib_path else _load()
+    u, delta, B, C = (_as(x, "in") for x in (u, delta, B, C))
+    z = _as(z, "in")
+    kinds = {x.dtype for x in (u, delta, B, C) + ((z,) if z is not None else ())}
+    if len(kinds) != 1:
+        raise TypeError("u, delta, z, B, C must share one storage dtype")
+    in_dtype = 1 if kinds.pop() == np.uint16 else 0
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    A = _as(A, "p")
+    D = _as(D, "p")
+    delta_bias = _as(delta_bias, "p")
+    h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+    gy = np.ascontiguousarray(gy, dtype=np.float64)
+    glast = None if glast is None else np.ascontiguousarray(glast, dtype=np.float64)
+    if gy.shape != (batch, dim, L) or (glast is not None and glast.shape != (batch, dim, N)):
+        raise ValueError("gy must be (batch, dim, L) and glast (batch, dim, N)")
+    out = {k: np.zeros(shape, dtype=np.float64) for k, shape in (
+        ("u", (batch, dim, L)), ("delta", (batch, dim, L)), ("z", (batch, dim, L)),
+        ("B", (batch, N, L)), ("C", (batch, N, L)), ("A", (dim, N)), ("D", (dim,)),
+        ("delta_bias", (dim,)), ("h0", (batch, dim, N)))}
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data
+
+    rc = lib.oracle_selective_scan_bwd(
+        batch, dim, L, N, in_dtype, ptr(u), ptr(delta), ptr(z), ptr(B), ptr(C), ptr(A), ptr(D),
+        ptr(delta_bias), ptr(h0), int(bool(delta_softplus)), ptr(gy), ptr(glast),
+        ptr(out["u"]), ptr(out["delta"]), ptr(out["z"]), ptr(out["B"]), ptr(out["C"]),
+        ptr(out["A"]), ptr(out["D"]), ptr(out["delta_bias"]), ptr(out["h0"]),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_selective_scan_bwd failed with {rc}")
+    if z is None:
+        del out["z"]
+    return out

@@ -152,3 +152,197 @@ int oracle_selective_scan(int64_t batch, int64_t dim, int64_t len, int64_t dstat
         if (orc_worker(&jobs[t]) != NULL) ok = 0;
     return ok ? 0 : -8;
 }
+
+/* ----------------------------------------------------------------------------------------------
+ * Backward pass: the gradients of a scalar loss that depends on the scan through y (gradient gy,
+ * (batch, D, L)) and through the final state (gradient glast, (batch, D, N), or none).
+ *
+ * Training is what "手把手用PyTorch实现Mamba的SSM层…" §4.2 (memory-efficient training: states are
+ * not kept from the forward pass but recomputed for the backward) and "Mamba代码实战…" §7 (item 3,
+ * an efficient backward pass by automatic differentiation) ask of the scan. The derivative has a
+ * plain definition; this is it written out by the chain rule through the forward recurrence
+ * above, taken in reverse step order. With x = delta + bias, dt = softplus(x) (or exp(x)),
+ * a_n = exp(dt A[d,n]), h_t = a h_{t-1} + dt B_t u_t, p_t = sum_n C_t h_t + D u_t, y_t = p_t g_t,
+ * g_t = silu(z_t) (1 without z), and lam_t = dLoss/dh_t (lam after the last step = glast):
+ *   gp_t = gy_t g_t;  gz_t = gy_t p_t silu'(z_t);  lam_t += gp_t C_t
+ *   gC[b,n,t] += gp_t h_t;  gB[b,n,t] += lam_t dt_t u_t  (summed over d)
+ *   gu_t = gp_t D + sum_n lam_t dt_t B_t
+ *   gdt_t = sum_n lam_t (a_t h_{t-1} A + B_t u_t);  gA[d,n] += lam_t a_t h_{t-1} dt_t (summed over b, t)
+ *   gx_t = gdt_t sigmoid(x_t) (softplus) or gdt_t dt_t (exp);  gdelta_t = gx_t;  gbias[d] += gx_t
+ *   gD[d] += gp_t u_t;  then lam_{t-1} = a_t lam_t;  gh0 = lam before the first step.
+ * Each row keeps its forward states (fp64); the reductions over rows use per-thread fp64
+ * partial sums added in thread order.
+ * ---------------------------------------------------------------------------------------------- */
+
+typedef struct {
+    const orc_args* f;              /* forward inputs (y, last_state, rows unused) */
+    const double *gy, *glast;
+    double *gu, *gdelta, *gz;       /* (batch, D, L) */
+    double *gh0;                    /* (batch, D, N) or NULL */
+    /* per-thread partials: gB, gC (batch, N, L), gA (D, N), gD, gbias (D) */
+    double *pB, *pC, *pA, *pD, *pbias;
+    int64_t begin, end;
+} orc_bwd_job;
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static void bwd_row(const orc_bwd_job* j, int64_t b, int64_t d, double* hist, double* lam) {
+    const orc_args* a = j->f;
+    const int64_t L = a->len, N = a->dstate, D = a->dim;
+    const int64_t row_off = (b * D + d) * L;
+    const int64_t bc_off = b * N * L;
+    const double bias = a->delta_bias ? (double)a->delta_bias[d] : 0.0;
+    const double dskip = a->Dvec ? (double)a->Dvec[d] : 0.0;
+    /* forward, keeping h_{t} for t = -1 .. L-1 in hist[(t + 1) * N + n] */
+    for (int64_t n = 0; n < N; ++n) hist[n] = a->h0 ? a->h0[(b * D + d) * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const double x = widen(a->delta, a->in_dtype, row_off + t) + bias;
+        const double dt = a->delta_softplus ? softplus(x) : exp(x);
+        const double ut = widen(a->u, a->in_dtype, row_off + t);
+        for (int64_t n = 0; n < N; ++n) {
+            const double Bt = widen(a->B, a->in_dtype, bc_off + n * L + t);
+            hist[(t + 1) * N + n] = exp(dt * (double)a->A[d * N + n]) * hist[t * N + n] + dt * Bt * ut;
+        }
+    }
+    for (int64_t n = 0; n < N; ++n) lam[n] = j->glast ? j->glast[(b * D + d) * N + n] : 0.0;
+    double gD = 0.0, gbias = 0.0;
+    for (int64_t t = L - 1; t >= 0; --t) {
+        const double x = widen(a->delta, a->in_dtype, row_off + t) + bias;
+        const double dt = a->delta_softplus ? softplus(x) : exp(x);
+        const double ut = widen(a->u, a->in_dtype, row_off + t);
+        const double* h = hist + (t + 1) * N;
+        const double* hprev = hist + t * N;
+        double s = 0.0;
+        for (int64_t n = 0; n < N; ++n) s += widen(a->C, a->in_dtype, bc_off + n * L + t) * h[n];
+        const double p = s + dskip * ut;
+        double g = 1.0;
+        const double gyt = j->gy[row_off + t];
+        if (a->z) {
+            const double zt = widen(a->z, a->in_dtype, row_off + t);
+            const double sg = sigmoid(zt);
+            g = zt * sg;
+            j->gz[row_off + t] = gyt * p * (sg + zt * sg * (1.0 - sg));
+        }
+        const double gp = gyt * g;
+        gD += gp * ut;
+        double gu = gp * dskip, gdt = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double Bt = widen(a->B, a->in_dtype, bc_off + n * L + t);
+            const double Ct = widen(a->C, a->in_dtype, bc_off + n * L + t);
+            const double An = (double)a->A[d * N + n];
+            const double an = exp(dt * An);
+            lam[n] += gp * Ct;
+            j->pC[bc_off + n * L + t] += gp * h[n];
+            j->pB[bc_off + n * L + t] += lam[n] * dt * ut;
+            gu += lam[n] * dt * Bt;
+            gdt += lam[n] * (an * hprev[n] * An + Bt * ut);
+            j->pA[d * N + n] += lam[n] * an * hprev[n] * dt;
+            lam[n] *= an;
+        }
+        const double gx = a->delta_softplus ? gdt * sigmoid(x) : gdt * dt;
+        j->gdelta[row_off + t] = gx;
+        j->gu[row_off + t] = gu;
+        gbias += gx;
+    }
+    if (j->gh0)
+        for (int64_t n = 0; n < N; ++n) j->gh0[(b * D + d) * N + n] = lam[n];
+    j->pD[d] += gD;
+    j->pbias[d] += gbias;
+}
+
+static void* orc_bwd_worker(void* p) {
+    const orc_bwd_job* j = (const orc_bwd_job*)p;
+    const int64_t N = j->f->dstate;
+    double* hist = (double*)malloc(sizeof(double) * (size_t)((j->f->len + 1) * N));
+    double* lam = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!hist || !lam) {
+        free(hist);
+        free(lam);
+        return (void*)1;
+    }
+    for (int64_t k = j->begin; k < j->end; ++k) bwd_row(j, k / j->f->dim, k % j->f->dim, hist, lam);
+    free(hist);
+    free(lam);
+    return NULL;
+}
+
+/*
+ * Gradients of the scan (all fp64, contiguous). gy (batch, D, L) is required; glast (batch, D, N)
+ * may be NULL (no loss on the final state). Outputs: gu, gdelta (batch, D, L); gz (batch, D, L),
+ * required when z is given; gB, gC (batch, N, L); gA (D, N); gD, gbias (D); gh0 (batch, D, N) or
+ * NULL. gz/gD/gbias are written even when z/D/delta_bias are absent (then as if they were zero,
+ * with gz left untouched). Returns 0, or a negative value on a bad argument or allocation failure.
+ */
+int oracle_selective_scan_bwd(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int in_dtype,
+                              const void* u, const void* delta, const void* z, const void* B,
+                              const void* C, const float* A, const float* Dvec,
+                              const float* delta_bias, const double* h0, int delta_softplus,
+                              const double* gy, const double* glast, double* gu, double* gdelta,
+                              double* gz, double* gB, double* gC, double* gA, double* gD,
+                              double* gbias, double* gh0, int nthreads) {
+    if (batch <= 0 || dim <= 0 || len <= 0 || dstate <= 0) return -2;
+    if (in_dtype != ORC_F32 && in_dtype != ORC_BF16) return -4;
+    if (!u || !delta || !B || !C || !A || !gy || !gu || !gdelta || !gB || !gC || !gA || !gD || !gbias)
+        return -1;
+    if (z && !gz) return -1;
+    orc_args f = {batch, dim, len, dstate, in_dtype, u, delta, z, B, C, A, Dvec, delta_bias, h0,
+                  delta_softplus, NULL, batch * dim, NULL, NULL};
+    const int64_t nrows = batch * dim;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > ORC_MAX_THREADS) nthreads = ORC_MAX_THREADS;
+    if (nthreads > nrows) nthreads = (int)nrows;
+    const int64_t nbc = batch * dstate * len, na = dim * dstate;
+    const int64_t per_thread = 2 * nbc + na + 2 * dim;
+    double* part = (double*)calloc((size_t)(per_thread * nthreads), sizeof(double));
+    if (!part) return -8;
+    orc_bwd_job jobs[ORC_MAX_THREADS];
+    pthread_t tids[ORC_MAX_THREADS];
+    const int64_t per = (nrows + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        double* q = part + per_thread * t;
+        orc_bwd_job j = {&f, gy, glast, gu, gdelta, gz, gh0, q, q + nbc, q + 2 * nbc, q + 2 * nbc + na,
+                         q + 2 * nbc + na + dim, per * t < nrows ? per * t : nrows,
+                         per * (t + 1) < nrows ? per * (t + 1) : nrows};
+        jobs[t] = j;
+    }
+    int ok = 1, started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, orc_bwd_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    if (orc_bwd_worker(&jobs[0]) != NULL) ok = 0;
+    for (int t = 1; t <= started; ++t) {
+        void* r = NULL;
+        pthread_join(tids[t], &r);
+        if (r != NULL) ok = 0;
+    }
+    for (int t = started + 1; t < nthreads; ++t)
+        if (orc_bwd_worker(&jobs[t]) != NULL) ok = 0;
+    if (ok) {
+        for (int64_t i = 0; i < nbc; ++i) {
+            double sb = 0.0, sc = 0.0;
+            for (int t = 0; t < nthreads; ++t) {
+                sb += jobs[t].pB[i];
+                sc += jobs[t].pC[i];
+            }
+            gB[i] = sb;
+            gC[i] = sc;
+        }
+        for (int64_t i = 0; i < na; ++i) {
+            double s = 0.0;
+            for (int t = 0; t < nthreads; ++t) s += jobs[t].pA[i];
+            gA[i] = s;
+        }
+        for (int64_t i = 0; i < dim; ++i) {
+            double sd = 0.0, sb = 0.0;
+            for (int t = 0; t < nthreads; ++t) {
+                sd += jobs[t].pD[i];
+                sb += jobs[t].pbias[i];
+            }
+            gD[i] = sd;
+            gbias[i] = sb;
+        }
+    }
+    free(part);
+    return ok ? 0 : -8;
+}

@@ -1,7 +1,8 @@
 """The pins are sharp: copies of the oracle with one planted slip each must fail a pin.
 
 Each mutant is a textual edit of a copy of ``oracle/scan_oracle.c`` compiled into a temporary
-library on the CPU; the oracle itself is never modified.
+library on the CPU; the oracle itself is never modified. Forward mutants edit the forward row
+function only (the backward repeats some of its expressions).
 """
 
 import os
@@ -33,14 +34,31 @@ MUTANTS = {
 }
 
 
+# mutants of the shared helpers are scoped to the helper itself
+HELPER_SCOPE = {
+    "gate_sigmoid_only": "static double silu(",
+    "bf16_widen_shift": "static double widen(",
+    "softplus_no_log1p": "static double softplus(",
+}
+
+
+def mutate(src, func_head, old, new, name):
+    """Replace `old` by `new` inside the body of the function starting at `func_head` (the site
+    must occur there exactly once)."""
+    a = src.index(func_head)
+    b = src.index("\n}\n", a) + 3
+    body = src[a:b]
+    assert body.count(old) == 1, f"mutation site for {name} not found exactly once"
+    return src[:a] + body.replace(old, new) + src[b:]
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_fails_some_pin(oracle_mod, tmp_path, name):
     old, new = MUTANTS[name]
     src = open(oracle_mod.SOURCE).read()
-    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
     mutant_c = os.path.join(tmp_path, f"{name}.c")
     with open(mutant_c, "w") as f:
-        f.write(src.replace(old, new))
+        f.write(mutate(src, HELPER_SCOPE.get(name, "static void scan_row("), old, new, name))
     lib = oracle_mod.build(force=True, source=mutant_c, out=os.path.join(tmp_path, f"{name}.so"))
 
     def scan(**kw):
