@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="instead of the one-shot scan, time recurrent decode: each call advances "
                          "the state by --chunk steps from the previous call's last_state")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward scan, time the backward pass (mamba_scan_bwd)")
     ap.add_argument("--chunk", type=int, default=1, help="steps per decode call")
     ap.add_argument("--decode-calls", type=int, default=256, help="timed decode calls")
     ap.add_argument("--copy-mb", type=float, default=0.0,
@@ -281,6 +283,93 @@ def decode_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def backward_bench(args):
+    """The backward pass at the workload's shape: gradients of sum(dy * y) + sum(dl * last_state)
+    for seeded dy, dl. One step = one mamba_scan_bwd call (B/C widening, the two-phase scan,
+    the fixed-order reduction), timed with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    from selective_state_space_29_amd import scan, workloads
+    import oracle
+
+    w = workloads.WORKLOADS[args.workload]
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    g = {k: to_dev(v) for k, v in x.items()}
+    rng = np.random.default_rng(11)
+    dy_np = rng.standard_normal((w.batch, w.dim, w.seqlen)).astype(np.float32)
+    dl_np = rng.standard_normal((w.batch, w.dim, w.dstate)).astype(np.float32)
+    dy, dl = torch.from_numpy(dy_np).to(dev), torch.from_numpy(dl_np).to(dev)
+
+    def step():
+        return scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"],
+                                       z=g["z"], delta_bias=g["delta_bias"],
+                                       delta_softplus=w.softplus, dlast_state=dl, want_dh0=False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    out = None
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        out = step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    mean_us = float(per_us.mean())
+
+    # parity of this run against the fp64 backward oracle on every gradient
+    ref = oracle.selective_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                    dy_np.astype(np.float64), D=x["D"], z=x["z"],
+                                    delta_bias=x["delta_bias"], delta_softplus=w.softplus,
+                                    glast=dl_np.astype(np.float64))
+    errs = {}
+    for k, v in out.items():
+        r = ref[k]
+        errs[k] = float(np.max(np.abs(v.cpu().numpy() - r) / (1 + np.abs(r))))
+
+    es = 2 if w.dtype == "bf16" else 4
+    nz = 1 if w.has_z else 0
+    read = ((2 + nz) * w.rows * w.seqlen * es + 2 * w.batch * w.dstate * w.seqlen * es
+            + w.rows * w.seqlen * 4 + w.rows * w.dstate * 4 + w.dim * (w.dstate + 2) * 4)
+    written = ((2 + nz) * w.rows * w.seqlen * 4 + 2 * w.batch * w.dstate * w.seqlen * 4
+               + w.dim * (w.dstate + 2) * 4)
+    gbs = (read + written) / (mean_us * 1e-6) / 1e9
+    res = {
+        "metric": "scan backward, Gelem/s (B*D*L*N) per mamba_scan_bwd call",
+        "value": round(w.elements / (mean_us * 1e-6) / 1e9, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator)",
+        "config": {"workload": w.name + "-backward", "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
+                   "seq_len": w.seqlen, "storage": w.dtype},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": read + written, "mean_call_us": round(mean_us, 2),
+                     "min_call_us": round(float(per_us.min()), 2)},
+        "parity": {"max_rel_err": errs},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -298,6 +387,9 @@ def main():
         sys.exit(1)
     if args.decode:
         decode_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
     if args.copy_mb > 0:
         copy_calibration(args.copy_mb, args.steps, args.warmup)

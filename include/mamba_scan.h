@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 1
+#define MAMBA_SCAN_ABI_VERSION 2
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -117,6 +117,68 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s,
  * A call given less workspace than this still runs, unsplit. Negative on invalid arguments. */
 int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype,
                                    uint32_t flags);
+
+/*
+ * Backward pass (ABI version 2).
+ *
+ * Gradients of a scalar loss that depends on the forward pass above through y (gradient dy)
+ * and, optionally, through last_state (gradient dlast_state). Sources: "手把手用PyTorch实现Mamba的
+ * SSM层…" §4.2 (memory-efficient training: the states are recomputed for the backward pass, not
+ * stored by the forward pass) and "Mamba代码实战…" §7 (item 3, an efficient backward pass); the
+ * function differentiated is the forward operation defined at the top of this file. With
+ * x = delta + delta_bias, dt = softplus(x) or exp(x), a = exp(dt*A), p = sum_n C*h + D*u:
+ *   dz = dy * p * silu'(z);   dD[d] = sum_{b,t} dy*silu(z)*u;   dh0 = dLoss/d(initial state)
+ *   du, ddelta (= dLoss/dx), dB, dC, dA, ddelta_bias[d] = sum_{b,t} ddelta
+ * by the chain rule through the recurrence, in reverse step order.
+ *
+ * Conventions
+ *  - Every tensor is CONTIGUOUS in the layouts of the forward pass (no strides argument).
+ *  - Forward inputs as in mamba_scan_ptrs (u, delta, z, B, C in `dtype`; A, D, delta_bias, h0
+ *    fp32; z, D, delta_bias, h0 may be NULL). The forward's output is not needed.
+ *  - dy (batch, dim, len) fp32 is required; dlast_state (batch, dim, dstate) fp32 may be NULL
+ *    (no loss on the final state).
+ *  - Gradients, all fp32, all written in full (never accumulated into): du, ddelta
+ *    (batch, dim, len), required; dz (batch, dim, len), required exactly when z is given;
+ *    dB, dC (batch, dstate, len), required; dA (dim, dstate), required; dD and ddelta_bias (dim),
+ *    each required exactly when D / delta_bias is given; dh0 (batch, dim, dstate) or NULL.
+ *  - Workspace: exactly mamba_scan_bwd_workspace_bytes() bytes or more, 256-byte aligned, device
+ *    memory owned by the caller (states every 16 steps, fp32 copies of B and C, partial sums).
+ *  - Flags: MAMBA_SCAN_DELTA_SOFTPLUS only.
+ *  - dstate <= 16 (MAMBA_SCAN_ERR_UNSUPPORTED above that).
+ *  - Outputs may not overlap each other, any input or the workspace (MAMBA_SCAN_ERR_ARGS).
+ *  - Enqueued on `stream`; three kernels (B/C widening, the scan, a fixed-order reduction).
+ *    Results are bitwise deterministic.
+ */
+typedef struct mamba_scan_bwd_ptrs {
+    const void* u;                /* forward inputs */
+    const void* delta;
+    const void* z;
+    const void* B;
+    const void* C;
+    const float* A;
+    const float* D;
+    const float* delta_bias;
+    const float* h0;
+    const float* dy;              /* (batch, dim, len) fp32, required */
+    const float* dlast_state;     /* (batch, dim, dstate) fp32, or NULL */
+    float* du;                    /* (batch, dim, len) */
+    float* ddelta;                /* (batch, dim, len) */
+    float* dz;                    /* (batch, dim, len) iff z */
+    float* dB;                    /* (batch, dstate, len) */
+    float* dC;                    /* (batch, dstate, len) */
+    float* dA;                    /* (dim, dstate) */
+    float* dD;                    /* (dim) iff D */
+    float* ddelta_bias;           /* (dim) iff delta_bias */
+    float* dh0;                   /* (batch, dim, dstate) or NULL */
+    void* workspace;
+    int64_t workspace_bytes;
+} mamba_scan_bwd_ptrs;
+
+int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
+                   uint32_t flags, void* stream);
+
+/* Workspace bytes mamba_scan_bwd needs for this shape (> 0), or a negative error code. */
+int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype, uint32_t flags);
 
 /* Static message for an error code; never NULL. */
 const char* mamba_scan_strerror(int code);

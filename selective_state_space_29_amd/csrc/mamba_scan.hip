@@ -7,6 +7,7 @@
 
 #include "../../include/mamba_scan.h"
 #include "common.hpp"
+#include "scan_bwd.hpp"
 #include "scan_generic.hpp"
 #include "scan_tiled.hpp"
 
@@ -187,6 +188,62 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
     if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
     return tiled_workspace_bytes(*s, flags);
+}
+
+int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype, uint32_t flags) {
+    if (!s) return MAMBA_SCAN_ERR_NULL;
+    if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
+    if (flags & ~MAMBA_SCAN_DELTA_SOFTPLUS) return MAMBA_SCAN_ERR_ARGS;
+    if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+    if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
+    return bwd_layout(*s).total;
+}
+
+int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
+                   uint32_t flags, void* stream) {
+    if (!p || !s) return MAMBA_SCAN_ERR_NULL;
+    const int64_t need = mamba_scan_bwd_workspace_bytes(s, dtype, flags);
+    if (need < 0) return (int)need;
+    if (!p->u || !p->delta || !p->B || !p->C || !p->A || !p->dy || !p->du || !p->ddelta || !p->dB ||
+        !p->dC || !p->dA)
+        return MAMBA_SCAN_ERR_NULL;
+    if ((p->z != nullptr) != (p->dz != nullptr) || (p->D != nullptr) != (p->dD != nullptr) ||
+        (p->delta_bias != nullptr) != (p->ddelta_bias != nullptr))
+        return MAMBA_SCAN_ERR_ARGS;
+    if (p->workspace_bytes < 0 || (p->workspace_bytes > 0 && !p->workspace)) return MAMBA_SCAN_ERR_ARGS;
+    if (!p->workspace || p->workspace_bytes < need) return MAMBA_SCAN_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(p->workspace) % 256 != 0) return MAMBA_SCAN_ERR_ARGS;
+    const int S = bwd_states_per_wave(s->dstate);
+    if (S == 0 || s->dstate % S != 0) return MAMBA_SCAN_ERR_UNSUPPORTED;
+    if (s->batch * ((s->dim + 63) / 64) > 0x7fffffff) return MAMBA_SCAN_ERR_UNSUPPORTED;
+
+    const int64_t es = dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+    const int64_t DL = s->batch * s->dim * s->len, NL = s->batch * s->dstate * s->len;
+    const int64_t DN = s->batch * s->dim * s->dstate;
+    auto span = [](const void* ptr, int64_t bytes) {
+        Span x{0, 0, false};
+        if (!ptr) return x;
+        x.lo = reinterpret_cast<uintptr_t>(ptr);
+        x.hi = x.lo + (uintptr_t)bytes;
+        x.valid = true;
+        return x;
+    };
+    const Span ins[] = {span(p->u, DL * es), span(p->delta, DL * es), span(p->z, DL * es), span(p->B, NL * es),
+                        span(p->C, NL * es), span(p->A, s->dim * s->dstate * 4), span(p->D, s->dim * 4),
+                        span(p->delta_bias, s->dim * 4), span(p->h0, DN * 4), span(p->dy, DL * 4),
+                        span(p->dlast_state, DN * 4), span(p->workspace, p->workspace_bytes)};
+    const Span outs[] = {span(p->du, DL * 4), span(p->ddelta, DL * 4), span(p->dz, DL * 4),
+                         span(p->dB, NL * 4), span(p->dC, NL * 4), span(p->dA, s->dim * s->dstate * 4),
+                         span(p->dD, s->dim * 4), span(p->ddelta_bias, s->dim * 4), span(p->dh0, DN * 4)};
+    for (const Span& o : outs) {
+        for (const Span& i : ins)
+            if (overlaps(o, i)) return MAMBA_SCAN_ERR_ARGS;
+        for (const Span& o2 : outs)
+            if (&o2 != &o && overlaps(o, o2)) return MAMBA_SCAN_ERR_ARGS;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool sp = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) != 0;
+    return dtype == MAMBA_SCAN_BF16 ? launch_bwd<bf16_t>(p, *s, sp, hs) : launch_bwd<float>(p, *s, sp, hs);
 }
 
 int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_scan_strides* st_in,

@@ -1,0 +1,532 @@
+// Backward pass of the selective scan for gfx950: the gradients of a loss that reaches the scan
+// through y (dy) and, optionally, through the final state (dlast_state).
+//
+// What is differentiated is the forward recurrence of "Mamba代码实战…" §3.1-§3.3 and §6 (with the
+// output contraction of "Mamba-minimal项目解析…" 关键技术点 1 and the optional initial state of
+// "手把手用PyTorch实现Mamba的SSM层…" §3.1). As "手把手用PyTorch实现Mamba的SSM层…" §4.2 (memory-efficient
+// training) prescribes, no per-step state is stored: the states are recomputed. With
+// x = delta + bias, dt = softplus(x) (or exp(x)), a = exp(dt A), h_t = a h_{t-1} + dt B_t u_t,
+// p_t = sum_n C_t h_t + D u_t, y_t = p_t g_t (g = silu(z), or 1), and lam = dLoss/dh:
+//   gp = dy g;  lam_t += gp C_t;  dC += gp h_t;  dB += lam dt u;  du = gp D + dt sum_n lam B
+//   ddt = sum_n lam (a h_{t-1} A + B u);  dA += lam a h_{t-1} dt;  ddelta = ddt softplus'(x)
+//   dz = dy p silu'(z);  dD += gp u;  dbias += ddelta;  then lam_{t-1} = a lam_t;  dh0 = lam.
+//
+// Decomposition (as the forward kernel): a workgroup owns 64 channels of one batch, one channel
+// per lane; wave w carries states w*S .. w*S+S-1 (S <= 2, so N <= 16).
+//   Phase 1: forward over 16-step segments, writing the state before each segment to the
+//            workspace (the only stored states: N floats per channel per 16 steps).
+//   Phase 2: segments in reverse. The workgroup computes the per-(channel, step) factors into
+//            LDS; each wave reloads its segment's starting state, recomputes the segment's 16
+//            states and decays in registers, then runs the reverse recurrence in two 8-step
+//            halves. After each half, the per-(channel, step) sums over states go through LDS
+//            (summed in wave order, like the forward's partial outputs) and the per-(state, step)
+//            sums over the 64 channels of dB and dC are reduced in LDS and written as one partial
+//            per workgroup.
+//   A last kernel adds the partials in a fixed order: dB, dC over the channel groups, dA, dD,
+//   dbias over the batch. Results are bitwise deterministic.
+// B and C are first widened by a pre-pass into an fp32 copy in the workspace, rows padded with
+// zeros to a multiple of 16 steps, so that a segment's values are aligned scalar loads.
+#pragma once
+
+#include "../../include/mamba_scan.h"
+#include "common.hpp"
+
+namespace mscan {
+
+struct BwdParams {
+    const void* u;
+    const void* delta;
+    const void* z;
+    const float* bc;  // fp32 B then C: (2, batch, N, lp)
+    const float* A;
+    const float* D;
+    const float* bias;
+    const float* h0;
+    const float* dy;
+    const float* dlast;
+    float* du;
+    float* ddelta;
+    float* dz;
+    float* dh0;
+    float* ck;      // (batch, dim, nseg, N) states before each segment
+    float* bcpart;  // (groups, batch, 2, N, lp) dB / dC partials of each 64-channel group
+    float* apart;   // (batch, dim, N)
+    float* dpart;   // (batch, dim)
+    float* bpart;   // (batch, dim)
+    int64_t batch, dim, len, dstate, lp, nseg, groups;
+};
+
+constexpr int kBwdW = 8;     // waves per workgroup
+constexpr int kBwdSeg = 16;  // steps per segment (checkpoint interval)
+constexpr int kBwdSub = 8;   // steps per LDS exchange
+
+typedef const __attribute__((address_space(4))) float* bwd_cptrf;
+
+template <typename T>
+__device__ __forceinline__ float load_el(const void* p, int64_t i) {
+    return to_f32(static_cast<const T*>(p)[i]);
+}
+
+template <typename T, int S, bool SOFTPLUS, bool HAS_Z, bool EXACT>
+__global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
+    constexpr int W = kBwdW, SEG = kBwdSeg, SUB = kBwdSub;
+    constexpr int QS = SEG / W;      // prologue steps per thread
+    constexpr int ROWP = SEG + 4;    // LDS row of one channel's segment
+    constexpr int SUBP = SUB + 1;    // LDS row of one channel's half-segment partials
+    static_assert(S >= 1 && S <= 2 && QS == 2 && SUB == W, "backward tiling");
+    enum { F_DT = 0, F_DTU, F_GP, F_U, F_SG, F_GZ, F_NUM };
+
+    __shared__ float s_seg[F_NUM][64 * ROWP];   // per (channel, step) factors of the segment
+    __shared__ float s_part[3][W * 64 * SUBP];  // per wave: sum lam B, sum q A, sum C h
+    __shared__ __align__(16) float s_red[W * 2 * S * SUB * 64];  // [w][dB|dC][s][t][lane]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t b = blockIdx.x / p.groups;
+    const int64_t grp = blockIdx.x - b * p.groups;
+    const int64_t d0 = grp * 64;
+    const int64_t L = p.len, N = p.dstate;
+    const int nbase = wave * S;
+    const bool wave_live = EXACT || nbase < (int)N;
+
+    // prologue / epilogue role: row r = tid / 8; prologue steps 2k, 2k+1 of a segment,
+    // epilogue step k of a half-segment (k = tid % 8)
+    const int r = tid >> 3;
+    const int k8 = tid & 7;
+    const int64_t pd = d0 + r;
+    const bool pvalid = pd < p.dim;
+    const int64_t pdc = pvalid ? pd : 0;
+    const int64_t prow = (b * p.dim + pdc) * L;
+    const float pbias = p.bias ? p.bias[pdc] : 0.0f;
+    const float pskip = p.D ? p.D[pdc] : 0.0f;
+
+    // main role: this lane's channel, this wave's states
+    const int64_t dm = d0 + lane;
+    const bool mvalid = dm < p.dim;
+    float a2[S], Av[S], h[S], lam[S], gA[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        Av[s] = 0.0f;
+        h[s] = 0.0f;
+        lam[s] = 0.0f;
+        gA[s] = 0.0f;
+        if (wave_live && mvalid) {
+            Av[s] = p.A[dm * N + nbase + s];
+            if (p.h0) h[s] = p.h0[(b * p.dim + dm) * N + nbase + s];
+            if (p.dlast) lam[s] = p.dlast[(b * p.dim + dm) * N + nbase + s];
+        }
+        a2[s] = Av[s] * kLog2e;
+    }
+    const int gclamp = wave_live ? nbase : 0;
+    const float* Brow = p.bc + (b * N + gclamp) * p.lp;              // state nbase + s at + s*lp
+    const float* Crow = p.bc + ((p.batch + b) * N + gclamp) * p.lp;
+    float* ckrow = p.ck + (b * p.dim + (mvalid ? dm : 0)) * p.nseg * N + nbase;
+
+    // zero partials for waves that hold no states (read by the epilogue, never written after)
+    if (!wave_live)
+        for (int i = lane; i < 64 * SUBP; i += 64)
+            for (int f = 0; f < 3; ++f) s_part[f][wave * 64 * SUBP + i] = 0.0f;
+
+    // ---- phase 1: forward, state before each segment to the workspace ----
+    for (int64_t k = 0; k < p.nseg; ++k) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < QS; ++j) {
+            const int64_t t = k * SEG + QS * k8 + j;
+            float dt = 0.0f, dtu = 0.0f;
+            if (t < L) {
+                const float x = load_el<T>(p.delta, prow + t) + pbias;
+                dt = SOFTPLUS ? softplus_f(x) : hw_exp2(x * kLog2e);
+                dtu = dt * load_el<T>(p.u, prow + t);
+            }
+            s_seg[F_DT][r * ROWP + QS * k8 + j] = dt;
+            s_seg[F_DTU][r * ROWP + QS * k8 + j] = dtu;
+        }
+        __syncthreads();
+        if (wave_live) {
+            if (mvalid)
+#pragma unroll
+                for (int s = 0; s < S; ++s) ckrow[k * N + s] = h[s];
+            float bv[S][SEG];
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const bwd_cptrf pb = (bwd_cptrf)(Brow + s * p.lp + k * SEG);
+#pragma unroll
+                for (int t = 0; t < SEG; ++t) bv[s][t] = pb[t];
+            }
+#pragma unroll
+            for (int t = 0; t < SEG; ++t) {
+                const float dt = s_seg[F_DT][lane * ROWP + t];
+                const float dtu = s_seg[F_DTU][lane * ROWP + t];
+#pragma unroll
+                for (int s = 0; s < S; ++s) h[s] = __builtin_fmaf(hw_exp2(dt * a2[s]), h[s], dtu * bv[s][t]);
+            }
+        }
+    }
+
+    // ---- phase 2: segments in reverse ----
+    float gDacc = 0.0f, gbacc = 0.0f;
+    for (int64_t k = p.nseg - 1; k >= 0; --k) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < QS; ++j) {
+            const int64_t t = k * SEG + QS * k8 + j;
+            float dt = 0.0f, dtu = 0.0f, gp = 0.0f, uu = 0.0f, sg = 0.0f, gz = 0.0f;
+            if (t < L && pvalid) {
+                const float x = load_el<T>(p.delta, prow + t) + pbias;
+                uu = load_el<T>(p.u, prow + t);
+                const float gy = p.dy[prow + t];
+                if constexpr (SOFTPLUS) {
+                    dt = softplus_f(x);
+                    sg = hw_rcp(1.0f + hw_exp2(-x * kLog2e));
+                } else {
+                    dt = hw_exp2(x * kLog2e);
+                }
+                dtu = dt * uu;
+                if constexpr (HAS_Z) {
+                    const float zz = load_el<T>(p.z, prow + t);
+                    const float sz = hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
+                    gp = gy * zz * sz;
+                    gz = gy * (sz + zz * sz * (1.0f - sz));
+                } else {
+                    gp = gy;
+                }
+            } else if (t < L) {
+                // rows past dim: same decay as row 0 would give, no gradient flowing in
+                const float x = load_el<T>(p.delta, prow + t) + pbias;
+                dt = SOFTPLUS ? softplus_f(x) : hw_exp2(x * kLog2e);
+            }
+            const int o = r * ROWP + QS * k8 + j;
+            s_seg[F_DT][o] = dt;
+            s_seg[F_DTU][o] = dtu;
+            s_seg[F_GP][o] = gp;
+            s_seg[F_U][o] = uu;
+            s_seg[F_SG][o] = sg;
+            s_seg[F_GZ][o] = gz;
+        }
+        __syncthreads();
+
+        // recompute the segment's states and decays
+        float hs[S], hseg[S][SEG], aseg[S][SEG], bv[S][SEG], cv[S][SEG], dtv[SEG], dtuv[SEG], gpv[SEG];
+        if (wave_live) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                hs[s] = mvalid ? ckrow[k * N + s] : 0.0f;
+                const bwd_cptrf pb = (bwd_cptrf)(Brow + s * p.lp + k * SEG);
+                const bwd_cptrf pc = (bwd_cptrf)(Crow + s * p.lp + k * SEG);
+#pragma unroll
+                for (int t = 0; t < SEG; ++t) {
+                    bv[s][t] = pb[t];
+                    cv[s][t] = pc[t];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < SEG; ++t) {
+                dtv[t] = s_seg[F_DT][lane * ROWP + t];
+                dtuv[t] = s_seg[F_DTU][lane * ROWP + t];
+                gpv[t] = s_seg[F_GP][lane * ROWP + t];
+            }
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                float hh = hs[s];
+#pragma unroll
+                for (int t = 0; t < SEG; ++t) {
+                    aseg[s][t] = hw_exp2(dtv[t] * a2[s]);
+                    hh = __builtin_fmaf(aseg[s][t], hh, dtuv[t] * bv[s][t]);
+                    hseg[s][t] = hh;
+                }
+            }
+        }
+
+#pragma unroll
+        for (int half = 1; half >= 0; --half) {
+            if (wave_live) {
+                float gBc[S][SUB], gCc[S][SUB];
+#pragma unroll
+                for (int tt = SUB - 1; tt >= 0; --tt) {
+                    const int t = half * SUB + tt;
+                    float P1 = 0.0f, P2 = 0.0f, Y = 0.0f;
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        lam[s] = __builtin_fmaf(gpv[t], cv[s][t], lam[s]);
+                        gCc[s][tt] = gpv[t] * hseg[s][t];
+                        gBc[s][tt] = lam[s] * dtuv[t];
+                        P1 = __builtin_fmaf(lam[s], bv[s][t], P1);
+                        const float hp = t > 0 ? hseg[s][t - 1] : hs[s];
+                        const float q = lam[s] * aseg[s][t] * hp;
+                        P2 = __builtin_fmaf(q, Av[s], P2);
+                        gA[s] = __builtin_fmaf(q, dtv[t], gA[s]);
+                        Y = __builtin_fmaf(cv[s][t], hseg[s][t], Y);
+                        lam[s] *= aseg[s][t];
+                    }
+                    const int o = (wave * 64 + lane) * SUBP + tt;
+                    s_part[0][o] = P1;
+                    s_part[1][o] = P2;
+                    s_part[2][o] = Y;
+                }
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int tt = 0; tt < SUB; ++tt) {
+                        s_red[(((wave * 2 + 0) * S + s) * SUB + tt) * 64 + lane] = gBc[s][tt];
+                        s_red[(((wave * 2 + 1) * S + s) * SUB + tt) * 64 + lane] = gCc[s][tt];
+                    }
+            }
+            __syncthreads();
+            // epilogue: step k8 of this half, channel r
+            {
+                const int tt = k8;
+                const int64_t t = k * SEG + half * SUB + tt;
+                float P1 = 0.0f, P2 = 0.0f, Y = 0.0f;
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    const int o = (w * 64 + r) * SUBP + tt;
+                    P1 += s_part[0][o];
+                    P2 += s_part[1][o];
+                    Y += s_part[2][o];
+                }
+                const int o = r * ROWP + half * SUB + tt;
+                const float dt = s_seg[F_DT][o], gp = s_seg[F_GP][o], uu = s_seg[F_U][o];
+                const float gdt = __builtin_fmaf(uu, P1, P2);
+                const float gx = SOFTPLUS ? gdt * s_seg[F_SG][o] : gdt * dt;
+                const float gu = __builtin_fmaf(gp, pskip, dt * P1);
+                if (pvalid && t < L) {
+                    p.du[prow + t] = gu;
+                    p.ddelta[prow + t] = gx;
+                    if constexpr (HAS_Z) p.dz[prow + t] = s_seg[F_GZ][o] * __builtin_fmaf(pskip, uu, Y);
+                    gDacc = __builtin_fmaf(gp, uu, gDacc);
+                    gbacc += gx;
+                }
+            }
+            // dB / dC of this half: one sum over the 64 channels per (dB|dC, state, step)
+            if (tid < 2 * W * S * SUB) {
+                const int tt = tid % SUB;
+                const int s = (tid / SUB) % S;
+                const int w = (tid / (SUB * S)) % W;
+                const int q = tid / (SUB * S * W);
+                const float* src = &s_red[(((w * 2 + q) * S + s) * SUB + tt) * 64];
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 64; i += 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(src + i);
+                    acc += v.x;
+                    acc += v.y;
+                    acc += v.z;
+                    acc += v.w;
+                }
+                const int n = w * S + s;
+                if (n < N)
+                    p.bcpart[(((grp * p.batch + b) * 2 + q) * N + n) * p.lp + k * SEG + half * SUB + tt] = acc;
+            }
+            __syncthreads();
+        }
+    }
+
+    // per-channel results: dh0, the batch's share of dA
+    if (wave_live && mvalid) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int64_t i = (b * p.dim + dm) * N + nbase + s;
+            if (p.dh0) p.dh0[i] = lam[s];
+            p.apart[i] = gA[s];
+        }
+    }
+    // the 8 threads of a channel add their dD and dbias shares
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+        gDacc += __shfl_xor(gDacc, off, 64);
+        gbacc += __shfl_xor(gbacc, off, 64);
+    }
+    if (k8 == 0 && pvalid) {
+        p.dpart[b * p.dim + pd] = gDacc;
+        p.bpart[b * p.dim + pd] = gbacc;
+    }
+}
+
+// B and C (any dtype, contiguous (batch, N, len)) widened into fp32 rows of length lp, zero past
+// len. One thread per output element.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_bc_widen_kernel(const void* B, const void* C, float* out,
+                                                           int64_t rows, int64_t len, int64_t lp) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= 2 * rows * lp) return;
+    const int64_t row = i / lp, t = i - row * lp;
+    const int64_t q = row / rows, rr = row - q * rows;
+    out[i] = t < len ? load_el<T>(q ? C : B, rr * len + t) : 0.0f;
+}
+
+struct BwdReduceParams {
+    const float* bcpart;
+    const float* apart;
+    const float* dpart;
+    const float* bpart;
+    float* dB;
+    float* dC;
+    float* dA;
+    float* dD;
+    float* dbias;
+    int64_t batch, dim, len, dstate, lp, groups;
+};
+
+// Fixed-order sums of the partials: dB, dC over channel groups; dA, dD, dbias over the batch.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdReduceParams p) {
+    const int64_t nbc = p.batch * p.dstate * p.len;  // per output tensor
+    const int64_t na = p.dim * p.dstate;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < 2 * nbc) {
+        const int64_t q = i / nbc, j = i - q * nbc;
+        const int64_t b = j / (p.dstate * p.len);
+        const int64_t rem = j - b * p.dstate * p.len;
+        const int64_t n = rem / p.len, t = rem - n * p.len;
+        float acc = 0.0f;
+        for (int64_t g = 0; g < p.groups; ++g)
+            acc += p.bcpart[(((g * p.batch + b) * 2 + q) * p.dstate + n) * p.lp + t];
+        (q ? p.dC : p.dB)[j] = acc;
+    } else if (i < 2 * nbc + na) {
+        const int64_t j = i - 2 * nbc;
+        float acc = 0.0f;
+        for (int64_t b = 0; b < p.batch; ++b) acc += p.apart[b * na + j];
+        p.dA[j] = acc;
+    } else if (i < 2 * nbc + na + p.dim) {
+        const int64_t d = i - 2 * nbc - na;
+        float accd = 0.0f, accb = 0.0f;
+        for (int64_t b = 0; b < p.batch; ++b) {
+            accd += p.dpart[b * p.dim + d];
+            accb += p.bpart[b * p.dim + d];
+        }
+        if (p.dD) p.dD[d] = accd;
+        if (p.dbias) p.dbias[d] = accb;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// host side
+
+struct BwdLayout {
+    int64_t lp, nseg, groups;
+    int64_t off_bc, off_ck, off_bcpart, off_apart, off_dpart, off_bpart, total;
+};
+
+inline int64_t bwd_align(int64_t x) { return (x + 255) / 256 * 256; }
+
+inline BwdLayout bwd_layout(const mamba_scan_shape& s) {
+    BwdLayout l;
+    l.lp = (s.len + kBwdSeg - 1) / kBwdSeg * kBwdSeg;
+    l.nseg = l.lp / kBwdSeg;
+    l.groups = (s.dim + 63) / 64;
+    int64_t o = 0;
+    l.off_bc = o;
+    o = bwd_align(o + 2 * s.batch * s.dstate * l.lp * 4);
+    l.off_ck = o;
+    o = bwd_align(o + s.batch * s.dim * l.nseg * s.dstate * 4);
+    l.off_bcpart = o;
+    o = bwd_align(o + l.groups * s.batch * 2 * s.dstate * l.lp * 4);
+    l.off_apart = o;
+    o = bwd_align(o + s.batch * s.dim * s.dstate * 4);
+    l.off_dpart = o;
+    o = bwd_align(o + s.batch * s.dim * 4);
+    l.off_bpart = o;
+    o = bwd_align(o + s.batch * s.dim * 4);
+    l.total = o;
+    return l;
+}
+
+inline int bwd_states_per_wave(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : 0; }
+
+template <typename T, int S, bool SP, bool HZ>
+int launch_bwd_cfg(const BwdParams& q, hipStream_t stream) {
+    void* args[] = {const_cast<BwdParams*>(&q)};
+    const bool exact = q.dstate == (int64_t)S * kBwdW;
+    const void* fn = exact ? reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, true>)
+                           : reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)(q.batch * q.groups)), dim3(64 * kBwdW), args, 0, stream) ==
+                   hipSuccess
+               ? MAMBA_SCAN_OK
+               : MAMBA_SCAN_ERR_LAUNCH;
+}
+
+template <typename T, int S>
+int launch_bwd_s(const BwdParams& q, bool softplus, hipStream_t stream) {
+    const bool hz = q.z != nullptr;
+    if (softplus && hz) return launch_bwd_cfg<T, S, true, true>(q, stream);
+    if (softplus) return launch_bwd_cfg<T, S, true, false>(q, stream);
+    if (hz) return launch_bwd_cfg<T, S, false, true>(q, stream);
+    return launch_bwd_cfg<T, S, false, false>(q, stream);
+}
+
+template <typename T>
+int launch_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool softplus, hipStream_t stream) {
+    const BwdLayout l = bwd_layout(s);
+    char* ws = static_cast<char*>(p->workspace);
+    BwdParams q;
+    q.u = p->u;
+    q.delta = p->delta;
+    q.z = p->z;
+    q.bc = reinterpret_cast<const float*>(ws + l.off_bc);
+    q.A = p->A;
+    q.D = p->D;
+    q.bias = p->delta_bias;
+    q.h0 = p->h0;
+    q.dy = p->dy;
+    q.dlast = p->dlast_state;
+    q.du = p->du;
+    q.ddelta = p->ddelta;
+    q.dz = p->dz;
+    q.dh0 = p->dh0;
+    q.ck = reinterpret_cast<float*>(ws + l.off_ck);
+    q.bcpart = reinterpret_cast<float*>(ws + l.off_bcpart);
+    q.apart = reinterpret_cast<float*>(ws + l.off_apart);
+    q.dpart = reinterpret_cast<float*>(ws + l.off_dpart);
+    q.bpart = reinterpret_cast<float*>(ws + l.off_bpart);
+    q.batch = s.batch;
+    q.dim = s.dim;
+    q.len = s.len;
+    q.dstate = s.dstate;
+    q.lp = l.lp;
+    q.nseg = l.nseg;
+    q.groups = l.groups;
+
+    const int64_t nwide = 2 * s.batch * s.dstate * l.lp;
+    {
+        const void* bsrc = p->B;
+        const void* csrc = p->C;
+        float* dst = reinterpret_cast<float*>(ws + l.off_bc);
+        int64_t rows = s.batch * s.dstate, len = s.len, lp = l.lp;
+        void* args[] = {&bsrc, &csrc, &dst, &rows, &len, &lp};
+        if (hipLaunchKernel(reinterpret_cast<const void*>(&bwd_bc_widen_kernel<T>),
+                            dim3((unsigned)((nwide + 255) / 256)), dim3(256), args, 0, stream) != hipSuccess)
+            return MAMBA_SCAN_ERR_LAUNCH;
+    }
+    int rc;
+    switch (bwd_states_per_wave(s.dstate)) {
+        case 1: rc = launch_bwd_s<T, 1>(q, softplus, stream); break;
+        case 2: rc = launch_bwd_s<T, 2>(q, softplus, stream); break;
+        default: return MAMBA_SCAN_ERR_UNSUPPORTED;
+    }
+    if (rc != MAMBA_SCAN_OK) return rc;
+    BwdReduceParams r;
+    r.bcpart = q.bcpart;
+    r.apart = q.apart;
+    r.dpart = q.dpart;
+    r.bpart = q.bpart;
+    r.dB = p->dB;
+    r.dC = p->dC;
+    r.dA = p->dA;
+    r.dD = p->dD;
+    r.dbias = p->ddelta_bias;
+    r.batch = s.batch;
+    r.dim = s.dim;
+    r.len = s.len;
+    r.dstate = s.dstate;
+    r.lp = l.lp;
+    r.groups = l.groups;
+    const int64_t nred = 2 * s.batch * s.dstate * s.len + s.dim * s.dstate + s.dim;
+    void* rargs[] = {&r};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&bwd_reduce_kernel), dim3((unsigned)((nred + 255) / 256)),
+                        dim3(256), rargs, 0, stream) != hipSuccess)
+        return MAMBA_SCAN_ERR_LAUNCH;
+    return MAMBA_SCAN_OK;
+}
+
+}  // namespace mscan

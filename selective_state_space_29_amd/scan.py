@@ -47,6 +47,12 @@ class Strides(ctypes.Structure):
                 ("A", _I64 * 2), ("D", _I64), ("delta_bias", _I64)]
 
 
+class BwdPtrs(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("u", "delta", "z", "B", "C", "A", "D", "delta_bias", "h0", "dy",
+                                  "dlast_state", "du", "ddelta", "dz", "dB", "dC", "dA", "dD",
+                                  "ddelta_bias", "dh0", "workspace")] + [("workspace_bytes", _I64)]
+
+
 class MambaScanError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"mamba_scan_fwd failed ({code}): {msg}")
@@ -74,6 +80,11 @@ def load_library(path: str = LIB_PATH):
     lib.mamba_scan_strerror.argtypes = [ctypes.c_int]
     lib.mamba_scan_abi_version.restype = ctypes.c_int
     lib.mamba_scan_abi_version.argtypes = []
+    lib.mamba_scan_bwd.restype = ctypes.c_int
+    lib.mamba_scan_bwd.argtypes = [ctypes.POINTER(BwdPtrs), ctypes.POINTER(Shape), ctypes.c_int,
+                                   ctypes.c_uint32, _P]
+    lib.mamba_scan_bwd_workspace_bytes.restype = _I64
+    lib.mamba_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, ctypes.c_uint32]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -187,4 +198,112 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
         raise err
     if ws is not None:
         ws.record_stream(torch.cuda.current_stream(dev))
+    return (y, ls) if return_last_state else y
+
+
+def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False,
+                       h0=None, dlast_state=None, want_dh0=True):
+    """Gradients of the scan (``mamba_scan_bwd``) for incoming gradients dy (batch, dim, L) and,
+    optionally, dlast_state (batch, dim, N). Inputs as for ``selective_scan_fn``; all tensors are
+    made contiguous first. Returns a dict of fp32 gradients: u, delta, B, C, A, and z, D,
+    delta_bias when given, h0 when ``want_dh0`` (the gradient of the initial state, which is zero
+    when h0 is None).
+    """
+    lib = load_library()
+    if u.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"u must be float32 or bfloat16, got {u.dtype}")
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("selective_scan_bwd runs on the GPU only: inputs must be device tensors")
+    for name, x in (("delta", delta), ("z", z), ("B", B), ("C", C)):
+        if x is not None and (x.dtype != u.dtype or x.device != dev):
+            raise TypeError(f"{name} must have u's dtype and device")
+    u, delta, z, B, C = (None if x is None else x.contiguous() for x in (u, delta, z, B, C))
+    A = A.float().contiguous()
+    D = None if D is None else D.float().contiguous()
+    delta_bias = None if delta_bias is None else delta_bias.float().contiguous()
+    h0 = None if h0 is None else h0.float().contiguous()
+    dy = dy.float().contiguous()
+    dlast_state = None if dlast_state is None else dlast_state.float().contiguous()
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape) or dy.shape != u.shape:
+        raise ValueError("u, delta, z and dy must have the same shape")
+    if B.shape != (batch, N, L) or C.shape != (batch, N, L) or A.shape != (dim, N):
+        raise ValueError("B, C must be (batch, N, L) and A (dim, N)")
+    for name, x, shape in (("D", D, (dim,)), ("delta_bias", delta_bias, (dim,)),
+                           ("h0", h0, (batch, dim, N)), ("dlast_state", dlast_state, (batch, dim, N))):
+        if x is not None and tuple(x.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"u": torch.empty((batch, dim, L), **f32), "delta": torch.empty((batch, dim, L), **f32),
+         "B": torch.empty((batch, N, L), **f32), "C": torch.empty((batch, N, L), **f32),
+         "A": torch.empty((dim, N), **f32)}
+    if z is not None:
+        g["z"] = torch.empty((batch, dim, L), **f32)
+    if D is not None:
+        g["D"] = torch.empty((dim,), **f32)
+    if delta_bias is not None:
+        g["delta_bias"] = torch.empty((dim,), **f32)
+    if want_dh0:
+        g["h0"] = torch.empty((batch, dim, N), **f32)
+    shape = Shape(batch, dim, L, N)
+    dtype = BF16 if u.dtype == torch.bfloat16 else F32
+    flags = DELTA_SOFTPLUS if delta_softplus else 0
+    ws_bytes = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(shape), dtype, flags)
+    if ws_bytes < 0:
+        raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
+    ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev)
+    ptrs = BwdPtrs(_ptr(u), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(delta_bias),
+                   _ptr(h0), _ptr(dy), _ptr(dlast_state), _ptr(g["u"]), _ptr(g["delta"]), _ptr(g.get("z")),
+                   _ptr(g["B"]), _ptr(g["C"]), _ptr(g["A"]), _ptr(g.get("D")), _ptr(g.get("delta_bias")),
+                   _ptr(g.get("h0")), _ptr(ws), int(ws_bytes))
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.mamba_scan_bwd(ctypes.byref(ptrs), ctypes.byref(shape), dtype, flags, stream)
+    if rc != 0:
+        err = MambaScanError(rc, strerror(rc))
+        if rc in (-1, -2, -3, -4, -5, -6, -8, -9):
+            raise ValueError(str(err)) from err
+        raise err
+    ws.record_stream(torch.cuda.current_stream(dev))
+    return g
+
+
+class SelectiveScan(torch.autograd.Function):
+    """y (and last_state) = selective_scan(...) with a backward pass through ``mamba_scan_bwd``.
+
+    Only the inputs are saved; the backward recomputes the states ("手把手用PyTorch实现Mamba的SSM层…"
+    §4.2). Gradients come back in each input's dtype.
+    """
+
+    @staticmethod
+    def forward(ctx, u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus):
+        y, ls = selective_scan_fn(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
+                                  delta_softplus=delta_softplus, return_last_state=True, h0=h0)
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0)
+        ctx.delta_softplus = delta_softplus
+        return y, ls
+
+    @staticmethod
+    def backward(ctx, gy, gls):
+        u, delta, A, B, C, D, z, delta_bias, h0 = ctx.saved_tensors
+        if gy is None:
+            gy = torch.zeros(u.shape, dtype=torch.float32, device=u.device)
+        g = selective_scan_bwd(u, delta, A, B, C, gy, D=D, z=z, delta_bias=delta_bias,
+                               delta_softplus=ctx.delta_softplus, h0=h0, dlast_state=gls,
+                               want_dh0=h0 is not None and ctx.needs_input_grad[8])
+
+        def cast(name, like):
+            return None if like is None or name not in g else g[name].to(like.dtype)
+
+        return (cast("u", u), cast("delta", delta), cast("A", A), cast("B", B), cast("C", C),
+                cast("D", D), cast("z", z), cast("delta_bias", delta_bias), cast("h0", h0), None)
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                   return_last_state=False, h0=None):
+    """Differentiable form of ``selective_scan_fn`` (torch autograd through the HIP backward)."""
+    y, ls = SelectiveScan.apply(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
     return (y, ls) if return_last_state else y

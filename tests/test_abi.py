@@ -25,7 +25,8 @@ def header_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["mamba_scan_abi_version", "mamba_scan_fwd",
+    assert header_functions() == ["mamba_scan_abi_version", "mamba_scan_bwd",
+                                  "mamba_scan_bwd_workspace_bytes", "mamba_scan_fwd",
                                   "mamba_scan_strerror", "mamba_scan_workspace_bytes"]
 
 
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 1
+    assert scan.load_library().mamba_scan_abi_version() == 2
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -132,3 +133,60 @@ def test_binding_refuses_host_tensors():
     u = torch.zeros(1, 2, 8)
     with pytest.raises(ValueError, match="GPU"):
         scan.selective_scan_fn(u, u, torch.zeros(2, 4), torch.zeros(1, 4, 8), torch.zeros(1, 4, 8))
+
+
+# ---- backward entry point ----
+
+def fake_bwd(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16)):
+    lib = scan.load_library()
+    base = 1 << 40
+    names = [f[0] for f in scan.BwdPtrs._fields_ if f[0] != "workspace_bytes"]
+    ptrs = scan.BwdPtrs(**{n: base + (i + 1) * (1 << 32) for i, n in enumerate(names)})
+    shp = scan.Shape(*shape)
+    ptrs.workspace_bytes = max(0, lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(shp), dtype, flags))
+    ctx = dict(ptrs=ptrs, shape=shp, flags=flags, dtype=dtype)
+    if mutate:
+        mutate(ctx)
+    return lib.mamba_scan_bwd(ctypes.byref(ctx["ptrs"]), ctypes.byref(ctx["shape"]), ctx["dtype"],
+                              ctx["flags"], None)
+
+
+BWD_CASES = [
+    ("null_dy", _set("ptrs", "dy", None), -1),
+    ("null_dA", _set("ptrs", "dA", None), -1),
+    ("z_without_dz", _set("ptrs", "dz", None), -6),
+    ("D_without_dD", _set("ptrs", "dD", None), -6),
+    ("dbias_without_bias", _set("ptrs", "delta_bias", None), -6),
+    ("no_workspace", _set("ptrs", "workspace", None), -6),
+    ("workspace_too_small", _set("ptrs", "workspace_bytes", 1024), -9),
+    ("unknown_flag", lambda c: c.__setitem__("flags", 1 << 9), -6),
+    ("bad_dtype", lambda c: c.__setitem__("dtype", 7), -4),
+    ("zero_len", _set("shape", "len", 0), -2),
+    ("dstate_above_max", _set("shape", "dstate", 300), -5),
+    ("output_aliases_input", lambda c: setattr(c["ptrs"], "du", c["ptrs"].dy), -6),
+    ("outputs_alias", lambda c: setattr(c["ptrs"], "dB", c["ptrs"].dC), -6),
+    ("misaligned_workspace", lambda c: setattr(c["ptrs"], "workspace", c["ptrs"].workspace + 16), -6),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_invalid_arguments_are_rejected(name, mutate, code):
+    assert fake_bwd(mutate) == code
+
+
+def test_backward_unsupported_dstate():
+    assert fake_bwd(shape=(2, 3, 40, 32)) == -8   # more than 2 states per wave
+    assert fake_bwd(shape=(2, 3, 40, 11)) == -8   # N in (8, 16] must be even
+
+
+def test_backward_workspace_query():
+    lib = scan.load_library()
+    ok = scan.Shape(8, 1536, 2048, 16)
+    n = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), scan.BF16, scan.DELTA_SOFTPLUS)
+    # states every 16 steps + fp32 B/C + per-group dB/dC partials + dA/dD/dbias partials
+    assert n >= 8 * 1536 * 16 * 128 * 4 + 2 * 8 * 16 * 2048 * 4 + 24 * 8 * 2 * 16 * 2048 * 4
+    assert n % 256 == 0
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(0, 1, 1, 1)), 0, 0) == -2
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 3, 0) == -4
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 0, 1 << 1) == -6
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(1, 1, 1, 300)), 0, 0) == -5
