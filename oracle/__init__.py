@@ -1,4 +1,5 @@
-"""fp64 CPU oracle of the selective-scan forward and backward passes (wrapper over ``scan_oracle.c``).
+"""fp64 CPU oracle of the selective-scan forward and backward passes (``scan_oracle.c``) and of the
+block's upstream stages that produce the scan's inputs (``block_oracle.c``).
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU-baseline leg may use
 it; the product path never does. It shares no code with the HIP library. Which passage of the
@@ -12,6 +13,11 @@ in torch fp64). One reading is not pinned by any page value: the exp branch take
 
 The backward pass (``selective_scan_bwd``) is pinned by central finite differences of the forward
 oracle and by torch's fp64 CPU autograd through an independent step-by-step formulation.
+
+The upstream stages (``block_upstream``: causal depthwise convolution + SiLU, x projection, dt
+projection, each output rounded once to bf16) are pinned against torch's fp64 ``conv1d`` and
+numpy's ``convolve`` and ``matmul``, an impulse-response hand case, and their bf16 rounding
+against torch's own fp32 -> bf16 conversion and hand-made ties.
 """
 
 from __future__ import annotations
@@ -24,16 +30,20 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "scan_oracle.c")
+BLOCK_SOURCE = os.path.join(_HERE, "block_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(force: bool = True, source: str = SOURCE, out: str = _LIB) -> str:
-    """Compile the oracle with plain gcc: -O2, no fast-math, host libm."""
+def build(force: bool = True, source=None, out: str = _LIB) -> str:
+    """Compile the oracle with plain gcc: -O2, no fast-math, host libm. ``source``: one file or a
+    list of files (default: both oracle sources)."""
+    sources = [SOURCE, BLOCK_SOURCE] if source is None else (
+        [source] if isinstance(source, str) else list(source))
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
         subprocess.run(
-            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", tmp, source, "-lm"],
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", tmp, *sources, "-lm"],
             check=True,
         )
         os.replace(tmp, out)
@@ -59,12 +69,23 @@ def _bind_bwd(lib):
     return lib
 
 
+def _bind_block(lib):
+    P = ctypes.c_void_p
+    f = lib.oracle_block_upstream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int64] * 6 + [P] * 5 + [P] * 6 + [ctypes.c_int]
+    g = lib.oracle_round_bf16
+    g.restype = None
+    g.argtypes = [P, P, ctypes.c_int64]
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
             build(force=False)
-        _lib = _bind_bwd(_bind(_LIB))
+        _lib = _bind_block(_bind_bwd(_bind(_LIB)))
     return _lib
 
 
@@ -180,4 +201,55 @@ def selective_scan_bwd(u, delta, A, B, C, gy, D=None, z=None, delta_bias=None,
         raise RuntimeError(f"oracle_selective_scan_bwd failed with {rc}")
     if z is None:
         del out["z"]
+    return out
+
+
+def round_bf16(values, lib_path=None) -> np.ndarray:
+    """The oracle's rounding of fp64 values to bf16 (nearest, ties to even), as uint16 bits."""
+    lib = _bind_block(ctypes.CDLL(lib_path)) if lib_path else _load()
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib.oracle_round_bf16(v.ctypes.data, out.ctypes.data, v.size)
+    return out
+
+
+def block_upstream(x, conv_w, conv_b, w_x, w_dt, dstate, dt_rank, want_pre=False, nthreads=None,
+                   lib_path=None):
+    """The stages in front of the scan, in fp64 with bf16 storage between them.
+
+    x: (batch, dim, L) bf16 bits (uint16); conv_w: (dim, d_conv) fp32; conv_b: (dim,) fp32 or None;
+    w_x: (dt_rank + 2 dstate, dim) bf16 bits; w_dt: (dim, dt_rank) bf16 bits.
+    Returns a dict with u (batch, dim, L), xdbl (batch, dt_rank + 2 dstate, L) and delta
+    (batch, dim, L) as bf16 bits; with ``want_pre`` also u_pre, xdbl_pre, delta_pre: the fp64
+    values before each rounding. The scan's B and C are ``xdbl[:, dt_rank:dt_rank + dstate]`` and
+    ``xdbl[:, dt_rank + dstate:]``.
+    """
+    lib = _bind_block(ctypes.CDLL(lib_path)) if lib_path else _load()
+    x = np.ascontiguousarray(x)
+    w_x = np.ascontiguousarray(w_x)
+    w_dt = np.ascontiguousarray(w_dt)
+    for name, a in (("x", x), ("w_x", w_x), ("w_dt", w_dt)):
+        if a.dtype != np.uint16:
+            raise TypeError(f"{name} must hold bf16 bit patterns (uint16)")
+    batch, dim, L = x.shape
+    conv_w = np.ascontiguousarray(conv_w, dtype=np.float32)
+    conv_b = None if conv_b is None else np.ascontiguousarray(conv_b, dtype=np.float32)
+    d_conv = conv_w.shape[1]
+    J = dt_rank + 2 * dstate
+    if conv_w.shape[0] != dim or w_x.shape != (J, dim) or w_dt.shape != (dim, dt_rank):
+        raise ValueError("weight shapes do not match x, dstate and dt_rank")
+    out = {"u": np.empty((batch, dim, L), np.uint16), "xdbl": np.empty((batch, J, L), np.uint16),
+           "delta": np.empty((batch, dim, L), np.uint16)}
+    if want_pre:
+        out.update({k + "_pre": np.empty(out[k].shape, np.float64) for k in ("u", "xdbl", "delta")})
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data
+
+    rc = lib.oracle_block_upstream(
+        batch, dim, L, dstate, dt_rank, d_conv, ptr(x), ptr(conv_w), ptr(conv_b), ptr(w_x),
+        ptr(w_dt), ptr(out["u"]), ptr(out["xdbl"]), ptr(out["delta"]), ptr(out.get("u_pre")),
+        ptr(out.get("xdbl_pre")), ptr(out.get("delta_pre")), int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_block_upstream failed with {rc}")
     return out

@@ -18,7 +18,8 @@ import numpy as np
 
 from . import gen
 
-STREAM = {"u": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "D": 6, "delta_bias": 7}
+STREAM = {"u": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "D": 6, "delta_bias": 7,
+          "x": 8, "conv_w": 9, "conv_b": 10, "w_x": 11, "w_dt": 12}
 
 
 @dataclass(frozen=True)
@@ -147,3 +148,79 @@ def make_row_inputs(w: Workload, rows) -> dict:
     res["D"] = np.ascontiguousarray(full["D"][ds])
     res["delta_bias"] = np.ascontiguousarray(full["delta_bias"][ds])
     return res
+
+
+# ---------------------------------------------------------------------------------------------
+# The stages in front of the scan (convolution + SiLU, x projection, dt projection).
+
+
+@dataclass(frozen=True)
+class UpstreamWorkload:
+    """Shapes of the block's upstream stages: x (batch, dim, L) bf16 in; u, delta (batch, dim, L)
+    and x_dbl (batch, dt_rank + 2 dstate, L) bf16 out. Seed ``29100 + id``."""
+
+    wid: int
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    dt_rank: int
+    seqlen: int
+    d_conv: int = 4
+    note: str = field(default="", compare=False)
+
+    @property
+    def seed(self) -> int:
+        return 29100 + self.wid
+
+    @property
+    def proj_rows(self) -> int:
+        return self.dt_rank + 2 * self.dstate
+
+    def algorithmic_bytes(self) -> int:
+        """x read once; u, x_dbl, delta written once; the weights read once."""
+        b, d, l, j = self.batch, self.dim, self.seqlen, self.proj_rows
+        rd = b * d * l * 2 + d * self.d_conv * 4 + d * 4 + j * d * 2 + d * self.dt_rank * 2
+        wr = 2 * b * d * l * 2 + b * j * l * 2
+        return rd + wr
+
+    def flops(self) -> int:
+        """Multiply-adds of the two projections, as 2 flops each (the convolution is not counted)."""
+        b, d, l = self.batch, self.dim, self.seqlen
+        return 2 * b * l * d * (self.proj_rows + self.dt_rank)
+
+
+UPSTREAM = {
+    1: UpstreamWorkload(1, "upstream-small", 2, 192, 16, 8, 200,
+                        note="ragged: 192 channels, 200 steps, dt_rank 8"),
+    2: UpstreamWorkload(2, "mamba130m-upstream", 8, 1536, 16, 48, 2048,
+                        note="Mamba-130m: d_inner 1536, d_state 16, dt_rank 48 = 768 / 16, "
+                             "d_conv 4, L 2048; produces the scan inputs of the layer workload"),
+}
+
+
+def make_upstream_inputs(w: UpstreamWorkload) -> dict:
+    """x ~ N(0, 1) in bf16, and weights drawn as PyTorch initialises the layers the pages build:
+    Conv1d(dim, dim, d_conv, groups=dim) weight and bias U(-1/sqrt(d_conv), 1/sqrt(d_conv)) (fp32),
+    Linear(dim, dt_rank + 2 dstate) weight U(-1/sqrt(dim), 1/sqrt(dim)) and Linear(dt_rank, dim)
+    weight U(-1/sqrt(dt_rank), 1/sqrt(dt_rank)) (bf16)."""
+    kc = 1.0 / np.sqrt(w.d_conv)
+    kx = 1.0 / np.sqrt(w.dim)
+    kt = 1.0 / np.sqrt(w.dt_rank)
+    return {
+        "x": gen.normal(w.seed, STREAM["x"], (w.batch, w.dim, w.seqlen), "bf16"),
+        "conv_w": gen.uniform(w.seed, STREAM["conv_w"], (w.dim, w.d_conv), -kc, kc, "f32"),
+        "conv_b": gen.uniform(w.seed, STREAM["conv_b"], (w.dim,), -kc, kc, "f32"),
+        "w_x": gen.uniform(w.seed, STREAM["w_x"], (w.proj_rows, w.dim), -kx, kx, "bf16"),
+        "w_dt": gen.uniform(w.seed, STREAM["w_dt"], (w.dim, w.dt_rank), -kt, kt, "bf16"),
+    }
+
+
+def make_upstream_case(seed: int, batch: int, dim: int, dstate: int, dt_rank: int, seqlen: int,
+                       d_conv: int = 4, bias: bool = True) -> dict:
+    """An ad-hoc upstream case with the same distributions (for tests of odd shapes)."""
+    w = UpstreamWorkload(seed - 29100, "case", batch, dim, dstate, dt_rank, seqlen, d_conv)
+    x = make_upstream_inputs(w)
+    if not bias:
+        x["conv_b"] = None
+    return x
