@@ -49,6 +49,10 @@ def parse():
                          "the state by --chunk steps from the previous call's last_state")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward scan, time the backward pass (mamba_scan_bwd)")
+    ap.add_argument("--upstream", action="store_true",
+                    help="instead of the scan, time the block's upstream stages "
+                         "(mamba_block_upstream: conv1d + SiLU, x_proj, dt_proj) at the Mamba-130m "
+                         "shape, and the upstream followed by the scan")
     ap.add_argument("--chunk", type=int, default=1, help="steps per decode call")
     ap.add_argument("--decode-calls", type=int, default=256, help="timed decode calls")
     ap.add_argument("--copy-mb", type=float, default=0.0,
@@ -374,6 +378,138 @@ def backward_bench(args):
     print(json.dumps(res), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+
+
+def upstream_bench(args):
+    """The stages in front of the scan at the Mamba-130m shape (batch 8, d_inner 1536, d_state 16,
+    dt_rank 48, d_conv 4, L 2048, bf16): one step = one mamba_block_upstream call. Three buffer
+    sets rotate so no launch finds its 150 MB in the last-level cache. Also times the upstream
+    call followed by the scan (the block's SSM part: u, delta, B, C never leave the GPU)."""
+    import numpy as np
+    import torch
+
+    from selective_state_space_29_amd import scan, workloads
+    import oracle
+
+    w = workloads.UPSTREAM[2]
+    x = workloads.make_upstream_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    cw, cb = torch.from_numpy(x["conv_w"]).to(dev), torch.from_numpy(x["conv_b"]).to(dev)
+    wx, wdt = bf(x["w_x"]), bf(x["w_dt"])
+    sets = []
+    for i in range(max(1, args.sets)):
+        xi = bf(x["x"])
+        outs = (torch.empty_like(xi), torch.empty((w.batch, w.proj_rows, w.seqlen), dtype=torch.bfloat16,
+                                                  device=dev), torch.empty_like(xi))
+        sets.append((xi, outs))
+    stream = torch.cuda.current_stream(dev)
+
+    def up(i):
+        xi, outs = sets[i % len(sets)]
+        return scan.block_upstream(xi, cw, cb, wx, wdt, w.dstate, w.dt_rank, out=outs)
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        return per, ev[0][0].elapsed_time(ev[-1][1]) * 1e3 / steps
+
+    per_us, span_us = timed(up, args.steps, args.warmup)
+    mean_us = float(per_us.mean())
+    log(f"upstream: mean {mean_us:.2f} us, min {per_us.min():.2f} us, span/step {span_us:.2f} us")
+
+    # the block's SSM part: upstream, then the scan on its outputs (dt_proj bias = delta_bias)
+    A = torch.from_numpy(workloads.a_matrix(w.dim, w.dstate)).to(dev)
+    rng = np.random.default_rng(5)
+    dt_bias = torch.from_numpy(rng.uniform(-4.0, -1.0, w.dim).astype(np.float32)).to(dev)
+    Dv = torch.ones(w.dim, device=dev)
+    z = torch.from_numpy(rng.standard_normal((w.batch, w.dim, w.seqlen)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    y = torch.empty((w.batch, w.dim, w.seqlen), dtype=torch.float32, device=dev)
+
+    def block(i):
+        u, xdbl, delta = up(i)
+        _, B, C = scan.split_xdbl(xdbl, w.dt_rank, w.dstate)
+        scan.selective_scan_fn(u, delta, A, B, C, D=Dv, z=z, delta_bias=dt_bias, delta_softplus=True, out=y)
+
+    blk_us, blk_span = timed(block, args.steps, args.warmup)
+    log(f"upstream + scan: mean {blk_us.mean():.2f} us")
+
+    # parity of the last upstream outputs against the fp64 oracle, every element
+    last = sets[(args.steps - 1) % len(sets)][1]
+    got = {k: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+           for k, t in zip(("u", "xdbl", "delta"), last)}
+    t0 = time.perf_counter()
+    ref = oracle.block_upstream(x["x"], x["conv_w"], x["conv_b"], x["w_x"], x["w_dt"], w.dstate, w.dt_rank)
+    t_oracle = time.perf_counter() - t0
+
+    def widen(b):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    parity = {}
+    for k in got:
+        g, r = widen(got[k]), widen(ref[k])
+        parity[k] = {"bit_identical": round(float(np.mean(got[k] == ref[k])), 6),
+                     "max_diff_in_bf16_spacings": round(float(np.max(np.abs(g - r) / np.maximum(
+                         2.0**-7 * np.abs(r), 2.0**-133))), 3)}
+    log(f"parity vs oracle: {parity}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        one = {k: (v[:1] if k == "x" else v) for k, v in x.items()}
+        cores = oracle.default_threads()
+        t0 = time.perf_counter()
+        oracle.block_upstream(one["x"], one["conv_w"], one["conv_b"], one["w_x"], one["w_dt"], w.dstate,
+                              w.dt_rank, nthreads=cores)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(w.dim * w.seqlen / dt / 1e9, 5), "unit": "Gelem/s", "cores": cores,
+               "kind": "oracle", "sample": f"batch 0 ({w.dim} channels x {w.seqlen} steps), fp64, "
+                                           f"{dt:.2f} s wall on {cores} threads"}
+
+    elems = w.batch * w.dim * w.seqlen
+    alg = w.algorithmic_bytes()
+    gbs = alg / (mean_us * 1e-6) / 1e9
+    tflops = w.flops() / (mean_us * 1e-6) / 1e12
+    res = {
+        "metric": "block upstream (conv1d+SiLU, x_proj, dt_proj) Gelem/s (B*D*L) + % HBM roofline",
+        "value": round(elems / (span_us * 1e-6) / 1e9, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(span_us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator)",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
+                   "dt_rank": w.dt_rank, "d_conv": w.d_conv, "seq_len": w.seqlen, "buffer_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": alg,
+                     "mean_launch_us": round(mean_us, 2), "min_launch_us": round(float(per_us.min()), 2),
+                     "mfma": {"flops_per_launch": w.flops(), "achieved_TFLOP_s": round(tflops, 1),
+                              "peak_TFLOP_s": MFMA_BF16_PEAK_TFLOPS,
+                              "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}},
+        "block_ssm": {"what": "upstream then the scan (z gate, D = 1, softplus), per call",
+                      "mean_us": round(float(blk_us.mean()), 2), "min_us": round(float(blk_us.min()), 2)},
+        "cpu_baseline": cpu,
+        "parity": {"vs": "fp64 oracle, every element", "oracle_s": round(t_oracle, 2), **parity},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -394,6 +530,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.upstream:
+        upstream_bench(args)
         return
     if args.copy_mb > 0:
         copy_calibration(args.copy_mb, args.steps, args.warmup)

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 2
+#define MAMBA_SCAN_ABI_VERSION 3
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -179,6 +179,59 @@ int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
 
 /* Workspace bytes mamba_scan_bwd needs for this shape (> 0), or a negative error code. */
 int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype, uint32_t flags);
+
+/*
+ * Upstream stages of a Mamba block (ABI version 3): the producer of the scan's inputs.
+ *
+ *   u[b,d,t]     = bf16( silu( conv_b[d] + sum_k conv_w[d,k] * x[b,d,t-(d_conv-1)+k] ) )
+ *                  (x = 0 before t = 0: a causal depthwise convolution)
+ *   xdbl[b,j,t]  = bf16( sum_d w_x[j,d] * u[b,d,t] )              j < dt_rank + 2*dstate
+ *   delta[b,d,t] = bf16( sum_{r < dt_rank} w_dt[d,r] * xdbl[b,r,t] )
+ * bf16() rounds fp32 to the nearest bf16 (ties to even); the sums are accumulated in fp32.
+ * The scan's B and C are then rows dt_rank .. dt_rank+dstate-1 and dt_rank+dstate .. of xdbl
+ * (batch stride (dt_rank + 2*dstate)*len, state stride len), and dt_proj's bias is the scan's
+ * delta_bias (the scan adds it before its softplus).
+ *
+ * Sources: "告别'炼丹'：从Mamba-minimal入手，亲手调参并可视化SSM的状态变化" §1.1 (MambaBlock: Conv1d
+ * with kernel d_conv and padding d_conv-1, x_proj = Linear(d_inner, dt_rank + 2*d_state),
+ * dt_proj = Linear(dt_rank, d_inner)) and §2.2 (the dt rows are x_dbl[..., :dt_rank]);
+ * "Mamba-minimal项目解析：深入理解Mamba模型的极简实现" §4 (x_proj without bias, dt_proj with bias)
+ * and §5 (x_dbl splits into delta, B, C in that order; softplus(dt_proj(delta))). The convolution
+ * is read as depthwise (groups = channels, as the conv-gated block of "手把手用PyTorch实现Mamba的SSM层…"
+ * §5.2 builds it) and causal (the first len outputs of the padded convolution), followed by SiLU.
+ *
+ * Conventions
+ *  - Device pointers; every tensor CONTIGUOUS: x, u, delta (batch, dim, len) bf16; xdbl
+ *    (batch, dt_rank + 2*dstate, len) bf16; conv_w (dim, d_conv) fp32; conv_b (dim) fp32 or NULL
+ *    (no bias); w_x (dt_rank + 2*dstate, dim) bf16; w_dt (dim, dt_rank) bf16 (row-major, as the
+ *    weights of the layers above).
+ *  - dtype must be MAMBA_SCAN_BF16 (MAMBA_SCAN_ERR_UNSUPPORTED for MAMBA_SCAN_F32,
+ *    MAMBA_SCAN_ERR_DTYPE for an unknown value).
+ *  - Supported (MAMBA_SCAN_ERR_UNSUPPORTED otherwise): len % 4 == 0, dim % 8 == 0 and
+ *    dim <= 4096, dt_rank % 8 == 0 and dt_rank <= 64, dt_rank + 2*dstate <= 128,
+ *    1 <= d_conv <= 4, dim*len and (dt_rank + 2*dstate)*len below 2^30 (one batch of a tensor
+ *    under 2 GiB); x, u, delta, xdbl 8-byte aligned; w_x, w_dt 16-byte aligned.
+ *  - u, xdbl and delta are written in full; they may not overlap each other or any input
+ *    (MAMBA_SCAN_ERR_ARGS).
+ *  - Enqueued on `stream` as one kernel; results are bitwise deterministic.
+ */
+typedef struct mamba_upstream_ptrs {
+    const void* x;        /* (batch, dim, len) bf16 */
+    const float* conv_w;  /* (dim, d_conv) */
+    const float* conv_b;  /* (dim) or NULL */
+    const void* w_x;      /* (dt_rank + 2*dstate, dim) bf16 */
+    const void* w_dt;     /* (dim, dt_rank) bf16 */
+    void* u;              /* out: (batch, dim, len) bf16 */
+    void* xdbl;           /* out: (batch, dt_rank + 2*dstate, len) bf16 */
+    void* delta;          /* out: (batch, dim, len) bf16 */
+} mamba_upstream_ptrs;
+
+typedef struct mamba_upstream_shape {
+    int64_t batch, dim, len, dstate, dt_rank, d_conv;
+} mamba_upstream_shape;
+
+int mamba_block_upstream(const mamba_upstream_ptrs* p, const mamba_upstream_shape* s,
+                         mamba_scan_dtype dtype, void* stream);
 
 /* Static message for an error code; never NULL. */
 const char* mamba_scan_strerror(int code);

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "../../include/mamba_scan.h"
+#include "block_upstream.hpp"
 #include "common.hpp"
 #include "scan_bwd.hpp"
 #include "scan_generic.hpp"
@@ -244,6 +245,59 @@ int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool sp = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) != 0;
     return dtype == MAMBA_SCAN_BF16 ? launch_bwd<bf16_t>(p, *s, sp, hs) : launch_bwd<float>(p, *s, sp, hs);
+}
+
+int mamba_block_upstream(const mamba_upstream_ptrs* p, const mamba_upstream_shape* s, mamba_scan_dtype dtype,
+                         void* stream) {
+    if (!p || !s) return MAMBA_SCAN_ERR_NULL;
+    if (!p->x || !p->conv_w || !p->w_x || !p->w_dt || !p->u || !p->xdbl || !p->delta) return MAMBA_SCAN_ERR_NULL;
+    if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0 || s->dt_rank <= 0 || s->d_conv <= 0)
+        return MAMBA_SCAN_ERR_SHAPE;
+    if (dtype != MAMBA_SCAN_BF16) return dtype == MAMBA_SCAN_F32 ? MAMBA_SCAN_ERR_UNSUPPORTED : MAMBA_SCAN_ERR_DTYPE;
+    const int64_t J = s->dt_rank + 2 * s->dstate;
+    if (s->len % 4 || s->dim % 8 || s->dim > kUpMaxDim || s->dt_rank % 8 || s->dt_rank > 64 || J > 128 || s->d_conv > 4)
+        return MAMBA_SCAN_ERR_UNSUPPORTED;
+    if (!aligned(p->x, 8) || !aligned(p->u, 8) || !aligned(p->delta, 8) || !aligned(p->xdbl, 8) ||
+        !aligned(p->w_x, 16) || !aligned(p->w_dt, 16) || !aligned(p->conv_w, 4) ||
+        (p->conv_b && !aligned(p->conv_b, 4)))
+        return MAMBA_SCAN_ERR_UNSUPPORTED;
+    if (s->batch * ((s->len + kUpTT - 1) / kUpTT) > 0x7fffffff) return MAMBA_SCAN_ERR_UNSUPPORTED;
+    // one batch of each tensor is addressed with 32-bit byte offsets
+    if (s->dim * s->len * 2 >= ((int64_t)1 << 31) || J * s->len * 2 >= ((int64_t)1 << 31))
+        return MAMBA_SCAN_ERR_UNSUPPORTED;
+    const int64_t DL = s->batch * s->dim * s->len;
+    auto span = [](const void* ptr, int64_t bytes) {
+        Span x{0, 0, false};
+        if (!ptr) return x;
+        x.lo = reinterpret_cast<uintptr_t>(ptr);
+        x.hi = x.lo + (uintptr_t)bytes;
+        x.valid = true;
+        return x;
+    };
+    const Span ins[] = {span(p->x, DL * 2), span(p->conv_w, s->dim * s->d_conv * 4), span(p->conv_b, s->dim * 4),
+                        span(p->w_x, J * s->dim * 2), span(p->w_dt, s->dim * s->dt_rank * 2)};
+    const Span outs[] = {span(p->u, DL * 2), span(p->xdbl, s->batch * J * s->len * 2), span(p->delta, DL * 2)};
+    for (const Span& o : outs) {
+        for (const Span& i : ins)
+            if (overlaps(o, i)) return MAMBA_SCAN_ERR_ARGS;
+        for (const Span& o2 : outs)
+            if (&o2 != &o && overlaps(o, o2)) return MAMBA_SCAN_ERR_ARGS;
+    }
+    UpParams q;
+    q.x = static_cast<const uint16_t*>(p->x);
+    q.conv_w = p->conv_w;
+    q.conv_b = p->conv_b;
+    q.w_x = static_cast<const uint16_t*>(p->w_x);
+    q.w_dt = static_cast<const uint16_t*>(p->w_dt);
+    q.u = static_cast<uint16_t*>(p->u);
+    q.xdbl = static_cast<uint16_t*>(p->xdbl);
+    q.delta = static_cast<uint16_t*>(p->delta);
+    q.batch = s->batch;
+    q.dim = s->dim;
+    q.len = s->len;
+    q.dstate = (int)s->dstate;
+    q.dt_rank = (int)s->dt_rank;
+    return launch_upstream(q, (int)s->d_conv, static_cast<hipStream_t>(stream));
 }
 
 int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_scan_strides* st_in,

@@ -53,6 +53,14 @@ class BwdPtrs(ctypes.Structure):
                                   "ddelta_bias", "dh0", "workspace")] + [("workspace_bytes", _I64)]
 
 
+class UpPtrs(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("x", "conv_w", "conv_b", "w_x", "w_dt", "u", "xdbl", "delta")]
+
+
+class UpShape(ctypes.Structure):
+    _fields_ = [(n, _I64) for n in ("batch", "dim", "len", "dstate", "dt_rank", "d_conv")]
+
+
 class MambaScanError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"mamba_scan_fwd failed ({code}): {msg}")
@@ -85,6 +93,8 @@ def load_library(path: str = LIB_PATH):
                                    ctypes.c_uint32, _P]
     lib.mamba_scan_bwd_workspace_bytes.restype = _I64
     lib.mamba_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, ctypes.c_uint32]
+    lib.mamba_block_upstream.restype = ctypes.c_int
+    lib.mamba_block_upstream.argtypes = [ctypes.POINTER(UpPtrs), ctypes.POINTER(UpShape), ctypes.c_int, _P]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -307,3 +317,60 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     """Differentiable form of ``selective_scan_fn`` (torch autograd through the HIP backward)."""
     y, ls = SelectiveScan.apply(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
     return (y, ls) if return_last_state else y
+
+
+def block_upstream(x, conv_w, conv_b, w_x, w_dt, dstate, dt_rank, out=None):
+    """The stages in front of the scan (``mamba_block_upstream``): causal depthwise conv1d + SiLU,
+    x_proj, dt_proj, each output rounded to bf16.
+
+    x: (batch, dim, L) bf16; conv_w: (dim, d_conv) fp32 (a Conv1d weight (dim, 1, d_conv) may be
+    passed); conv_b: (dim,) fp32 or None; w_x: (dt_rank + 2 dstate, dim) bf16; w_dt: (dim, dt_rank)
+    bf16. Returns (u, xdbl, delta), bf16; the scan's B and C are views of xdbl (see
+    :func:`split_xdbl`). ``out`` = optional preallocated (u, xdbl, delta).
+    """
+    lib = load_library()
+    if conv_w.dim() == 3:
+        conv_w = conv_w.reshape(conv_w.shape[0], conv_w.shape[2])
+    x, conv_w, w_x, w_dt = (t.contiguous() for t in (x, conv_w, w_x, w_dt))
+    conv_b = None if conv_b is None else conv_b.contiguous()
+    for name, t, dt in (("x", x, torch.bfloat16), ("w_x", w_x, torch.bfloat16), ("w_dt", w_dt, torch.bfloat16),
+                        ("conv_w", conv_w, torch.float32)) + ((("conv_b", conv_b, torch.float32),) if conv_b is not None else ()):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != x.device or not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU of x")
+    batch, dim, L = x.shape
+    J = dt_rank + 2 * dstate
+    if out is None:
+        u = torch.empty_like(x)
+        xdbl = torch.empty((batch, J, L), dtype=torch.bfloat16, device=x.device)
+        delta = torch.empty_like(x)
+    else:
+        u, xdbl, delta = out
+    ptrs = UpPtrs(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(w_x), _ptr(w_dt), _ptr(u), _ptr(xdbl), _ptr(delta))
+    shape = UpShape(batch, dim, L, dstate, dt_rank, conv_w.shape[1])
+    with torch.cuda.device(x.device):
+        rc = lib.mamba_block_upstream(ctypes.byref(ptrs), ctypes.byref(shape), BF16,
+                                      torch.cuda.current_stream(x.device).cuda_stream)
+    if rc != 0:
+        err = MambaScanError(rc, strerror(rc))
+        if rc in (-1, -2, -3, -4, -5, -6, -8):
+            raise ValueError(str(err)) from err
+        raise err
+    return u, xdbl, delta
+
+
+def split_xdbl(xdbl, dt_rank, dstate):
+    """(dt rows, B, C) as views of x_dbl, in the split order dt_rank, dstate, dstate."""
+    return xdbl[:, :dt_rank], xdbl[:, dt_rank:dt_rank + dstate], xdbl[:, dt_rank + dstate:]
+
+
+def block_ssm(x, conv_w, conv_b, w_x, w_dt, dt_bias, A, D=None, z=None, return_last_state=False, h0=None):
+    """The selective-SSM part of a Mamba block: :func:`block_upstream` then the scan with
+    delta_bias = dt_proj's bias and softplus on, B and C read in place from x_dbl."""
+    dstate = A.shape[1]
+    dt_rank = w_dt.shape[1]
+    u, xdbl, delta = block_upstream(x, conv_w, conv_b, w_x, w_dt, dstate, dt_rank)
+    _, B, C = split_xdbl(xdbl, dt_rank, dstate)
+    return selective_scan_fn(u, delta, A, B, C, D=D, z=z, delta_bias=dt_bias, delta_softplus=True,
+                             return_last_state=return_last_state, h0=h0)

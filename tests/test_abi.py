@@ -21,11 +21,11 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def header_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(mamba_scan_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(mamba_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == ["mamba_scan_abi_version", "mamba_scan_bwd",
+    assert header_functions() == ["mamba_block_upstream", "mamba_scan_abi_version", "mamba_scan_bwd",
                                   "mamba_scan_bwd_workspace_bytes", "mamba_scan_fwd",
                                   "mamba_scan_strerror", "mamba_scan_workspace_bytes"]
 
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 2
+    assert scan.load_library().mamba_scan_abi_version() == 3
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -190,3 +190,49 @@ def test_backward_workspace_query():
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 3, 0) == -4
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 0, 1 << 1) == -6
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(1, 1, 1, 300)), 0, 0) == -5
+
+
+# ---- upstream entry point ----
+
+def fake_up(mutate=None, dtype=scan.BF16, shape=(2, 192, 200, 16, 8, 4)):
+    lib = scan.load_library()
+    base = 1 << 40
+    names = [f[0] for f in scan.UpPtrs._fields_]
+    ptrs = scan.UpPtrs(**{n: base + (i + 1) * (1 << 32) for i, n in enumerate(names)})
+    ctx = dict(ptrs=ptrs, shape=scan.UpShape(*shape), dtype=dtype)
+    if mutate:
+        mutate(ctx)
+    return lib.mamba_block_upstream(ctypes.byref(ctx["ptrs"]), ctypes.byref(ctx["shape"]), ctx["dtype"], None)
+
+
+UP_CASES = [
+    ("null_x", _set("ptrs", "x", None), -1),
+    ("null_delta", _set("ptrs", "delta", None), -1),
+    ("zero_batch", _set("shape", "batch", 0), -2),
+    ("zero_dt_rank", _set("shape", "dt_rank", 0), -2),
+    ("f32_unsupported", lambda c: c.__setitem__("dtype", scan.F32), -8),
+    ("bad_dtype", lambda c: c.__setitem__("dtype", 5), -4),
+    ("len_not_multiple_of_4", _set("shape", "len", 202), -8),
+    ("dim_not_multiple_of_8", _set("shape", "dim", 196), -8),
+    ("dim_above_4096", _set("shape", "dim", 4104), -8),
+    ("dt_rank_not_multiple_of_8", _set("shape", "dt_rank", 12), -8),
+    ("dt_rank_above_64", _set("shape", "dt_rank", 72), -8),
+    ("projection_rows_above_128", _set("shape", "dstate", 61), -8),
+    ("d_conv_above_4", _set("shape", "d_conv", 5), -8),
+    ("misaligned_w_x", lambda c: setattr(c["ptrs"], "w_x", c["ptrs"].w_x + 8), -8),
+    ("misaligned_x", lambda c: setattr(c["ptrs"], "x", c["ptrs"].x + 2), -8),
+    ("u_aliases_x", lambda c: setattr(c["ptrs"], "u", c["ptrs"].x), -6),
+    ("outputs_alias", lambda c: setattr(c["ptrs"], "xdbl", c["ptrs"].delta), -6),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", UP_CASES, ids=[c[0] for c in UP_CASES])
+def test_upstream_invalid_arguments_are_rejected(name, mutate, code):
+    assert fake_up(mutate) == code
+
+
+def test_upstream_binding_refuses_wrong_dtypes():
+    x = torch.zeros((1, 8, 4), dtype=torch.float32)
+    with pytest.raises((TypeError, ValueError)):
+        scan.block_upstream(x, torch.zeros(8, 4), None, torch.zeros(40, 8, dtype=torch.bfloat16),
+                            torch.zeros(8, 8, dtype=torch.bfloat16), 16, 8)

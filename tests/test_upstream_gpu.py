@@ -1,0 +1,141 @@
+"""GPU parity of the block's upstream stages (``mamba_block_upstream`` through the C ABI) against the
+fp64 upstream oracle on identical inputs.
+
+Both sides round u, x_dbl and delta to bf16, the GPU from fp32 sums, the oracle from fp64 sums,
+and each stage reads its own side's rounded values. So, element by element, with E the bound on
+the difference of the two values before rounding:
+    |g - r| <= 2 E + 2^-7 (|r| + 2 E)          (one bf16 spacing is at most 2^-7 |value|)
+    u:      E = 2^-18 (|conv_b| + sum_k |w_k x_k|)                      fp32 fma chain + SiLU
+    x_dbl:  E = sum_d |w_x| |u_g - u_r| + dim 2^-23 sum_d |w_x u_r|      the other side's u, fp32 sum
+    delta:  E = sum_r |w_dt| |dt_g - dt_r| + dt_rank 2^-23 sum_r |w_dt dt_r|
+and most elements are bit-identical (a wrong rounding mode or a misplaced operand is not).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+import oracle
+from selective_state_space_29_amd import scan, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def widen(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def bits_of(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_gpu(x, dstate, dt_rank):
+    u, xdbl, delta = scan.block_upstream(
+        bf16_dev(x["x"]), torch.from_numpy(x["conv_w"]).cuda(),
+        None if x["conv_b"] is None else torch.from_numpy(x["conv_b"]).cuda(),
+        bf16_dev(x["w_x"]), bf16_dev(x["w_dt"]), dstate, dt_rank)
+    torch.cuda.synchronize()
+    return {"u": bits_of(u), "xdbl": bits_of(xdbl), "delta": bits_of(delta)}
+
+
+def _bound_ok(g, r, E):
+    err = np.abs(widen(g) - widen(r))
+    tol = 2 * E + 2.0**-7 * (np.abs(widen(r)) + 2 * E) + 1e-30
+    bad = err > tol
+    return int(np.count_nonzero(bad)), float(np.max(err / tol))
+
+
+def check(x, dstate, dt_rank, min_exact=0.9):
+    g = run_gpu(x, dstate, dt_rank)
+    r = oracle.block_upstream(x["x"], x["conv_w"], x["conv_b"], x["w_x"], x["w_dt"], dstate, dt_rank)
+    K = x["conv_w"].shape[1]
+    xs = widen(x["x"])
+    L = xs.shape[-1]
+    # u
+    S = np.abs(x["conv_b"]).astype(np.float64)[None, :, None] if x["conv_b"] is not None else 0.0
+    S = S + np.zeros_like(xs)
+    for k in range(K):
+        shift = K - 1 - k  # tap k multiplies x[t - shift]
+        part = np.abs(x["conv_w"][:, k]).astype(np.float64)[None, :, None] * np.abs(xs)
+        S[..., shift:] += part[..., :L - shift] if shift else part
+    Eu = 2.0**-18 * S
+    # x_dbl
+    wx = np.abs(widen(x["w_x"]))
+    du = np.abs(widen(g["u"]) - widen(r["u"]))
+    Ex = np.matmul(wx, du) + x["x"].shape[1] * 2.0**-23 * np.matmul(wx, np.abs(widen(r["u"])))
+    # delta
+    wdt = np.abs(widen(x["w_dt"]))
+    ddt = np.abs(widen(g["xdbl"][:, :dt_rank]) - widen(r["xdbl"][:, :dt_rank]))
+    Ed = np.matmul(wdt, ddt) + dt_rank * 2.0**-23 * np.matmul(wdt, np.abs(widen(r["xdbl"][:, :dt_rank])))
+    for name, E in (("u", Eu), ("xdbl", Ex), ("delta", Ed)):
+        nbad, worst = _bound_ok(g[name], r[name], E)
+        exact = float(np.mean(g[name] == r[name]))
+        print(f"  {name}: {exact * 100:.3f}% bit-identical, worst err/bound {worst:.3f}", flush=True)
+        assert nbad == 0, f"{name}: {nbad} elements beyond the derived bound (worst {worst:.3g})"
+        assert exact >= min_exact, f"{name}: only {exact:.4f} bit-identical"
+    return g, r
+
+
+@pytest.mark.parametrize("wid", sorted(workloads.UPSTREAM))
+def test_upstream_workload_parity(wid):
+    w = workloads.UPSTREAM[wid]
+    print(f"upstream parity, workload {wid}: {w.name}", flush=True)
+    check(workloads.make_upstream_inputs(w), w.dstate, w.dt_rank)
+
+
+EDGE = [
+    # (batch, dim, dstate, dt_rank, L, d_conv, conv bias)
+    (1, 8, 1, 8, 4, 4, True),          # one chunk, one step group
+    (1, 16, 16, 64, 64, 4, True),      # dt_rank 64: two full k-steps; L one tile exactly
+    (2, 136, 32, 64, 132, 4, True),    # 128 projection rows (8 waves); ragged chunk and tile
+    (1, 1544, 16, 48, 68, 4, True),    # dim % 16 == 8: half of the last dt tile
+    (2, 256, 8, 16, 128, 3, False),    # d_conv 3, no bias
+    (1, 64, 4, 8, 36, 2, True),        # d_conv 2
+    (1, 72, 16, 32, 20, 1, True),      # d_conv 1 (no convolution, SiLU only)
+    (3, 320, 16, 24, 192, 4, True),    # dt_rank 24: zero-padded k-step
+]
+
+
+@pytest.mark.parametrize("idx", range(len(EDGE)))
+def test_upstream_edge_cases(idx):
+    batch, dim, dstate, dt_rank, L, d_conv, bias = EDGE[idx]
+    print(f"upstream edge case {EDGE[idx]}", flush=True)
+    x = workloads.make_upstream_case(29300 + idx, batch, dim, dstate, dt_rank, L, d_conv, bias)
+    check(x, dstate, dt_rank)
+
+
+def test_upstream_is_deterministic():
+    w = workloads.UPSTREAM[1]
+    x = workloads.make_upstream_inputs(w)
+    a = run_gpu(x, w.dstate, w.dt_rank)
+    b = run_gpu(x, w.dstate, w.dt_rank)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_block_ssm_is_upstream_then_scan():
+    """block_ssm = block_upstream, then the scan with B and C read in place from x_dbl and
+    dt_proj's bias as delta_bias: the same bits as running the two calls by hand on copies."""
+    w = workloads.UPSTREAM[1]
+    x = workloads.make_upstream_inputs(w)
+    dev = torch.device("cuda:0")
+    args = (bf16_dev(x["x"]), torch.from_numpy(x["conv_w"]).to(dev), torch.from_numpy(x["conv_b"]).to(dev),
+            bf16_dev(x["w_x"]), bf16_dev(x["w_dt"]))
+    A = torch.from_numpy(workloads.a_matrix(w.dim, w.dstate)).to(dev)
+    rng = np.random.default_rng(3)
+    dt_bias = torch.from_numpy(rng.uniform(-4, -1, w.dim).astype(np.float32)).to(dev)
+    D = torch.ones(w.dim, device=dev)
+    z = torch.from_numpy(rng.standard_normal((w.batch, w.dim, w.seqlen)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    y, ls = scan.block_ssm(*args, dt_bias, A, D=D, z=z, return_last_state=True)
+    u, xdbl, delta = scan.block_upstream(*args, w.dstate, w.dt_rank)
+    _, B, C = scan.split_xdbl(xdbl, w.dt_rank, w.dstate)
+    y2, ls2 = scan.selective_scan_fn(u, delta, A, B.contiguous(), C.contiguous(), D=D, z=z,
+                                     delta_bias=dt_bias, delta_softplus=True, return_last_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(ls, ls2)
+    assert torch.isfinite(y).all()
