@@ -57,6 +57,10 @@ def _bind(path: str):
     P = ctypes.c_void_p
     f.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int] + [P] * 5 + [P] * 4 + [ctypes.c_int] + [
         P, ctypes.c_int64, P, P, ctypes.c_int]
+    g = lib.oracle_selective_scan_ex
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int] + [P] * 5 + [P] * 4 + [ctypes.c_int] * 2 + [
+        P, ctypes.c_int64, P, P, ctypes.c_int]
     return lib
 
 
@@ -109,8 +113,9 @@ def _as(arr, kind):
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
-                   h0=None, rows=None, nthreads=None, lib_path=None):
-    """Reference scan in fp64.
+                   h0=None, rows=None, nthreads=None, lib_path=None, zoh_b=False):
+    """Reference scan in fp64. ``zoh_b``: B discretised by zero-order hold, (e^{dt A} - 1) / A * B
+    (dt * B where A = 0), instead of the selective scan's dt * B.
 
     u, delta, z: (batch, dim, L); B, C: (batch, N, L), all fp32 or all bf16 bit patterns
     (numpy uint16). A: (dim, N) fp32; D, delta_bias: (dim,) fp32; h0: (batch, dim, N), widened to fp64.
@@ -146,10 +151,10 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     def ptr(a):
         return None if a is None else a.ctypes.data
 
-    rc = lib.oracle_selective_scan(
+    rc = lib.oracle_selective_scan_ex(
         batch, dim, L, N, in_dtype, ptr(u), ptr(delta), ptr(z), ptr(B), ptr(C), ptr(A), ptr(D),
-        ptr(delta_bias), ptr(h0), int(bool(delta_softplus)), ptr(rows_arr), nrows, ptr(y), ptr(ls),
-        int(nthreads or default_threads()),
+        ptr(delta_bias), ptr(h0), int(bool(delta_softplus)), int(bool(zoh_b)), ptr(rows_arr), nrows,
+        ptr(y), ptr(ls), int(nthreads or default_threads()),
     )
     if rc != 0:
         raise RuntimeError(f"oracle_selective_scan failed with {rc}")

@@ -40,6 +40,7 @@ typedef struct {
     const float *A, *Dvec, *delta_bias;
     const double* h0;
     int delta_softplus;
+    int zoh_b;
     const int64_t* rows;
     int64_t nrows;
     double *y, *last_state;
@@ -57,6 +58,11 @@ static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* Zero-order-hold input coefficient of one diagonal state: B_d = A^-1 (e^{A dt} - 1) B, written
+ * per state as (e^{A dt} - 1) / A ("手把手用PyTorch实现Mamba的SSM层…" §2.1); at A = 0 (not
+ * invertible) its limit dt. expm1 keeps it accurate when A dt is small. */
+static double zoh_coef(double dt, double An) { return An == 0.0 ? dt : expm1(dt * An) / An; }
+
 /* One row (b, d): writes y[out_row, 0..L) and last_state[out_row, 0..N). */
 static void scan_row(const orc_args* a, int64_t b, int64_t d, int64_t out_row, double* h) {
     const int64_t L = a->len, N = a->dstate, D = a->dim;
@@ -73,8 +79,10 @@ static void scan_row(const orc_args* a, int64_t b, int64_t d, int64_t out_row, d
         for (int64_t n = 0; n < N; ++n) {
             const double Bt = widen(a->B, a->in_dtype, bc_off + n * L + t);
             const double Ct = widen(a->C, a->in_dtype, bc_off + n * L + t);
-            const double dA = exp(dt * (double)a->A[d * N + n]);
-            h[n] = dA * h[n] + dt * Bt * ut;
+            const double An = (double)a->A[d * N + n];
+            const double dA = exp(dt * An);
+            const double dB = a->zoh_b ? zoh_coef(dt, An) : dt; /* discretised B per unit B */
+            h[n] = dA * h[n] + dB * Bt * ut;
             acc += Ct * h[n];
         }
         double v = acc + dskip * ut;
@@ -111,17 +119,17 @@ static void* orc_worker(void* p) {
  * scan split at any step continues exactly from the fp64 state of its first part.
  * Returns 0, or a negative value on a bad argument or allocation failure.
  */
-int oracle_selective_scan(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int in_dtype,
-                          const void* u, const void* delta, const void* z, const void* B,
-                          const void* C, const float* A, const float* Dvec,
-                          const float* delta_bias, const double* h0, int delta_softplus,
-                          const int64_t* rows, int64_t nrows, double* y, double* last_state,
-                          int nthreads) {
+int oracle_selective_scan_ex(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int in_dtype,
+                             const void* u, const void* delta, const void* z, const void* B,
+                             const void* C, const float* A, const float* Dvec,
+                             const float* delta_bias, const double* h0, int delta_softplus,
+                             int zoh_b, const int64_t* rows, int64_t nrows, double* y,
+                             double* last_state, int nthreads) {
     if (batch <= 0 || dim <= 0 || len <= 0 || dstate <= 0) return -2;
     if (in_dtype != ORC_F32 && in_dtype != ORC_BF16) return -4;
     if (!u || !delta || !B || !C || !A || !y) return -1;
     orc_args a = {batch, dim, len, dstate, in_dtype, u, delta, z, B, C, A, Dvec, delta_bias, h0,
-                  delta_softplus, rows, rows ? nrows : batch * dim, y, last_state};
+                  delta_softplus, zoh_b, rows, rows ? nrows : batch * dim, y, last_state};
     if (rows)
         for (int64_t k = 0; k < nrows; ++k)
             if (rows[k] < 0 || rows[k] >= batch * dim) return -2;
@@ -151,6 +159,18 @@ int oracle_selective_scan(int64_t batch, int64_t dim, int64_t len, int64_t dstat
     for (int t = started + 1; t < nthreads; ++t)
         if (orc_worker(&jobs[t]) != NULL) ok = 0;
     return ok ? 0 : -8;
+}
+
+/* The scan with Euler B (dB = dt B), as the pages' selective scan computes it. */
+int oracle_selective_scan(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int in_dtype,
+                          const void* u, const void* delta, const void* z, const void* B,
+                          const void* C, const float* A, const float* Dvec,
+                          const float* delta_bias, const double* h0, int delta_softplus,
+                          const int64_t* rows, int64_t nrows, double* y, double* last_state,
+                          int nthreads) {
+    return oracle_selective_scan_ex(batch, dim, len, dstate, in_dtype, u, delta, z, B, C, A, Dvec,
+                                    delta_bias, h0, delta_softplus, 0, rows, nrows, y, last_state,
+                                    nthreads);
 }
 
 /* ----------------------------------------------------------------------------------------------
@@ -286,7 +306,7 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t dim, int64_t len, int64_t d
         return -1;
     if (z && !gz) return -1;
     orc_args f = {batch, dim, len, dstate, in_dtype, u, delta, z, B, C, A, Dvec, delta_bias, h0,
-                  delta_softplus, NULL, batch * dim, NULL, NULL};
+                  delta_softplus, 0, NULL, batch * dim, NULL, NULL};
     const int64_t nrows = batch * dim;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > ORC_MAX_THREADS) nthreads = ORC_MAX_THREADS;

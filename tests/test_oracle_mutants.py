@@ -13,7 +13,7 @@ import pins
 
 MUTANTS = {
     "drop_skip": ("double v = acc + dskip * ut;", "double v = acc;"),
-    "sign_of_decay": ("exp(dt * (double)a->A[d * N + n])", "exp(-dt * (double)a->A[d * N + n])"),
+    "sign_of_decay": ("exp(dt * An)", "exp(-dt * An)"),
     "B_for_C": ("acc += Ct * h[n];", "acc += Bt * h[n];"),
     "C_one_step_late": ("widen(a->C, a->in_dtype, bc_off + n * L + t)",
                         "widen(a->C, a->in_dtype, bc_off + n * L + (t > 0 ? t - 1 : t))"),
@@ -23,9 +23,9 @@ MUTANTS = {
                              "a->delta_softplus ? exp(x) : softplus(x)"),
     "bias_dropped": ("widen(a->delta, a->in_dtype, row_off + t) + bias;",
                      "widen(a->delta, a->in_dtype, row_off + t);"),
-    "dt_missing_from_input": ("dt * Bt * ut", "Bt * ut"),
-    "output_before_update": ("h[n] = dA * h[n] + dt * Bt * ut;\n            acc += Ct * h[n];",
-                             "acc += Ct * h[n];\n            h[n] = dA * h[n] + dt * Bt * ut;"),
+    "dt_missing_from_input": ("a->zoh_b ? zoh_coef(dt, An) : dt;", "a->zoh_b ? zoh_coef(dt, An) : 1.0;"),
+    "output_before_update": ("h[n] = dA * h[n] + dB * Bt * ut;\n            acc += Ct * h[n];",
+                             "acc += Ct * h[n];\n            h[n] = dA * h[n] + dB * Bt * ut;"),
     "h0_ignored": ("h[n] = a->h0 ? a->h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     "gate_on_u": ("if (a->z) v *= silu(widen(a->z,", "if (a->z) v *= silu(widen(a->u,"),
     "bf16_widen_shift": ("(uint32_t)((const uint16_t*)p)[i] << 16", "(uint32_t)((const uint16_t*)p)[i] << 15"),
