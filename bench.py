@@ -30,6 +30,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 VALU_PEAK_TFLOPS = 157.3
 SLOTS_PER_ELEMENT = 8      # mul (dt*A), exp, mul (dt*u*B), fma (h), fma (y)
 SLOTS_PER_ROW_STEP = 30    # softplus, dt*u, bias, skip, silu gate
+# zero-order-hold B adds, per element: dt*A, the 4-term series and dt*p, dA - 1 and * 1/A, the
+# compare and select, and * u
+SLOTS_PER_ELEMENT_ZOH = SLOTS_PER_ELEMENT + 11
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "scan_tiled_mamba130m_traffic.json")
 RATES_LIB = os.path.join(ROOT, "selective_state_space_29_amd", "probe", "libmscan_rates.so")
 
@@ -53,6 +56,8 @@ def parse():
                     help="instead of the scan, time the block's upstream stages "
                          "(mamba_block_upstream: conv1d + SiLU, x_proj, dt_proj) at the Mamba-130m "
                          "shape, and the upstream followed by the scan")
+    ap.add_argument("--zoh", action="store_true",
+                    help="the forward scan with B discretised by zero-order hold (MAMBA_SCAN_ZOH_B)")
     ap.add_argument("--chunk", type=int, default=1, help="steps per decode call")
     ap.add_argument("--decode-calls", type=int, default=256, help="timed decode calls")
     ap.add_argument("--copy-mb", type=float, default=0.0,
@@ -133,7 +138,7 @@ def transcendentals_per_launch(w):
     return w.elements + w.rows * w.seqlen * per_row_step
 
 
-def cpu_baseline_one_thread(w, inputs):
+def cpu_baseline_one_thread(w, inputs, zoh=False):
     """fp64 oracle on one thread over batch 0 of the workload (all its channels)."""
     import oracle
 
@@ -142,7 +147,7 @@ def cpu_baseline_one_thread(w, inputs):
     t0 = time.perf_counter()
     oracle.selective_scan(one["u"], one["delta"], one["A"], one["B"], one["C"], D=one["D"],
                           z=one["z"], delta_bias=one["delta_bias"], delta_softplus=w.softplus,
-                          nthreads=1)
+                          nthreads=1, zoh_b=zoh)
     dt = time.perf_counter() - t0
     n = w.dim * w.seqlen * w.dstate
     return {"value": round(n / dt / 1e9, 4), "unit": "Gelem/s", "cores": 1, "kind": "oracle",
@@ -150,7 +155,7 @@ def cpu_baseline_one_thread(w, inputs):
                       f"states), fp64, {dt:.2f} s on one thread"}
 
 
-def cpu_baseline(w, inputs):
+def cpu_baseline(w, inputs, zoh=False):
     """fp64 oracle over the whole workload on every core this process may use."""
     import oracle
 
@@ -158,7 +163,7 @@ def cpu_baseline(w, inputs):
     t0 = time.perf_counter()
     oracle.selective_scan(inputs["u"], inputs["delta"], inputs["A"], inputs["B"], inputs["C"],
                           D=inputs["D"], z=inputs["z"], delta_bias=inputs["delta_bias"],
-                          delta_softplus=w.softplus, nthreads=cores)
+                          delta_softplus=w.softplus, nthreads=cores, zoh_b=zoh)
     dt = time.perf_counter() - t0
     return {"value": round(w.elements / dt / 1e9, 4), "unit": "Gelem/s", "cores": cores,
             "kind": "oracle",
@@ -582,7 +587,7 @@ def main():
         scan.selective_scan_fn(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
                                delta_bias=s["delta_bias"], delta_softplus=w.softplus,
                                return_last_state=w.last_state, kernel=kernel, out=s["y"],
-                               last_state_out=s["ls"])
+                               last_state_out=s["ls"], zoh_b=args.zoh)
 
     for i in range(args.warmup):
         step(i)
@@ -608,7 +613,7 @@ def main():
     value = w.elements / (ms_per_step * 1e-3) / 1e9
     alg_bytes = w.algorithmic_bytes()
     achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
-    slots = w.elements * SLOTS_PER_ELEMENT + w.rows * w.seqlen * SLOTS_PER_ROW_STEP
+    slots = w.elements * (SLOTS_PER_ELEMENT_ZOH if args.zoh else SLOTS_PER_ELEMENT) + w.rows * w.seqlen * SLOTS_PER_ROW_STEP
     achieved_tflops = 2 * slots / (mean_launch_ms * 1e-3) / 1e12
 
     check = None
@@ -628,7 +633,7 @@ def main():
             a, c = oracle.selective_scan(
                 xr["u"][s1], xr["delta"][s1], xr["A"][s1], xr["B"][s1], xr["C"][s1], D=xr["D"][s1],
                 z=None if xr["z"] is None else xr["z"][s1], delta_bias=xr["delta_bias"][s1],
-                delta_softplus=w.softplus)
+                delta_softplus=w.softplus, zoh_b=args.zoh)
             yr.append(a.reshape(-1))
             lr.append(c.reshape(-1))
         yr, lr = np.stack(yr), np.stack(lr)
@@ -640,9 +645,9 @@ def main():
     cpu = cpu1 = None
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on the whole workload")
-        cpu = cpu_baseline(w, x)
+        cpu = cpu_baseline(w, x, args.zoh)
         log(f"cpu baseline: {cpu}")
-        cpu1 = cpu_baseline_one_thread(w, x)
+        cpu1 = cpu_baseline_one_thread(w, x, args.zoh)
         log(f"cpu baseline, one thread: {cpu1}")
 
     rates = measured_rates()
@@ -654,7 +659,8 @@ def main():
              "frac": None if rates is None else round(trans_rate / rates["exp_T_lane_ops_per_s"], 4)}
 
     out = {
-        "metric": "scan Gelem/s (B*D*L*N) + % HBM roofline, Mamba-130m layer shape, L=2048",
+        "metric": "scan Gelem/s (B*D*L*N) + % HBM roofline, Mamba-130m layer shape, L=2048"
+                  + (", zero-order-hold B" if args.zoh else ""),
         "value": round(value, 2),
         "unit": "Gelem/s",
         "n_gpus": 1,
@@ -668,11 +674,12 @@ def main():
         "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seq_len": w.seqlen, "storage": w.dtype, "z_gate": w.has_z,
-                   "last_state": w.last_state, "kernel": args.kernel, "buffer_sets": len(sets)},
+                   "last_state": w.last_state, "kernel": args.kernel, "buffer_sets": len(sets),
+                   "zoh_b": args.zoh},
         "roofline": {"bound": "alu", "achieved": round(achieved_tflops, 2),
                      "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / VALU_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(w, args.kernel),
+                     "traffic": None if args.zoh else measured_traffic(w, args.kernel),
                      "valu_slots_per_launch": slots, "algorithmic_bytes": alg_bytes,
                      "hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)},

@@ -57,10 +57,14 @@ typedef enum mamba_scan_dtype {
 /* flags */
 #define MAMBA_SCAN_DELTA_SOFTPLUS (1u << 0)    /* dt = softplus(.) ; clear: dt = exp(.) */
 #define MAMBA_SCAN_RETURN_LAST_STATE (1u << 1) /* write last_state */
+/* B discretised by zero-order hold: the input term becomes (exp(dt*A[d,n]) - 1) / A[d,n] * B * u
+ * (dt * B * u where A[d,n] = 0) instead of dt * B * u. "手把手用PyTorch实现Mamba的SSM层…" §2.1:
+ * B_d = A^-1 (e^{A dt} - I) B, for a diagonal A. Forward only (mamba_scan_bwd rejects it). */
+#define MAMBA_SCAN_ZOH_B (1u << 2)
 /* Kernel selection, for testing and tuning. Default (neither bit): the library picks. */
 #define MAMBA_SCAN_FORCE_GENERIC (1u << 8) /* one lane per row, any shape and alignment */
 #define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
-#define MAMBA_SCAN_KNOWN_FLAGS 0x303u
+#define MAMBA_SCAN_KNOWN_FLAGS 0x307u
 
 /* error codes */
 #define MAMBA_SCAN_OK 0

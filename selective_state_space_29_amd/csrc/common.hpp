@@ -26,6 +26,7 @@ struct ScanParams {
     int64_t sh0_b, sh0_d, sls_b, sls_d;
     int64_t sA_d, sD, sbias;
     int softplus;
+    int zoh_b;  // B discretised by zero-order hold instead of dt * B
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -58,6 +59,19 @@ __device__ __forceinline__ float softplus_f(float x) {
 // dt from the biased delta: softplus, or exp when the softplus flag is clear.
 __device__ __forceinline__ float delta_to_dt(float x, int softplus) {
     return softplus ? softplus_f(x) : hw_exp2(x * kLog2e);
+}
+
+// Zero-order-hold coefficient of B for one diagonal state, (e^{dt A} - 1) / A, given x = dt * A,
+// dA = e^x (already computed for the decay) and invA = 1 / A (0 where A = 0). For |x| < 1/16 the
+// series dt (1 + x/2 + x^2/6 + x^3/24 + x^4/120), whose truncation is below 2^-29 relative and
+// which is exact at A = 0 (dt); above, (dA - 1) * invA, where |dA - 1| > 0.06 keeps the
+// cancellation under 2^-20 relative. The discretisation of "手把手用PyTorch实现Mamba的SSM层…" §2.1,
+// B_d = A^-1 (e^{A dt} - I) B, for a diagonal A.
+__device__ __forceinline__ float zoh_coef_f(float dt, float x, float dA, float invA) {
+    const float p = __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 120.0f, 1.0f / 24.0f), 1.0f / 6.0f), 0.5f), 1.0f);
+    const float small = dt * p;
+    const float big = (dA - 1.0f) * invA;
+    return __builtin_fabsf(x) < 0.0625f ? small : big;
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).

@@ -113,6 +113,7 @@ ScanParams make_params(const mamba_scan_ptrs* p, const mamba_scan_shape* s, cons
     q.bias = p->delta_bias;
     q.h0 = p->h0;
     q.y = p->y;
+    q.zoh_b = (flags & MAMBA_SCAN_ZOH_B) ? 1 : 0;
     q.last_state = (flags & MAMBA_SCAN_RETURN_LAST_STATE) ? p->last_state : nullptr;
     q.batch = s->batch;
     q.dim = s->dim;

@@ -8,7 +8,8 @@
 //
 // Per step and state it evaluates the recurrence of "Mamba代码实战…" §3.1-§3.2 as
 //   dA = 2^(dt * A*log2(e)),  h = dA * h + (dt*u) * B,  y += C * h
-// followed by the skip and silu gate of §3.3.
+// followed by the skip and silu gate of §3.3; with zoh_b the input term is the zero-order-hold
+// one, (e^{dt A} - 1)/A * u * B.
 #pragma once
 
 #include "common.hpp"
@@ -35,13 +36,15 @@ __global__ __launch_bounds__(64) void scan_generic_kernel(ScanParams p) {
         const int nb = (int)((p.dstate - n0) < NB ? (p.dstate - n0) : NB);
         const bool first = (n0 == 0);
         const bool last = (n0 + NB >= p.dstate);
-        float h[NB], a2[NB];
+        float h[NB], a2[NB], an[NB], ian[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             h[j] = 0.0f;
-            a2[j] = 0.0f;
+            a2[j] = an[j] = ian[j] = 0.0f;
             if (j < nb) {
-                a2[j] = p.A[d * p.sA_d + n0 + j] * kLog2e;
+                an[j] = p.A[d * p.sA_d + n0 + j];
+                a2[j] = an[j] * kLog2e;
+                ian[j] = an[j] != 0.0f ? 1.0f / an[j] : 0.0f;
                 if (p.h0) h[j] = p.h0[b * p.sh0_b + d * p.sh0_d + n0 + j];
             }
         }
@@ -56,7 +59,8 @@ __global__ __launch_bounds__(64) void scan_generic_kernel(ScanParams p) {
                     const float bv = to_f32(Bb[(n0 + j) * p.sB_n + t]);
                     const float cv = to_f32(Cb[(n0 + j) * p.sC_n + t]);
                     const float dA = hw_exp2(dt * a2[j]);
-                    h[j] = __builtin_fmaf(dA, h[j], dtu * bv);
+                    const float inc = p.zoh_b ? zoh_coef_f(dt, dt * an[j], dA, ian[j]) * uu * bv : dtu * bv;
+                    h[j] = __builtin_fmaf(dA, h[j], inc);
                     acc = __builtin_fmaf(cv, h[j], acc);
                 }
             }

@@ -184,7 +184,7 @@ __device__ __forceinline__ void buffer_store(const float (&v)[QS], __amdgpu_buff
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, (int)off, 0, 0);
 }
 
-template <typename T, int S, int W, int TC, bool SOFTPLUS, bool HAS_Z, bool EXACT>
+template <typename T, int S, int W, int TC, bool SOFTPLUS, bool HAS_Z, bool EXACT, bool ZOH>
 __global__ __launch_bounds__(64 * W) void scan_tiled_kernel(ScanParams p) {
     constexpr int QS = TC / W;    // steps per thread in prologue/epilogue
     constexpr int NQ = TC / QS;   // step groups per channel and chunk (= W)
@@ -226,14 +226,16 @@ __global__ __launch_bounds__(64 * W) void scan_tiled_kernel(ScanParams p) {
     // ---- main-loop role: this lane's channel, this wave's states ----
     const int64_t dm = d0 + lane;
     const bool mvalid = dm < p.dim;
-    float a2[S], h[S];
+    float a2[S], h[S], an[S], ian[S];  // an, ian: A and 1/A (zero-order-hold B only)
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int n = nbase + s;
-        a2[s] = 0.0f;
+        a2[s] = an[s] = ian[s] = 0.0f;
         h[s] = 0.0f;
         if (wave_live && mvalid) {
-            a2[s] = p.A[dm * p.sA_d + n] * kLog2e;
+            an[s] = p.A[dm * p.sA_d + n];
+            a2[s] = an[s] * kLog2e;
+            if constexpr (ZOH) ian[s] = an[s] != 0.0f ? 1.0f / an[s] : 0.0f;
             if (p.h0) h[s] = p.h0[b * p.sh0_b + dm * p.sh0_d + n];
         }
     }
@@ -267,7 +269,8 @@ __global__ __launch_bounds__(64 * W) void scan_tiled_kernel(ScanParams p) {
         }
     };
 
-    // prologue of chunk c: dt and dt*u into LDS; keeps u and z for its epilogue
+    // prologue of chunk c: dt and dt*u (u alone with zero-order-hold B) into LDS; keeps u and z
+    // for its epilogue
     auto prologue = [&](int64_t c, auto set_tag, float (&cu)[QS], float (&cz)[QS]) {
         constexpr int k = decltype(set_tag)::value;
         const int64_t left = L - c * TC - QS * pq;
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(64 * W) void scan_tiled_kernel(ScanParams p) {
             cz[j] = HAS_Z ? rz[k].get(j) : 0.0f;
             const float v = dt_of<SOFTPLUS>(rdl[k].get(j) + pbias);
             dt[j] = (j < nvalid) ? v : 0.0f;  // steps beyond L leave h unchanged
-            dtu[j] = dt[j] * cu[j];
+            dtu[j] = ZOH ? cu[j] : dt[j] * cu[j];
         }
         lds_store<QS>(&s_dt[prow], dt);
         lds_store<QS>(&s_dtu[prow], dtu);
@@ -371,7 +374,12 @@ __global__ __launch_bounds__(64 * W) void scan_tiled_kernel(ScanParams p) {
                 float yv = 0.0f;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
-                    h[s] = __builtin_fmaf(dA[s][t], h[s], dtuv[t] * bv[s].get(t));
+                    float inc;
+                    if constexpr (ZOH)
+                        inc = zoh_coef_f(dtv[t], dtv[t] * an[s], dA[s][t], ian[s]) * dtuv[t] * bv[s].get(t);
+                    else
+                        inc = dtuv[t] * bv[s].get(t);
+                    h[s] = __builtin_fmaf(dA[s][t], h[s], inc);
                     yv = __builtin_fmaf(cv[s].get(t), h[s], yv);
                 }
                 yq[j] = yv;
@@ -396,7 +404,8 @@ __global__ __launch_bounds__(64 * W) void scan_tiled_kernel(ScanParams p) {
                 const float bvv = lane_load(Bw, s * sBn + t0 + i);
                 const float cvv = lane_load(Cw, s * sCn + t0 + i);
                 const float d = hw_exp2(dt * a2[s]);
-                h[s] = __builtin_fmaf(d, h[s], dtu * bvv);
+                const float inc = ZOH ? zoh_coef_f(dt, dt * an[s], d, ian[s]) * dtu * bvv : dtu * bvv;
+                h[s] = __builtin_fmaf(d, h[s], inc);
                 yv = __builtin_fmaf(cvv, h[s], yv);
             }
             yrow[i] = yv;
@@ -540,8 +549,11 @@ int launch_tiled_cfg(const ScanParams& q, hipStream_t stream) {
     const int64_t groups = q.batch * ((q.dim + 63) / 64);
     void* args[] = {const_cast<ScanParams*>(&q)};
     const bool exact = q.dstate == (int64_t)S * W;
-    const void* fn = exact ? reinterpret_cast<const void*>(&scan_tiled_kernel<T, S, W, TC, SP, HZ, true>)
-                           : reinterpret_cast<const void*>(&scan_tiled_kernel<T, S, W, TC, SP, HZ, false>);
+    const void* fn =
+        q.zoh_b ? (exact ? reinterpret_cast<const void*>(&scan_tiled_kernel<T, S, W, TC, SP, HZ, true, true>)
+                         : reinterpret_cast<const void*>(&scan_tiled_kernel<T, S, W, TC, SP, HZ, false, true>))
+                : (exact ? reinterpret_cast<const void*>(&scan_tiled_kernel<T, S, W, TC, SP, HZ, true, false>)
+                         : reinterpret_cast<const void*>(&scan_tiled_kernel<T, S, W, TC, SP, HZ, false, false>));
     return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * W), args, 0, stream) == hipSuccess
                ? MAMBA_SCAN_OK
                : MAMBA_SCAN_ERR_LAUNCH;

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libmamba_scan.so")
 F32, BF16 = 0, 1
 DELTA_SOFTPLUS = 1 << 0
 RETURN_LAST_STATE = 1 << 1
+ZOH_B = 1 << 2
 FORCE_GENERIC = 1 << 8
 FORCE_TILED = 1 << 9
 
@@ -128,9 +129,10 @@ def _s3(x, fallback=(0, 0, 1)):
 
 def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
                       return_last_state=False, h0=None, *, kernel=None, out=None,
-                      last_state_out=None):
+                      last_state_out=None, zoh_b=False):
     """y = selective_scan(...), fp32 (batch, dim, L); with ``return_last_state`` also the final
-    state (batch, dim, N) fp32.
+    state (batch, dim, N) fp32. ``zoh_b``: B discretised by zero-order hold,
+    (e^{dt A} - 1) / A * B, instead of dt * B (forward only).
 
     u, delta, z: (batch, dim, L); B, C: (batch, N, L); one storage dtype for all five
     (torch.float32 or torch.bfloat16). A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N);
@@ -169,7 +171,7 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
 
     y = out if out is not None else torch.empty((batch, dim, L), dtype=torch.float32, device=dev)
     ls = None
-    flags = (DELTA_SOFTPLUS if delta_softplus else 0)
+    flags = (DELTA_SOFTPLUS if delta_softplus else 0) | (ZOH_B if zoh_b else 0)
     if return_last_state:
         ls = last_state_out if last_state_out is not None else torch.empty(
             (batch, dim, N), dtype=torch.float32, device=dev)

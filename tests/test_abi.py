@@ -95,6 +95,8 @@ CASES = [
     ("last_state_flag_without_ptr", _flags(scan.RETURN_LAST_STATE), -6),
     ("last_state_ptr_without_flag", _set("ptrs", "last_state", (1 << 40) + (20 << 32)), -6),
     ("unknown_flag", _flags(1 << 5), -6),
+    # the flag check comes before the pointer checks: a known flag reaches the NULL-pointer error
+    ("zoh_flag_is_known", lambda c: (c.__setitem__("flags", scan.ZOH_B), setattr(c["ptrs"], "u", None)), -1),
     ("both_forced", _flags(scan.FORCE_GENERIC | scan.FORCE_TILED), -6),
     ("y_aliases_u", _set("ptrs", "y", (1 << 40) + (1 << 32) + 64), -6),
     ("y_aliases_A", _set("ptrs", "A", (1 << 40) + (10 << 32) + 4), -6),
@@ -160,6 +162,7 @@ BWD_CASES = [
     ("no_workspace", _set("ptrs", "workspace", None), -6),
     ("workspace_too_small", _set("ptrs", "workspace_bytes", 1024), -9),
     ("unknown_flag", lambda c: c.__setitem__("flags", 1 << 9), -6),
+    ("zoh_not_in_backward", lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.ZOH_B), -6),
     ("bad_dtype", lambda c: c.__setitem__("dtype", 7), -4),
     ("zero_len", _set("shape", "len", 0), -2),
     ("dstate_above_max", _set("shape", "dstate", 300), -5),
