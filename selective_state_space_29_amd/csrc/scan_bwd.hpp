@@ -78,7 +78,10 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
 
     __shared__ float s_seg[F_NUM][64 * ROWP];   // per (channel, step) factors of the segment
     __shared__ float s_part[3][W * 64 * SUBP];  // per wave: sum lam B, sum q A, sum C h
-    __shared__ __align__(16) float s_red[W * 2 * S * SUB * 64];  // [w][dB|dC][s][t][lane]
+    // [w][dB|dC][s][t] rows of the 64 lanes' values, padded so that consecutive rows start 4
+    // banks apart: the channel sums below read one row per lane, 16 bytes at a time
+    constexpr int REDP = 64 + 4;
+    __shared__ __align__(16) float s_red[W * 2 * S * SUB * REDP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -128,17 +131,36 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
         for (int i = lane; i < 64 * SUBP; i += 64)
             for (int f = 0; f < 3; ++f) s_part[f][wave * 64 * SUBP + i] = 0.0f;
 
+    // Raw inputs of a segment's prologue, fetched one segment ahead of their use. Step indices
+    // are clamped into the row so every load is unconditional; steps past L are zeroed when used.
+    auto tclamp = [&](int64_t t) __attribute__((always_inline)) { return t < 0 ? 0 : (t < L ? t : L - 1); };
+    struct Raw1 {
+        float x[QS], u[QS];
+    };
+    auto fetch1 = [&](int64_t k, Raw1& r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < QS; ++j) {
+            const int64_t t = tclamp(k * SEG + QS * k8 + j);
+            r.x[j] = load_el<T>(p.delta, prow + t);
+            r.u[j] = load_el<T>(p.u, prow + t);
+        }
+    };
+
     // ---- phase 1: forward, state before each segment to the workspace ----
+    Raw1 nx1;
+    fetch1(0, nx1);
     for (int64_t k = 0; k < p.nseg; ++k) {
         __syncthreads();
+        const Raw1 r1 = nx1;
+        fetch1(k + 1, nx1);
 #pragma unroll
         for (int j = 0; j < QS; ++j) {
             const int64_t t = k * SEG + QS * k8 + j;
             float dt = 0.0f, dtu = 0.0f;
             if (t < L) {
-                const float x = load_el<T>(p.delta, prow + t) + pbias;
+                const float x = r1.x[j] + pbias;
                 dt = SOFTPLUS ? softplus_f(x) : hw_exp2(x * kLog2e);
-                dtu = dt * load_el<T>(p.u, prow + t);
+                dtu = dt * r1.u[j];
             }
             s_seg[F_DT][r * ROWP + QS * k8 + j] = dt;
             s_seg[F_DTU][r * ROWP + QS * k8 + j] = dtu;
@@ -166,17 +188,34 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
     }
 
     // ---- phase 2: segments in reverse ----
+    struct Raw2 {
+        float x[QS], u[QS], gy[QS], z[QS];
+    };
+    auto fetch2 = [&](int64_t k, Raw2& r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < QS; ++j) {
+            const int64_t t = tclamp(k * SEG + QS * k8 + j);
+            r.x[j] = load_el<T>(p.delta, prow + t);
+            r.u[j] = load_el<T>(p.u, prow + t);
+            r.gy[j] = p.dy[prow + t];
+            r.z[j] = HAS_Z ? load_el<T>(p.z, prow + t) : 0.0f;
+        }
+    };
     float gDacc = 0.0f, gbacc = 0.0f;
+    Raw2 nx2;
+    fetch2(p.nseg - 1, nx2);
     for (int64_t k = p.nseg - 1; k >= 0; --k) {
         __syncthreads();
+        const Raw2 r2 = nx2;
+        fetch2(k - 1, nx2);
 #pragma unroll
         for (int j = 0; j < QS; ++j) {
             const int64_t t = k * SEG + QS * k8 + j;
             float dt = 0.0f, dtu = 0.0f, gp = 0.0f, uu = 0.0f, sg = 0.0f, gz = 0.0f;
             if (t < L && pvalid) {
-                const float x = load_el<T>(p.delta, prow + t) + pbias;
-                uu = load_el<T>(p.u, prow + t);
-                const float gy = p.dy[prow + t];
+                const float x = r2.x[j] + pbias;
+                uu = r2.u[j];
+                const float gy = r2.gy[j];
                 if constexpr (SOFTPLUS) {
                     dt = softplus_f(x);
                     sg = hw_rcp(1.0f + hw_exp2(-x * kLog2e));
@@ -185,7 +224,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                 }
                 dtu = dt * uu;
                 if constexpr (HAS_Z) {
-                    const float zz = load_el<T>(p.z, prow + t);
+                    const float zz = r2.z[j];
                     const float sz = hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
                     gp = gy * zz * sz;
                     gz = gy * (sz + zz * sz * (1.0f - sz));
@@ -194,7 +233,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                 }
             } else if (t < L) {
                 // rows past dim: same decay as row 0 would give, no gradient flowing in
-                const float x = load_el<T>(p.delta, prow + t) + pbias;
+                const float x = r2.x[j] + pbias;
                 dt = SOFTPLUS ? softplus_f(x) : hw_exp2(x * kLog2e);
             }
             const int o = r * ROWP + QS * k8 + j;
@@ -269,8 +308,8 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                 for (int s = 0; s < S; ++s)
 #pragma unroll
                     for (int tt = 0; tt < SUB; ++tt) {
-                        s_red[(((wave * 2 + 0) * S + s) * SUB + tt) * 64 + lane] = gBc[s][tt];
-                        s_red[(((wave * 2 + 1) * S + s) * SUB + tt) * 64 + lane] = gCc[s][tt];
+                        s_red[(((wave * 2 + 0) * S + s) * SUB + tt) * REDP + lane] = gBc[s][tt];
+                        s_red[(((wave * 2 + 1) * S + s) * SUB + tt) * REDP + lane] = gCc[s][tt];
                     }
             }
             __syncthreads();
@@ -305,7 +344,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                 const int s = (tid / SUB) % S;
                 const int w = (tid / (SUB * S)) % W;
                 const int q = tid / (SUB * S * W);
-                const float* src = &s_red[(((w * 2 + q) * S + s) * SUB + tt) * 64];
+                const float* src = &s_red[(((w * 2 + q) * S + s) * SUB + tt) * REDP];
                 float acc = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 64; i += 4) {
