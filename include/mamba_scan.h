@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 3
+#define MAMBA_SCAN_ABI_VERSION 4
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -123,7 +123,7 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
                                    uint32_t flags);
 
 /*
- * Backward pass (ABI version 2).
+ * Backward pass (ABI version 2; any dstate from version 4).
  *
  * Gradients of a scalar loss that depends on the forward pass above through y (gradient dy)
  * and, optionally, through last_state (gradient dlast_state). Sources: "手把手用PyTorch实现Mamba的
@@ -148,9 +148,12 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *  - Workspace: exactly mamba_scan_bwd_workspace_bytes() bytes or more, 256-byte aligned, device
  *    memory owned by the caller (states every 16 steps, fp32 copies of B and C, partial sums).
  *  - Flags: MAMBA_SCAN_DELTA_SOFTPLUS only.
- *  - dstate <= 16 (MAMBA_SCAN_ERR_UNSUPPORTED above that).
+ *  - Any dstate up to MAMBA_SCAN_MAX_DSTATE. Above 16 the states are processed in blocks of at
+ *    most 16, one launch each: du, ddelta and dz are accumulated in place across the blocks, in
+ *    block order, so their values can differ in the last bits from a one-block sum.
  *  - Outputs may not overlap each other, any input or the workspace (MAMBA_SCAN_ERR_ARGS).
- *  - Enqueued on `stream`; three kernels (B/C widening, the scan, a fixed-order reduction).
+ *  - Enqueued on `stream`; B/C widening, the scan (one launch per block of states), a
+ *    fixed-order reduction.
  *    Results are bitwise deterministic.
  */
 typedef struct mamba_scan_bwd_ptrs {

@@ -215,8 +215,6 @@ int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     if (p->workspace_bytes < 0 || (p->workspace_bytes > 0 && !p->workspace)) return MAMBA_SCAN_ERR_ARGS;
     if (!p->workspace || p->workspace_bytes < need) return MAMBA_SCAN_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(p->workspace) % 256 != 0) return MAMBA_SCAN_ERR_ARGS;
-    const int S = bwd_states_per_wave(s->dstate);
-    if (S == 0 || s->dstate % S != 0) return MAMBA_SCAN_ERR_UNSUPPORTED;
     if (s->batch * ((s->dim + 63) / 64) > 0x7fffffff) return MAMBA_SCAN_ERR_UNSUPPORTED;
 
     const int64_t es = dtype == MAMBA_SCAN_BF16 ? 2 : 4;

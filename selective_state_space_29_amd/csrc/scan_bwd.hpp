@@ -12,7 +12,10 @@
 //   dz = dy p silu'(z);  dD += gp u;  dbias += ddelta;  then lam_{t-1} = a lam_t;  dh0 = lam.
 //
 // Decomposition (as the forward kernel): a workgroup owns 64 channels of one batch, one channel
-// per lane; wave w carries states w*S .. w*S+S-1 (S <= 2, so N <= 16).
+// per lane; wave w carries states w*S .. w*S+S-1 of the launch's block of at most 16 states
+// (S <= 2). Larger N runs one launch per block of 16 states: per-state results (dB, dC, dA, dh0)
+// belong to one block, and the per-(channel, step) sums over states (du, ddelta and, for the
+// gate, sum_n C h) are added across the blocks in block order.
 //   Phase 1: forward over 16-step segments, writing the state before each segment to the
 //            workspace (the only stored states: N floats per channel per 16 steps).
 //   Phase 2: segments in reverse. The workgroup computes the per-(channel, step) factors into
@@ -48,12 +51,14 @@ struct BwdParams {
     float* ddelta;
     float* dz;
     float* dh0;
-    float* ck;      // (batch, dim, nseg, N) states before each segment
+    float* ck;      // (batch, dim, nseg, ckn) this block's states before each segment
     float* bcpart;  // (groups, batch, 2, N, lp) dB / dC partials of each 64-channel group
     float* apart;   // (batch, dim, N)
     float* dpart;   // (batch, dim)
     float* bpart;   // (batch, dim)
     int64_t batch, dim, len, dstate, lp, nseg, groups;
+    int64_t n0, nb, ckn;  // this launch's states n0 .. n0 + nb - 1; ck's state stride
+    int first, last;      // first / last block of states: initialises / finishes the sums
 };
 
 constexpr int kBwdW = 8;     // waves per workgroup
@@ -67,7 +72,9 @@ __device__ __forceinline__ float load_el(const void* p, int64_t i) {
     return to_f32(static_cast<const T*>(p)[i]);
 }
 
-template <typename T, int S, bool SOFTPLUS, bool HAS_Z, bool EXACT>
+// MULTI: one of several blocks of states (first / last read from the parameters); otherwise the
+// only block, with the sums over states finished in this launch.
+template <typename T, int S, bool SOFTPLUS, bool HAS_Z, bool EXACT, bool MULTI>
 __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
     constexpr int W = kBwdW, SEG = kBwdSeg, SUB = kBwdSub;
     constexpr int QS = SEG / W;      // prologue steps per thread
@@ -90,8 +97,10 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
     const int64_t grp = blockIdx.x - b * p.groups;
     const int64_t d0 = grp * 64;
     const int64_t L = p.len, N = p.dstate;
-    const int nbase = wave * S;
-    const bool wave_live = EXACT || nbase < (int)N;
+    const int nloc = wave * S;  // within the block
+    const bool wave_live = EXACT || nloc < (int)p.nb;
+    const int64_t nbase = p.n0 + (wave_live ? nloc : 0);
+    const bool first = !MULTI || p.first, last = !MULTI || p.last;
 
     // prologue / epilogue role: row r = tid / 8; prologue steps 2k, 2k+1 of a segment,
     // epilogue step k of a half-segment (k = tid % 8)
@@ -121,10 +130,10 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
         }
         a2[s] = Av[s] * kLog2e;
     }
-    const int gclamp = wave_live ? nbase : 0;
-    const float* Brow = p.bc + (b * N + gclamp) * p.lp;              // state nbase + s at + s*lp
-    const float* Crow = p.bc + ((p.batch + b) * N + gclamp) * p.lp;
-    float* ckrow = p.ck + (b * p.dim + (mvalid ? dm : 0)) * p.nseg * N + nbase;
+    const float* Brow = p.bc + (b * N + nbase) * p.lp;              // state nbase + s at + s*lp
+    const float* Crow = p.bc + ((p.batch + b) * N + nbase) * p.lp;
+    const int64_t ckn = p.ckn;
+    float* ckrow = p.ck + (b * p.dim + (mvalid ? dm : 0)) * p.nseg * ckn + (wave_live ? nloc : 0);
 
     // zero partials for waves that hold no states (read by the epilogue, never written after)
     if (!wave_live)
@@ -169,7 +178,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
         if (wave_live) {
             if (mvalid)
 #pragma unroll
-                for (int s = 0; s < S; ++s) ckrow[k * N + s] = h[s];
+                for (int s = 0; s < S; ++s) ckrow[k * ckn + s] = h[s];
             float bv[S][SEG];
 #pragma unroll
             for (int s = 0; s < S; ++s) {
@@ -251,7 +260,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
         if (wave_live) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                hs[s] = mvalid ? ckrow[k * N + s] : 0.0f;
+                hs[s] = mvalid ? ckrow[k * ckn + s] : 0.0f;
                 const bwd_cptrf pb = (bwd_cptrf)(Brow + s * p.lp + k * SEG);
                 const bwd_cptrf pc = (bwd_cptrf)(Crow + s * p.lp + k * SEG);
 #pragma unroll
@@ -329,13 +338,22 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                 const float dt = s_seg[F_DT][o], gp = s_seg[F_GP][o], uu = s_seg[F_U][o];
                 const float gdt = __builtin_fmaf(uu, P1, P2);
                 const float gx = SOFTPLUS ? gdt * s_seg[F_SG][o] : gdt * dt;
-                const float gu = __builtin_fmaf(gp, pskip, dt * P1);
                 if (pvalid && t < L) {
+                    // this block's share; earlier blocks' shares are already in the outputs
+                    float gu = dt * P1, gxs = gx, ys = Y;
+                    if (first) {
+                        gu = __builtin_fmaf(gp, pskip, gu);
+                        gDacc = __builtin_fmaf(gp, uu, gDacc);
+                    } else {
+                        gu += p.du[prow + t];
+                        gxs += p.ddelta[prow + t];
+                        if constexpr (HAS_Z) ys += p.dz[prow + t];
+                    }
                     p.du[prow + t] = gu;
-                    p.ddelta[prow + t] = gx;
-                    if constexpr (HAS_Z) p.dz[prow + t] = s_seg[F_GZ][o] * __builtin_fmaf(pskip, uu, Y);
-                    gDacc = __builtin_fmaf(gp, uu, gDacc);
-                    gbacc += gx;
+                    p.ddelta[prow + t] = gxs;
+                    if constexpr (HAS_Z)  // sum_n C h until the last block, then the gate's gradient
+                        p.dz[prow + t] = last ? s_seg[F_GZ][o] * __builtin_fmaf(pskip, uu, ys) : ys;
+                    if (last) gbacc += gxs;  // dbias sums the finished ddelta
                 }
             }
             // dB / dC of this half: one sum over the 64 channels per (dB|dC, state, step)
@@ -355,8 +373,8 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                     acc += v.w;
                 }
                 const int n = w * S + s;
-                if (n < N)
-                    p.bcpart[(((grp * p.batch + b) * 2 + q) * N + n) * p.lp + k * SEG + half * SUB + tt] = acc;
+                if (n < p.nb)
+                    p.bcpart[(((grp * p.batch + b) * 2 + q) * N + p.n0 + n) * p.lp + k * SEG + half * SUB + tt] = acc;
             }
             __syncthreads();
         }
@@ -378,8 +396,8 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
         gbacc += __shfl_xor(gbacc, off, 64);
     }
     if (k8 == 0 && pvalid) {
-        p.dpart[b * p.dim + pd] = gDacc;
-        p.bpart[b * p.dim + pd] = gbacc;
+        if (first) p.dpart[b * p.dim + pd] = gDacc;
+        if (last) p.bpart[b * p.dim + pd] = gbacc;
     }
 }
 
@@ -449,6 +467,11 @@ struct BwdLayout {
 
 inline int64_t bwd_align(int64_t x) { return (x + 255) / 256 * 256; }
 
+// States per launch: blocks of 16; a remainder in (8, 16] that is odd (two states per wave would
+// leave one wave half used) is split into 8 and the rest.
+inline int64_t bwd_next_block(int64_t rem) { return rem > 16 ? 16 : (rem > 8 && rem % 2) ? 8 : rem; }
+inline int64_t bwd_block_states(int64_t N) { return bwd_next_block(N); }
+
 inline BwdLayout bwd_layout(const mamba_scan_shape& s) {
     BwdLayout l;
     l.lp = (s.len + kBwdSeg - 1) / kBwdSeg * kBwdSeg;
@@ -458,7 +481,7 @@ inline BwdLayout bwd_layout(const mamba_scan_shape& s) {
     l.off_bc = o;
     o = bwd_align(o + 2 * s.batch * s.dstate * l.lp * 4);
     l.off_ck = o;
-    o = bwd_align(o + s.batch * s.dim * l.nseg * s.dstate * 4);
+    o = bwd_align(o + s.batch * s.dim * l.nseg * bwd_block_states(s.dstate) * 4);
     l.off_bcpart = o;
     o = bwd_align(o + l.groups * s.batch * 2 * s.dstate * l.lp * 4);
     l.off_apart = o;
@@ -471,14 +494,18 @@ inline BwdLayout bwd_layout(const mamba_scan_shape& s) {
     return l;
 }
 
-inline int bwd_states_per_wave(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : 0; }
+inline int bwd_states_per_wave(int64_t nb) { return nb <= 8 ? 1 : 2; }
 
 template <typename T, int S, bool SP, bool HZ>
 int launch_bwd_cfg(const BwdParams& q, hipStream_t stream) {
     void* args[] = {const_cast<BwdParams*>(&q)};
-    const bool exact = q.dstate == (int64_t)S * kBwdW;
-    const void* fn = exact ? reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, true>)
-                           : reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, false>);
+    const bool exact = q.nb == (int64_t)S * kBwdW;
+    const bool multi = !(q.first && q.last);
+    const void* fn =
+        multi ? (exact ? reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, true, true>)
+                       : reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, false, true>))
+              : (exact ? reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, true, false>)
+                       : reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, false, false>));
     return hipLaunchKernel(fn, dim3((unsigned)(q.batch * q.groups)), dim3(64 * kBwdW), args, 0, stream) ==
                    hipSuccess
                ? MAMBA_SCAN_OK
@@ -537,13 +564,16 @@ int launch_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool sof
                             dim3((unsigned)((nwide + 255) / 256)), dim3(256), args, 0, stream) != hipSuccess)
             return MAMBA_SCAN_ERR_LAUNCH;
     }
-    int rc;
-    switch (bwd_states_per_wave(s.dstate)) {
-        case 1: rc = launch_bwd_s<T, 1>(q, softplus, stream); break;
-        case 2: rc = launch_bwd_s<T, 2>(q, softplus, stream); break;
-        default: return MAMBA_SCAN_ERR_UNSUPPORTED;
+    q.ckn = bwd_block_states(s.dstate);
+    for (int64_t n0 = 0; n0 < s.dstate; n0 += q.nb) {
+        q.n0 = n0;
+        q.nb = bwd_next_block(s.dstate - n0);
+        q.first = n0 == 0;
+        q.last = n0 + q.nb == s.dstate;
+        const int rc = bwd_states_per_wave(q.nb) == 1 ? launch_bwd_s<T, 1>(q, softplus, stream)
+                                                       : launch_bwd_s<T, 2>(q, softplus, stream);
+        if (rc != MAMBA_SCAN_OK) return rc;
     }
-    if (rc != MAMBA_SCAN_OK) return rc;
     BwdReduceParams r;
     r.bcpart = q.bcpart;
     r.apart = q.apart;

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 3
+    assert scan.load_library().mamba_scan_abi_version() == 4
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -177,9 +177,16 @@ def test_backward_invalid_arguments_are_rejected(name, mutate, code):
     assert fake_bwd(mutate) == code
 
 
-def test_backward_unsupported_dstate():
-    assert fake_bwd(shape=(2, 3, 40, 32)) == -8   # more than 2 states per wave
-    assert fake_bwd(shape=(2, 3, 40, 11)) == -8   # N in (8, 16] must be even
+def test_backward_workspace_for_wide_states():
+    """Above 16 states the workspace holds the segment states of one block of 16 only, but B, C
+    and their per-group partials for all of them."""
+    lib = scan.load_library()
+    for N, ckn in ((64, 16), (24, 16), (11, 8), (256, 16)):
+        shp = scan.Shape(2, 200, 100, N)
+        n = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(shp), scan.F32, 0)
+        lp, groups = 112, 4
+        need = 2 * 2 * N * lp * 4 + 2 * 200 * (lp // 16) * ckn * 4 + groups * 2 * 2 * N * lp * 4
+        assert need <= n < need + 2 * 200 * N * 4 + 4 * 2 * 200 * 4 + 6 * 256, (N, n, need)
 
 
 def test_backward_workspace_query():

@@ -58,7 +58,7 @@ def _check(x, softplus=True, with_h0=False, with_dlast=True, seed=0, tol=TOL):
     return gg
 
 
-@pytest.mark.parametrize("wid", [2, 3])
+@pytest.mark.parametrize("wid", [1, 2, 3])
 def test_workload_backward_parity(wid):
     w = workloads.WORKLOADS[wid]
     x = workloads.make_inputs(w)
@@ -78,6 +78,15 @@ EDGE = [
     (1, 128, 10, 48, "bf16", {"h0": True, "dlast": False}),
     (2, 96, 16, 7, "f32", {"a_kind": "rand"}),
     (1, 192, 16, 257, "bf16", {"h0": True}),
+    # more than 16 states: one launch per block of states, sums carried across the blocks
+    (2, 70, 24, 40, "f32", {"h0": True}),            # blocks 16 + 8
+    (1, 64, 32, 33, "bf16", {}),                     # 16 + 16
+    (2, 100, 40, 50, "f32", {"softplus": False}),    # 16 + 16 + 8
+    (1, 130, 64, 70, "bf16", {"h0": True}),          # 4 x 16
+    (2, 64, 11, 20, "f32", {}),                      # odd in (8, 16]: 8 + 3
+    (1, 65, 27, 17, "f32", {"z": False}),            # 16 + 8 + 3
+    (1, 66, 46, 24, "bf16", {"D": False, "bias": False, "dlast": False}),  # 16 + 16 + 14
+    (1, 40, 256, 19, "f32", {}),                     # the largest dstate
 ]
 
 
@@ -89,6 +98,81 @@ def test_backward_edge_cases(idx):
                 bias=fl.get("bias", True), a_kind=fl.get("a_kind", "mamba"))
     _check(x, softplus=fl.get("softplus", True), with_h0=fl.get("h0", False),
            with_dlast=fl.get("dlast", True), seed=idx)
+
+
+def test_state_blocks_are_independent():
+    """dB, dC, dA and dh0 of a state depend on no other state, so with 32 states the first 16
+    states' gradients are the bits of a 16-state run on those states alone (the same block)."""
+    x = gu.case(73, 2, 96, 32, 90, dtype="bf16")
+    rng = np.random.default_rng(4)
+    dy = rng.standard_normal((2, 96, 90)).astype(np.float32)
+    dlast = rng.standard_normal((2, 96, 32)).astype(np.float32)
+    h0 = rng.standard_normal((2, 96, 32)).astype(np.float32)
+    full = _grads_gpu(x, dy, dlast, True, h0)
+    half = dict(x, A=np.ascontiguousarray(x["A"][:, :16]), B=np.ascontiguousarray(x["B"][:, :16]),
+                C=np.ascontiguousarray(x["C"][:, :16]))
+    part = _grads_gpu(half, dy, np.ascontiguousarray(dlast[..., :16]), True, np.ascontiguousarray(h0[..., :16]))
+    for k in ("B", "C"):
+        assert np.array_equal(full[k][:, :16], part[k]), k
+    assert np.array_equal(full["A"][:, :16], part["A"])
+    assert np.array_equal(full["h0"][..., :16], part["h0"])
+
+
+def test_wide_state_workload_sampled():
+    """Full-size backward of the 64-state workload (one launch per block of 16 states); the oracle
+    checks every channel-local gradient of sampled channels: du, ddelta, dz and dh0 of each
+    (batch, channel) row, and dA, dD, dbias of the channel (summed over the batch). dB and dC
+    sum over all channels and are checked at the smaller sizes above."""
+    w = workloads.WORKLOADS[5]
+    print(f"backward parity, workload 5: {w.name} (sampled channels)", flush=True)
+    x = workloads.make_inputs(w)
+    g = {k: gu.to_dev(v) if isinstance(v, np.ndarray) else v for k, v in x.items()}
+    del x
+    gen = torch.Generator(device="cuda:0").manual_seed(29505)
+    dy = torch.randn((w.batch, w.dim, w.seqlen), device="cuda:0", generator=gen)
+    dlast = torch.randn((w.batch, w.dim, w.dstate), device="cuda:0", generator=gen)
+    out = scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"], z=g["z"],
+                                  delta_bias=g["delta_bias"], delta_softplus=True, dlast_state=dlast,
+                                  want_dh0=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    chans = sorted({0, 1, 63, 64, w.dim - 1} | {int(c) for c in rng.integers(0, w.dim, 5)})
+    rows = [b * w.dim + d for b in range(w.batch) for d in chans]
+    idx = torch.tensor(rows, device="cuda:0")
+    got = {k: out[k].reshape(w.batch * w.dim, -1).index_select(0, idx).cpu().numpy()
+           for k in ("u", "delta", "z", "h0")}
+    cidx = torch.tensor(chans, device="cuda:0")
+    got_c = {k: out[k].index_select(0, cidx).cpu().numpy() for k in ("A", "D", "delta_bias")}
+    dy_r = dy.reshape(w.batch * w.dim, -1).index_select(0, idx).cpu().numpy()
+    dl_r = dlast.reshape(w.batch * w.dim, -1).index_select(0, idx).cpu().numpy()
+    assert all(bool(torch.isfinite(v).all()) for v in out.values())
+    del out, g, dy, dlast
+    xr = workloads.make_row_inputs(w, rows)
+
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(i):
+        s = slice(i, i + 1)
+        return oracle.selective_scan_bwd(
+            xr["u"][s], xr["delta"][s], xr["A"][s], xr["B"][s], xr["C"][s],
+            dy_r[s].reshape(1, 1, -1).astype(np.float64), D=xr["D"][s], z=xr["z"][s],
+            delta_bias=xr["delta_bias"][s], delta_softplus=True,
+            glast=dl_r[s].reshape(1, 1, -1).astype(np.float64), nthreads=1)
+
+    with ThreadPoolExecutor(max_workers=min(16, oracle.default_threads())) as ex:
+        res = list(ex.map(one, range(len(rows))))
+    ref = {k: np.stack([r[k].reshape(-1) for r in res]) for k in ("u", "delta", "z", "h0")}
+    nc = len(chans)
+    ref_c = {k: sum(np.stack([res[b * nc + j][k].reshape(-1) for j in range(nc)]) for b in range(w.batch))
+             for k in ("A", "D", "delta_bias")}
+    for k in ref:
+        err = gu.rel_err(got[k], ref[k])
+        print(f"  d{k}: {err:.3e} over {len(rows)} rows", flush=True)
+        assert err <= TOL, k
+    for k in ref_c:
+        err = gu.rel_err(got_c[k].reshape(nc, -1), ref_c[k].reshape(nc, -1))
+        print(f"  d{k}: {err:.3e} over {nc} channels", flush=True)
+        assert err <= TOL, k
 
 
 def test_backward_is_deterministic():
