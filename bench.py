@@ -33,7 +33,12 @@ SLOTS_PER_ROW_STEP = 30    # softplus, dt*u, bias, skip, silu gate
 # zero-order-hold B adds, per element: dt*A, the 4-term series and dt*p, dA - 1 and * 1/A, the
 # compare and select, and * u
 SLOTS_PER_ELEMENT_ZOH = SLOTS_PER_ELEMENT + 11
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "scan_tiled_mamba130m_traffic.json")
+# rocprofv3 FETCH_SIZE / WRITE_SIZE records of the forward kernels at the Mamba-130m shape, each
+# with a hash of the sources it was measured on
+TRAFFIC_RECORDS = {
+    "lanes": (os.path.join(ROOT, "profiles", "scan_ls_mamba130m_traffic.json"), ("common.hpp", "scan_ls.hpp")),
+    "tiled": (os.path.join(ROOT, "profiles", "scan_tiled_mamba130m_traffic.json"), ("common.hpp", "scan_tiled.hpp")),
+}
 RATES_LIB = os.path.join(ROOT, "selective_state_space_29_amd", "probe", "libmscan_rates.so")
 
 
@@ -43,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--kernel", choices=["auto", "generic", "tiled"], default="auto")
+    ap.add_argument("--kernel", choices=["auto", "generic", "tiled", "lanes"], default="auto")
     ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
@@ -90,30 +95,67 @@ def copy_calibration(mb, steps, warmup):
 
 # The sources of the kernel whose HBM traffic the counter record measured (the forward tiled
 # kernel): the record only applies while these are unchanged.
-TRAFFIC_KERNEL_SOURCES = ("common.hpp", "scan_tiled.hpp")
+def resolved_kernel(w, kernel, zoh=False):
+    """The forward kernel the library runs for this workload: its default picks the
+    lane-per-state kernel for 16 states (Euler B), else the tiled one."""
+    if kernel != "auto":
+        return kernel
+    return "lanes" if w.dstate == 16 and not zoh else "tiled"
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel):
     import hashlib
 
     h = hashlib.sha256()
-    for f in TRAFFIC_KERNEL_SOURCES:
+    for f in TRAFFIC_RECORDS[kernel][1]:
         with open(os.path.join(ROOT, "selective_state_space_29_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(w, kernel):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record, or None
-    when that record was taken on other kernel sources or another workload."""
+def measured_traffic(w, kernel, zoh=False):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record of the
+    kernel that runs, or None when there is none for it, it was taken on other kernel sources,
+    or on another workload."""
+    k = resolved_kernel(w, kernel, zoh)
+    if w.wid != 3 or zoh or k not in TRAFFIC_RECORDS:
+        return None
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(TRAFFIC_RECORDS[k][0]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if w.wid != 3 or kernel not in ("auto", "tiled") or rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("source_sha256") != kernel_source_hash(k):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def graph_timed(fn, steps, warmup, stream, reps=5, warm_reps=1):
+    """Per-call GPU time of fn(0..steps-1): the calls captured once in a HIP graph (the library
+    allocates nothing and launches on the current stream), the graph replayed `warm_reps` times
+    untimed and then `reps` times, each replay timed with HIP events on the launch stream. The
+    host-side marshalling of one eager call takes about as long as a short kernel, so eager
+    timing would measure the host."""
+    import numpy as np
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            fn(i)
+    for _ in range(warm_reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record(stream)
+        graph.replay()
+        ev[r][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 / steps for a, b in ev])
 
 
 def measured_rates():
@@ -467,34 +509,11 @@ def upstream_bench(args):
         xi, outs = sets[i % len(sets)]
         return scan.block_upstream(xi, cw, cb, wx, wdt, w.dstate, w.dt_rank, out=outs)
 
-    # The host-side marshalling of one call takes about as long as the kernel, so eager timing
-    # would measure the host. The timed calls are captured once in a HIP graph (the library
-    # allocates nothing and launches on the current stream) and the graph is replayed: mean
-    # launch time = replay time / calls, timed with HIP events on the launch stream.
-    def graph_timed(fn, steps, warmup):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(steps):
-                fn(i)
-        graph.replay()  # warm
-        torch.cuda.synchronize()
-        reps = 5
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for r in range(reps):
-            ev[r][0].record(stream)
-            graph.replay()
-            ev[r][1].record(stream)
-        torch.cuda.synchronize()
-        return np.array([a.elapsed_time(b) * 1e3 / steps for a, b in ev])
-
     eager = [None] * len(sets)
     for i in range(len(sets)):
         eager[i] = [t.clone() for t in up(i)]
     torch.cuda.synchronize()
-    per_us = graph_timed(up, args.steps, args.warmup)
+    per_us = graph_timed(up, args.steps, args.warmup, stream)
     replay_equal = all(torch.equal(a, b) for i in range(len(sets)) for a, b in zip(sets[i][1], eager[i]))
     mean_us = float(np.median(per_us))
     span_us = mean_us
@@ -513,7 +532,7 @@ def upstream_bench(args):
         _, B, C = scan.split_xdbl(xdbl, w.dt_rank, w.dstate)
         scan.selective_scan_fn(u, delta, A, B, C, D=Dv, z=z, delta_bias=dt_bias, delta_softplus=True, out=y)
 
-    blk_us = graph_timed(block, args.steps, args.warmup)
+    blk_us = graph_timed(block, args.steps, args.warmup, stream)
     log(f"upstream + scan: graph replay {blk_us.round(2).tolist()} us per call")
 
     # parity of the last upstream outputs against the fp64 oracle, every element
@@ -638,27 +657,37 @@ def main():
                                return_last_state=w.last_state, kernel=kernel, out=s["y"],
                                last_state_out=s["ls"], zoh_b=args.zoh)
 
+    stream = torch.cuda.current_stream(dev)
+    # eager calls, each bracketed by events: when the host-side marshalling of a call takes
+    # longer than its kernel, these measure the host (reported for reference only)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
-    span_ms = ev[0][0].elapsed_time(ev[-1][1])
-    mean_launch_ms = float(np.mean(per_launch_ms))
-    log(f"{args.steps} steps: span {span_ms:.3f} ms, wall {wall * 1e3:.3f} ms, launch mean "
-        f"{mean_launch_ms * 1e3:.1f} us min {min(per_launch_ms) * 1e3:.1f} us")
+    eager_span_ms = ev[0][0].elapsed_time(ev[-1][1])
+    eager = [(s["y"].clone(), s["ls"].clone()) for s in sets]
 
-    ms_per_step = span_ms / args.steps
+    # timed: the K steps captured once in a HIP graph, the graph replayed 3 times untimed (the
+    # clocks settle under sustained load) and then 7 times, each replay (exactly K steps, the
+    # buffer sets rotating) timed with HIP events on the launch stream and bracketed by device
+    # synchronisation; value and ms_per_step from the median replay
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    per_call_us = graph_timed(step, args.steps, 0, stream, reps=7, warm_reps=3)
+    wall = time.perf_counter() - t_start
+    replay_equal = all(torch.equal(s["y"], e[0]) and torch.equal(s["ls"], e[1]) for s, e in zip(sets, eager))
+    mean_launch_ms = float(np.median(per_call_us)) / 1e3
+    log(f"{args.steps} steps per replay: {np.round(per_call_us, 2).tolist()} us per call "
+        f"(replays equal eager: {replay_equal}); eager span {eager_span_ms * 1e3 / args.steps:.1f} us "
+        f"per call; wall {wall * 1e3:.1f} ms for capture + 10 replays")
+
+    ms_per_step = mean_launch_ms
     value = w.elements / (ms_per_step * 1e-3) / 1e9
     alg_bytes = w.algorithmic_bytes()
     achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
@@ -723,18 +752,23 @@ def main():
         "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seq_len": w.seqlen, "storage": w.dtype, "z_gate": w.has_z,
-                   "last_state": w.last_state, "kernel": args.kernel, "buffer_sets": len(sets),
+                   "last_state": w.last_state, "kernel": resolved_kernel(w, args.kernel, args.zoh),
+                   "buffer_sets": len(sets),
                    "zoh_b": args.zoh},
         "roofline": {"bound": "alu", "achieved": round(achieved_tflops, 2),
                      "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / VALU_PEAK_TFLOPS, 4),
-                     "traffic": None if args.zoh else measured_traffic(w, args.kernel),
+                     "traffic": measured_traffic(w, args.kernel, args.zoh),
                      "valu_slots_per_launch": slots, "algorithmic_bytes": alg_bytes,
                      "hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)},
                      "transcendental": trans,
                      "measured_rates": rates,
-                     "mean_launch_us": round(mean_launch_ms * 1e3, 2)},
+                     "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+                     "timing": f"median of 7 HIP-graph replays (after 3 untimed) of {args.steps} captured calls, per call",
+                     "graph_replay_us_per_call": [round(float(v), 2) for v in per_call_us],
+                     "graph_replays_equal_eager": replay_equal,
+                     "eager_us_per_call": round(eager_span_ms * 1e3 / args.steps, 2)},
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
         "parity_sample": check,

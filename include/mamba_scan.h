@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 4
+#define MAMBA_SCAN_ABI_VERSION 5
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -61,10 +61,14 @@ typedef enum mamba_scan_dtype {
  * (dt * B * u where A[d,n] = 0) instead of dt * B * u. "手把手用PyTorch实现Mamba的SSM层…" §2.1:
  * B_d = A^-1 (e^{A dt} - I) B, for a diagonal A. Forward only (mamba_scan_bwd rejects it). */
 #define MAMBA_SCAN_ZOH_B (1u << 2)
-/* Kernel selection, for testing and tuning. Default (neither bit): the library picks. */
+/* Kernel selection, for testing and tuning; at most one of these bits (MAMBA_SCAN_ERR_ARGS
+ * otherwise). Default (none): the lane-per-state kernel where it can run, else the tiled one,
+ * else the generic one. */
 #define MAMBA_SCAN_FORCE_GENERIC (1u << 8) /* one lane per row, any shape and alignment */
 #define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
-#define MAMBA_SCAN_KNOWN_FLAGS 0x307u
+#define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one lane per (channel, state), dstate 16 only, no
+                                              ZOH_B; error if it cannot run (ABI version 5) */
+#define MAMBA_SCAN_KNOWN_FLAGS 0x707u
 
 /* error codes */
 #define MAMBA_SCAN_OK 0

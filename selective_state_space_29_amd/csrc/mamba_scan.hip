@@ -10,6 +10,7 @@
 #include "common.hpp"
 #include "scan_bwd.hpp"
 #include "scan_generic.hpp"
+#include "scan_ls.hpp"
 #include "scan_tiled.hpp"
 
 using namespace mscan;
@@ -61,7 +62,8 @@ int validate(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_sc
     if (!p || !s || !st) return MAMBA_SCAN_ERR_NULL;
     if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
     if (flags & ~MAMBA_SCAN_KNOWN_FLAGS) return MAMBA_SCAN_ERR_ARGS;
-    if ((flags & MAMBA_SCAN_FORCE_GENERIC) && (flags & MAMBA_SCAN_FORCE_TILED)) return MAMBA_SCAN_ERR_ARGS;
+    const uint32_t forced = flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_LANES);
+    if (forced & (forced - 1)) return MAMBA_SCAN_ERR_ARGS;  // at most one kernel may be forced
     if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
     if (!p->u || !p->delta || !p->B || !p->C || !p->A || !p->y) return MAMBA_SCAN_ERR_NULL;
@@ -315,6 +317,11 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const ma
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool bf16 = dtype == MAMBA_SCAN_BF16;
 
+    // default order: lane-per-state (16 states), then the tiled kernel, then the generic one
+    if (!(flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED))) {
+        const int lrc = bf16 ? launch_ls<bf16_t>(q, hs) : launch_ls<float>(q, hs);
+        if (lrc != MAMBA_SCAN_ERR_UNSUPPORTED || (flags & MAMBA_SCAN_FORCE_LANES)) return lrc;
+    }
     if (!(flags & MAMBA_SCAN_FORCE_GENERIC)) {
         const int trc = bf16 ? launch_tiled<bf16_t>(q, p, flags, hs) : launch_tiled<float>(q, p, flags, hs);
         if (trc != MAMBA_SCAN_ERR_UNSUPPORTED) return trc;

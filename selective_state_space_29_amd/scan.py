@@ -27,6 +27,7 @@ RETURN_LAST_STATE = 1 << 1
 ZOH_B = 1 << 2
 FORCE_GENERIC = 1 << 8
 FORCE_TILED = 1 << 9
+FORCE_LANES = 1 << 10
 
 _I64 = ctypes.c_int64
 _P = ctypes.c_void_p
@@ -136,7 +137,8 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
 
     u, delta, z: (batch, dim, L); B, C: (batch, N, L); one storage dtype for all five
     (torch.float32 or torch.bfloat16). A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N);
-    these are taken in fp32. ``kernel``: None (library picks), "generic" or "tiled".
+    these are taken in fp32. ``kernel``: None (library picks), "generic", "tiled" or "lanes"
+    (one lane per (channel, state); 16 states only).
     """
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):
@@ -180,8 +182,10 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
         flags |= FORCE_GENERIC
     elif kernel == "tiled":
         flags |= FORCE_TILED
+    elif kernel == "lanes":
+        flags |= FORCE_LANES
     elif kernel is not None:
-        raise ValueError("kernel must be None, 'generic' or 'tiled'")
+        raise ValueError("kernel must be None, 'generic', 'tiled' or 'lanes'")
 
     shape = Shape(batch, dim, L, N)
     dtype = BF16 if u.dtype == torch.bfloat16 else F32

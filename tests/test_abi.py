@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 4
+    assert scan.load_library().mamba_scan_abi_version() == 5
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -98,6 +98,13 @@ CASES = [
     # the flag check comes before the pointer checks: a known flag reaches the NULL-pointer error
     ("zoh_flag_is_known", lambda c: (c.__setitem__("flags", scan.ZOH_B), setattr(c["ptrs"], "u", None)), -1),
     ("both_forced", _flags(scan.FORCE_GENERIC | scan.FORCE_TILED), -6),
+    ("lanes_and_tiled_forced", _flags(scan.FORCE_LANES | scan.FORCE_TILED), -6),
+    # the lane-per-state kernel takes 16 states, the Euler input term, 31-bit row offsets
+    ("lanes_forced_32_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
+                                          setattr(c["shape"], "dstate", 32)), -8),
+    ("lanes_forced_zoh", _flags(scan.DELTA_SOFTPLUS | scan.FORCE_LANES | scan.ZOH_B), -8),
+    ("lanes_forced_wide_rows", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
+                                          setattr(c["st"], "u", (ctypes.c_int64 * 3)(1 << 31, 1 << 29, 1))), -8),
     ("y_aliases_u", _set("ptrs", "y", (1 << 40) + (1 << 32) + 64), -6),
     ("y_aliases_A", _set("ptrs", "A", (1 << 40) + (10 << 32) + 4), -6),
     ("workspace_size_without_ptr", _set("ptrs", "workspace_bytes", 128), -6),

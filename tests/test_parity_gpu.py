@@ -18,7 +18,7 @@ from selective_state_space_29_amd import scan, workloads
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = [None, "generic", "tiled"]
+KERNELS = [None, "generic", "tiled", "lanes"]
 
 
 def _log(msg):
@@ -30,8 +30,8 @@ def run_or_skip(x, kernel, **kw):
     try:
         return gu.gpu_scan(x, kernel=kernel, **kw)
     except ValueError as e:
-        if kernel == "tiled" and "(-8)" in str(e):
-            pytest.skip("tiled kernel does not take this case")
+        if kernel in ("tiled", "lanes") and "(-8)" in str(e):
+            pytest.skip(f"{kernel} kernel does not take this case")
         raise
 
 
@@ -42,7 +42,7 @@ def tol_for(dtype):
 def test_library_is_the_in_tree_build():
     lib = scan.load_library()
     assert os.path.dirname(scan.LIB_PATH).endswith("selective_state_space_29_amd")
-    assert lib.mamba_scan_abi_version() == 4
+    assert lib.mamba_scan_abi_version() == 5
     maps = open("/proc/self/maps").read()
     assert scan.LIB_PATH in maps
 
@@ -99,8 +99,8 @@ def test_workload_sampled_parity(wid, kernel, big_inputs):
                                        z=g["z"], delta_bias=g["delta_bias"], delta_softplus=True,
                                        return_last_state=True, kernel=kernel)
     except ValueError as e:
-        if kernel == "tiled" and "(-8)" in str(e):
-            pytest.skip("tiled kernel does not take this case")
+        if kernel in ("tiled", "lanes") and "(-8)" in str(e):
+            pytest.skip(f"{kernel} kernel does not take this case")
         raise
     torch.cuda.synchronize()
     rows = sample_rows(w)
@@ -181,8 +181,8 @@ def test_strided_views(kernel):
                                        delta_softplus=True, return_last_state=True, kernel=kernel,
                                        out=yo)
     except ValueError as e:
-        if kernel == "tiled" and "(-8)" in str(e):
-            pytest.skip("tiled kernel does not take this case")
+        if kernel in ("tiled", "lanes") and "(-8)" in str(e):
+            pytest.skip(f"{kernel} kernel does not take this case")
         raise
     torch.cuda.synchronize()
     yr, lr = gu.oracle_scan({k: (np.ascontiguousarray(v) if v is not None else None)
@@ -255,8 +255,8 @@ def test_deterministic_and_inside_its_outputs(kernel):
                                    return_last_state=True, kernel=kernel, out=yv,
                                    last_state_out=lv)
         except ValueError as e:
-            if kernel == "tiled" and "(-8)" in str(e):
-                pytest.skip("tiled kernel does not take this case")
+            if kernel in ("tiled", "lanes") and "(-8)" in str(e):
+                pytest.skip(f"{kernel} kernel does not take this case")
             raise
         torch.cuda.synchronize()
         outs.append((yv.clone(), lv.clone()))
