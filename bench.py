@@ -338,6 +338,25 @@ def decode_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def forward_check_rows(w):
+    """Flat (batch, channel) rows the forward bench checks against the oracle: the first and
+    last, the middle, 63 and 64 (either side of a 64-channel tile) and 11 seeded ones; only rows
+    that exist (index_select on the device does not check its indices)."""
+    import numpy as np
+
+    rows = {0, 63, 64, w.rows // 2, w.rows - 1} | {int(r) for r in np.random.default_rng(3).integers(0, w.rows, 11)}
+    return sorted(r for r in rows if 0 <= r < w.rows)
+
+
+def sampled_channels(w, n_random=5, seed=11):
+    """Channels whose gradients the large-workload backward check compares (only existing ones)."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    chans = {0, 1, 63, 64, w.dim - 1} | {int(c) for c in rng.integers(0, w.dim, n_random)}
+    return sorted(c for c in chans if 0 <= c < w.dim)
+
+
 def backward_sampled_parity(w, out, dy_np, dl_np, n_random=5, seed=11):
     """Parity of a full-size backward run on sampled channels: the fp64 oracle on each sampled
     (batch, channel) row alone gives that row's du, ddelta, dz, and its batch's share of the
@@ -349,8 +368,7 @@ def backward_sampled_parity(w, out, dy_np, dl_np, n_random=5, seed=11):
     import oracle
     from selective_state_space_29_amd import workloads
 
-    rng = np.random.default_rng(seed)
-    chans = sorted({0, 1, 63, 64, w.dim - 1} | {int(c) for c in rng.integers(0, w.dim, n_random)})
+    chans = sampled_channels(w, n_random, seed)
     rows = [b * w.dim + d for b in range(w.batch) for d in chans]
     xr = workloads.make_row_inputs(w, rows)
     dy_r = dy_np.reshape(w.rows, -1)[rows].astype(np.float64)
@@ -698,8 +716,7 @@ def main():
     if not args.no_check:
         import oracle
 
-        rows = sorted({0, 63, 64, w.rows // 2, w.rows - 1} |
-                      {int(r) for r in np.random.default_rng(3).integers(0, w.rows, 11)})
+        rows = forward_check_rows(w)
         s = sets[(args.steps - 1) % len(sets)]
         idx = torch.tensor(rows, device=dev)
         yg = s["y"].reshape(w.rows, w.seqlen).index_select(0, idx).cpu().numpy()

@@ -32,3 +32,16 @@ def test_traffic_is_reported_only_for_the_profiled_sources():
     assert bench.measured_traffic(w3, "generic") is None
     assert bench.measured_traffic(w3, "auto", zoh=True) is None
     assert bench.measured_traffic(workloads.WORKLOADS[4], "auto") is None
+
+
+def test_sampled_indices_exist_for_every_workload():
+    """The rows / channels the bench reads back from the device exist in every workload (a
+    device-side index_select does not check its indices)."""
+    import bench
+    from selective_state_space_29_amd import workloads
+
+    for w in workloads.WORKLOADS.values():
+        rows = bench.forward_check_rows(w)
+        assert rows and all(0 <= r < w.rows for r in rows), w.name
+        chans = bench.sampled_channels(w)
+        assert chans and all(0 <= c < w.dim for c in chans), w.name
