@@ -97,10 +97,10 @@ def copy_calibration(mb, steps, warmup):
 # kernel): the record only applies while these are unchanged.
 def resolved_kernel(w, kernel, zoh=False):
     """The forward kernel the library runs for this workload: its default picks the
-    lane-per-state kernel for 16 states (Euler B), else the tiled one."""
+    lane-per-state kernels for 16, 32 or 64 states (Euler B), else the tiled one."""
     if kernel != "auto":
         return kernel
-    return "lanes" if w.dstate == 16 and not zoh else "tiled"
+    return "lanes" if w.dstate in (16, 32, 64) and not zoh else "tiled"
 
 
 def kernel_source_hash(kernel):

@@ -66,8 +66,8 @@ typedef enum mamba_scan_dtype {
  * else the generic one. */
 #define MAMBA_SCAN_FORCE_GENERIC (1u << 8) /* one lane per row, any shape and alignment */
 #define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
-#define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one lane per (channel, state), dstate 16 only, no
-                                              ZOH_B; error if it cannot run (ABI version 5) */
+#define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one lane per (channel, state): dstate 16, 32 or
+                                              64, no ZOH_B; error if it cannot run (ABI 5) */
 #define MAMBA_SCAN_KNOWN_FLAGS 0x707u
 
 /* error codes */

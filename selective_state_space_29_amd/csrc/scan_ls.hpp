@@ -64,7 +64,21 @@ __device__ __forceinline__ void ls_steps(LsRegs& r) {
     }
 }
 
-template <typename T, bool SOFTPLUS, bool HAS_Z>
+// Four consecutive elements of B or C with one 8-byte (bf16) or 16-byte (fp32) buffer load, as raw
+// fp32 / bf16 bits; the caller guarantees 4-element alignment.
+template <typename T>
+__device__ __forceinline__ void load4_bits(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff, uint32_t (&v)[4]) {
+    if constexpr (sizeof(T) == 2) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, (int)soff, 0);
+        v[0] = w[0] & 0xFFFFu, v[1] = w[0] >> 16, v[2] = w[1] & 0xFFFFu, v[3] = w[1] >> 16;
+    } else {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, (int)soff, 0);
+        v[0] = w[0], v[1] = w[1], v[2] = w[2], v[3] = w[3];
+    }
+}
+
+// VEC: B and C rows 4-element aligned, staged with one vector load per 4 steps
+template <typename T, bool SOFTPLUS, bool HAS_Z, bool VEC>
 __global__ __launch_bounds__(64 * kLsWaves) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_ls_kernel(ScanParams p) {
     __shared__ __align__(16) float s_p[kLsWaves * 4 * kLsChanP];
@@ -136,8 +150,12 @@ void scan_ls_kernel(ScanParams p) {
     auto stage_load = [&](int64_t k, bool tail, uint32_t (&v)[4]) __attribute__((always_inline)) {
         const uint32_t t0 = (uint32_t)(k * kLsT);
         if (!tail) {
+            if constexpr (VEC) {
+                load4_bits<T>(bcr, obc_l, t0 * es, v);
+            } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = load_el(bcr, obc_l + j * es, t0 * es);
+                for (int j = 0; j < 4; ++j) v[j] = load_el(bcr, obc_l + j * es, t0 * es);
+            }
         } else {
             // past len: the row's last value (finite wherever the true result is)
 #pragma unroll
@@ -270,36 +288,294 @@ void scan_ls_kernel(ScanParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// 32 and 64 states: the same lane-per-state scheme with a channel spread over N / 16 rows of
+// 16 lanes (a wave = 64 / N channels), in chunks of 16 steps.
+//   * Every row of a channel computes the channel's per-(channel, step) factors for the chunk,
+//     one step per lane, so that the row broadcast still reaches every lane of the channel.
+//   * Row r of a wave owns the 16 states 16 (r mod N/16) ... of its channel and one LDS block:
+//     each lane writes its C h terms there, then lane j of the row sums the row's 16 states for
+//     step j; the N / 16 row sums of a channel are added across rows with v_permlane16_swap
+//     (row pairs) and v_permlane32_swap (wave halves), in a fixed order. The channel's first row
+//     stores y.
+//   * B / C: the workgroup (4 waves) stages N states x 16 steps of each per chunk in LDS.
+constexpr int kLwT = 16;                      // steps per chunk
+constexpr int kLwRowP = kLwT + 4;             // LDS floats per state row
+constexpr int kLwBlkP = 16 * kLwRowP + 16;    // one row's block of 16 states, skewed 16 banks
+
+template <int N>
+struct LwRegs {
+    float h, a2;
+    float dt, dtu;
+    float Bv[kLwT], Cv[kLwT];
+    float pv[4];
+    float* sp;  // this lane's state row in its row's LDS block
+};
+
+template <int N, int S>
+__device__ __forceinline__ void lw_steps(LwRegs<N>& r) {
+    if constexpr (S < kLwT) {
+        const float dA = hw_exp2(row_bcast<S>(r.dt) * r.a2);
+        r.h = __builtin_fmaf(dA, r.h, row_bcast<S>(r.dtu) * r.Bv[S]);
+        r.pv[S % 4] = r.Cv[S] * r.h;
+        if constexpr (S % 4 == 3)
+            *reinterpret_cast<float4*>(r.sp + (S - 3)) = float4{r.pv[0], r.pv[1], r.pv[2], r.pv[3]};
+        lw_steps<N, S + 1>(r);
+    }
+}
+
+template <typename T, int N, bool SOFTPLUS, bool HAS_Z, bool VEC>
+__global__ __launch_bounds__(64 * kLsWaves) __attribute__((amdgpu_waves_per_eu(3)))
+void scan_ls_wide_kernel(ScanParams p) {
+    static_assert(N == 32 || N == 64, "wide lane-per-state kernel: 32 or 64 states");
+    constexpr int CW = 64 / N;        // channels per wave
+    constexpr int RPC = N / 16;       // rows per channel
+    constexpr int CG = kLsWaves * CW; // channels per workgroup
+    __shared__ __align__(16) float s_p[kLsWaves * 4 * kLwBlkP];
+    __shared__ __align__(16) float s_bc[2][2][N * kLwRowP];  // [chunk parity][B|C][state][step]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t blocks = (p.dim + CG - 1) / CG;
+    const int64_t b = blockIdx.x / blocks;
+    const int64_t d0 = (blockIdx.x - b * blocks) * CG + wave * CW;
+    const int c = lane / N, n = lane % N, row = lane >> 4, j = lane & 15;
+    const bool first_row = (n >> 4) == 0;
+    const bool valid = d0 + c < p.dim;
+    const int64_t d = valid ? d0 + c : p.dim - 1;
+    const int64_t L = p.len;
+
+    LwRegs<N> r;
+    r.a2 = p.A[d * p.sA_d + n] * kLog2e;
+    r.h = p.h0 ? p.h0[b * p.sh0_b + d * p.sh0_d + n] : 0.0f;
+    const float bias = p.bias ? p.bias[d * p.sbias] : 0.0f;
+    const float Dv = p.D ? p.D[d * p.sD] : 0.0f;  // no skip term: D = 0
+    float* const blk = s_p + (wave * 4 + row) * kLwBlkP;
+    r.sp = blk + j * kLwRowP;
+
+    constexpr uint32_t es = sizeof(T);
+    const int64_t d0c = d0 < p.dim ? d0 : p.dim - 1;
+    const int64_t dl = d0 + CW - 1 < p.dim ? d0 + CW - 1 : p.dim - 1;
+    const uint32_t dr = (uint32_t)(d - d0c);
+    auto rows_rsrc = [&](const void* base, int64_t sb, int64_t sd) __attribute__((always_inline)) {
+        const T* row0 = static_cast<const T*>(base) + b * sb + d0c * sd;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(row0), 0, (int)(((dl - d0c) * sd + L) * es), kLsWord3);
+    };
+    const __amdgpu_buffer_rsrc_t ur = rows_rsrc(p.u, p.su_b, p.su_d);
+    const __amdgpu_buffer_rsrc_t xr = rows_rsrc(p.delta, p.sdt_b, p.sdt_d);
+    const __amdgpu_buffer_rsrc_t zr = HAS_Z ? rows_rsrc(p.z, p.sz_b, p.sz_d) : ur;
+    const uint32_t ou = dr * (uint32_t)p.su_d * es, ox = dr * (uint32_t)p.sdt_d * es;
+    const uint32_t oz = HAS_Z ? dr * (uint32_t)p.sz_d * es : 0u;
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+        p.y + b * p.sy_b + d0c * p.sy_d, 0, (int)(((dl - d0c) * p.sy_d + L) * 4), kLsWord3);
+    const uint32_t oy_l = (valid && first_row) ? (dr * (uint32_t)p.sy_d + j) * 4u : kLsDropBase;
+
+    auto load_el = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff) __attribute__((always_inline)) {
+        if constexpr (sizeof(T) == 2)
+            return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, (int)soff, 0);
+        else
+            return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, (int)soff, 0);
+    };
+    auto widen = [](uint32_t v) __attribute__((always_inline)) {
+        return __uint_as_float(sizeof(T) == 2 ? v << 16 : v);
+    };
+
+    // B / C staging: 8 N slots of 4 steps, (B|C, state, quarter of the chunk); N / 32 slots per
+    // thread, slot = tid + 256 k, whose B|C half is wave-uniform
+    constexpr int SPT = N / 32;
+    uint32_t sofs[SPT], sofs_row[SPT];
+    float* sdst[SPT];
+    __amdgpu_buffer_rsrc_t bcr[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+        const int slot = wave * 64 + lane + 256 * k;
+        const int q = __builtin_amdgcn_readfirstlane(slot / (4 * N));
+        const int sn = (slot / 4) % N, st4 = (slot % 4) * 4;
+        const int64_t sb = q ? p.sC_b : p.sB_b, snn = q ? p.sC_n : p.sB_n;
+        bcr[k] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void*>(static_cast<const void*>(static_cast<const T*>(q ? p.C : p.B) + b * sb)), 0,
+            (int)(((N - 1) * snn + L) * es), kLsWord3);
+        sofs_row[k] = (uint32_t)(sn * snn) * es;
+        sofs[k] = sofs_row[k] + st4 * es;
+        sdst[k] = &s_bc[0][q][sn * kLwRowP + st4];
+    }
+    constexpr int kBufStride = 2 * N * kLwRowP;
+    auto stage_load = [&](int64_t k, bool tail, uint32_t (&v)[SPT][4]) __attribute__((always_inline)) {
+        const uint32_t t0 = (uint32_t)(k * kLwT);
+        if (!tail) {
+#pragma unroll
+            for (int s = 0; s < SPT; ++s) {
+                if constexpr (VEC) {
+                    load4_bits<T>(bcr[s], sofs[s], t0 * es, v[s]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[s][i] = load_el(bcr[s], sofs[s] + i * es, t0 * es);
+                }
+            }
+        } else {
+            // past len: the row's last value (finite wherever the true result is)
+#pragma unroll
+            for (int s = 0; s < SPT; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t t = t0 + (sofs[s] - sofs_row[s]) / es + i;
+                    const uint32_t tc = t < (uint32_t)L ? t : (uint32_t)L - 1;
+                    v[s][i] = load_el(bcr[s], sofs_row[s] + tc * es, 0);
+                }
+        }
+    };
+    auto stage_store = [&](int buf, const uint32_t (&v)[SPT][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < SPT; ++s)
+            *reinterpret_cast<float4*>(sdst[s] + buf * kBufStride) =
+                float4{widen(v[s][0]), widen(v[s][1]), widen(v[s][2]), widen(v[s][3])};
+    };
+
+    // raw per-(channel, step) inputs of this lane's step j of a chunk, one chunk ahead
+    struct Raw {
+        uint32_t x, u, z;
+    };
+    const uint32_t ou_l = ou + j * es, ox_l = ox + j * es, oz_l = oz + j * es;
+    constexpr uint32_t kNegInf = sizeof(T) == 2 ? 0xFF80u : 0xFF800000u;
+    auto fetch = [&](int64_t k, bool tail, Raw& w) __attribute__((always_inline)) {
+        const uint32_t t0 = (uint32_t)(k * kLwT);
+        if (!tail) {
+            w.x = load_el(xr, ox_l, t0 * es);
+            w.u = load_el(ur, ou_l, t0 * es);
+            w.z = HAS_Z ? load_el(zr, oz_l, t0 * es) : 0u;
+        } else {
+            // past len: u and z from the row's last step, delta = -inf so that dt = 0 exactly
+            const uint32_t t = t0 + j;
+            const uint32_t tj = t < (uint32_t)L ? t : (uint32_t)L - 1;
+            const uint32_t xv = load_el(xr, ox + tj * es, 0);
+            w.x = t < (uint32_t)L ? xv : kNegInf;
+            w.u = load_el(ur, ou + tj * es, 0);
+            w.z = HAS_Z ? load_el(zr, oz + tj * es, 0) : 0u;
+        }
+    };
+    auto read_bc = [&](int buf) __attribute__((always_inline)) {
+        const float* sb = &s_bc[buf][0][n * kLwRowP];
+        const float* sc = &s_bc[buf][1][n * kLwRowP];
+#pragma unroll
+        for (int q = 0; q < kLwT / 4; ++q) {
+            const float4 vb = *reinterpret_cast<const float4*>(sb + 4 * q);
+            const float4 vc = *reinterpret_cast<const float4*>(sc + 4 * q);
+            r.Bv[4 * q] = vb.x, r.Bv[4 * q + 1] = vb.y, r.Bv[4 * q + 2] = vb.z, r.Bv[4 * q + 3] = vb.w;
+            r.Cv[4 * q] = vc.x, r.Cv[4 * q + 1] = vc.y, r.Cv[4 * q + 2] = vc.z, r.Cv[4 * q + 3] = vc.w;
+        }
+    };
+    float uv, gz;
+    auto prologue = [&](const Raw& w) __attribute__((always_inline)) {
+        const float xb = widen(w.x) + bias;
+        r.dt = SOFTPLUS ? softplus_f(xb) : hw_exp2(xb * kLog2e);
+        uv = widen(w.u);
+        r.dtu = r.dt * uv;
+        gz = HAS_Z ? silu_f(widen(w.z)) : 1.0f;
+    };
+
+    // the same software pipeline as the 16-state kernel, per 16-step chunk
+    const int64_t nch = (L + kLwT - 1) / kLwT;
+    const bool ragged = L % kLwT != 0;
+    {
+        Raw w0;
+        fetch(0, ragged && nch == 1, w0);
+        uint32_t v[SPT][4];
+        stage_load(0, ragged && nch == 1, v);
+        stage_store(0, v);
+        prologue(w0);
+    }
+    for (int64_t k = 0; k < nch; ++k) {
+        const uint32_t t0 = (uint32_t)(k * kLwT);
+        const int buf = (int)(k & 1);
+        const int64_t kn = k + 1 < nch ? k + 1 : k;
+        const bool next_tail = ragged && kn == nch - 1;
+        __syncthreads();  // chunk k staged; every wave is done with chunk k-1's buffer
+        uint32_t sv[SPT][4];
+        stage_load(kn, next_tail, sv);
+        Raw nx;
+        fetch(kn, next_tail, nx);
+        read_bc(buf);
+        lw_steps<N, 0>(r);
+        stage_store(buf ^ 1, sv);
+        const float u0 = uv, g0 = gz;
+        prologue(nx);
+        __builtin_amdgcn_wave_barrier();
+        // step j: this row's 16 states in order, then the channel's rows: pairs, then halves
+        float y = blk[j];
+#pragma unroll
+        for (int m = 1; m < 16; ++m) y += blk[m * kLwRowP + j];
+        __builtin_amdgcn_wave_barrier();
+        if constexpr (RPC >= 2) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+            y = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        if constexpr (RPC == 4) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+            y = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        const float o = __builtin_fmaf(Dv, u0, y) * g0;
+        if (!(ragged && k == nch - 1)) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), yr, (int)oy_l, (int)(t0 * 4u), 0);
+        } else {
+            const uint32_t a = t0 + j < (uint32_t)L ? oy_l : kLsDropBase;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), yr, (int)a, (int)(t0 * 4u), 0);
+        }
+    }
+    if (p.last_state && valid) p.last_state[b * p.sls_b + d * p.sls_d + n] = r.h;
+}
+
+// ---------------------------------------------------------------------------------------------
 // host side
 
-// The lane-per-state kernel takes dstate 16 with the Euler input term, and shapes whose byte
-// offsets within a wave's 4 rows (u, delta, z, y) and within a batch's B / C fit 31 bits.
+// The lane-per-state kernels take dstate 16, 32 or 64 with the Euler input term, and shapes whose
+// byte offsets within a wave's rows (u, delta, z, y) and within a batch's B / C fit 31 bits.
 inline bool ls_eligible(const ScanParams& q, int64_t es) {
-    if (q.dstate != 16 || q.zoh_b) return false;
+    if ((q.dstate != 16 && q.dstate != 32 && q.dstate != 64) || q.zoh_b) return false;
     const int64_t lim = (int64_t)1 << 31;
     const auto rows_ok = [&](const void* ptr, int64_t sd, int64_t e) {
         return ptr == nullptr || (3 * sd + q.len) * e < lim;
     };
     if (!rows_ok(q.u, q.su_d, es) || !rows_ok(q.delta, q.sdt_d, es) || !rows_ok(q.z, q.sz_d, es)) return false;
     if (!rows_ok(q.y, q.sy_d, 4)) return false;
-    if ((15 * q.sB_n + q.len) * es >= lim || (15 * q.sC_n + q.len) * es >= lim) return false;
-    if (q.batch * ((q.dim + 15) / 16) > 0x7fffffff) return false;
+    if (((q.dstate - 1) * q.sB_n + q.len) * es >= lim || ((q.dstate - 1) * q.sC_n + q.len) * es >= lim) return false;
+    if (q.batch * q.dim > 0x7fffffff) return false;
     return true;
+}
+
+template <typename T, bool SP, bool HZ, bool VEC>
+int launch_ls_cfg(const ScanParams& q, hipStream_t stream) {
+    const void* fn;
+    int64_t per_group;
+    switch (q.dstate) {
+        case 16: fn = reinterpret_cast<const void*>(&scan_ls_kernel<T, SP, HZ, VEC>); per_group = 16; break;
+        case 32: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 32, SP, HZ, VEC>); per_group = 8; break;
+        default: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 64, SP, HZ, VEC>); per_group = 4; break;
+    }
+    void* args[] = {const_cast<ScanParams*>(&q)};
+    const int64_t groups = q.batch * ((q.dim + per_group - 1) / per_group);
+    return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * kLsWaves), args, 0, stream) == hipSuccess
+               ? MAMBA_SCAN_OK
+               : MAMBA_SCAN_ERR_LAUNCH;
+}
+
+template <typename T, bool SP, bool HZ>
+int launch_ls_vec(const ScanParams& q, hipStream_t stream) {
+    // B / C rows 4-element aligned: one vector load per 4 staged steps
+    const auto al = [](const void* ptr, int64_t sb, int64_t sn) {
+        return reinterpret_cast<uintptr_t>(ptr) % (4 * sizeof(T)) == 0 && sb % 4 == 0 && sn % 4 == 0;
+    };
+    if (al(q.B, q.sB_b, q.sB_n) && al(q.C, q.sC_b, q.sC_n)) return launch_ls_cfg<T, SP, HZ, true>(q, stream);
+    return launch_ls_cfg<T, SP, HZ, false>(q, stream);
 }
 
 template <typename T>
 int launch_ls(const ScanParams& q, hipStream_t stream) {
     if (!ls_eligible(q, sizeof(T))) return MAMBA_SCAN_ERR_UNSUPPORTED;
     const bool sp = q.softplus != 0, hz = q.z != nullptr;
-    const void* fn = sp ? (hz ? reinterpret_cast<const void*>(&scan_ls_kernel<T, true, true>)
-                              : reinterpret_cast<const void*>(&scan_ls_kernel<T, true, false>))
-                        : (hz ? reinterpret_cast<const void*>(&scan_ls_kernel<T, false, true>)
-                              : reinterpret_cast<const void*>(&scan_ls_kernel<T, false, false>));
-    void* args[] = {const_cast<ScanParams*>(&q)};
-    const int64_t groups = q.batch * ((q.dim + 15) / 16);
-    return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * kLsWaves), args, 0, stream) == hipSuccess
-               ? MAMBA_SCAN_OK
-               : MAMBA_SCAN_ERR_LAUNCH;
+    if (sp && hz) return launch_ls_vec<T, true, true>(q, stream);
+    if (sp) return launch_ls_vec<T, true, false>(q, stream);
+    if (hz) return launch_ls_vec<T, false, true>(q, stream);
+    return launch_ls_vec<T, false, false>(q, stream);
 }
 
 }  // namespace mscan

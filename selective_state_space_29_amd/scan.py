@@ -138,7 +138,7 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     u, delta, z: (batch, dim, L); B, C: (batch, N, L); one storage dtype for all five
     (torch.float32 or torch.bfloat16). A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N);
     these are taken in fp32. ``kernel``: None (library picks), "generic", "tiled" or "lanes"
-    (one lane per (channel, state); 16 states only).
+    (one lane per (channel, state); 16, 32 or 64 states).
     """
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):

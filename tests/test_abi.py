@@ -99,9 +99,11 @@ CASES = [
     ("zoh_flag_is_known", lambda c: (c.__setitem__("flags", scan.ZOH_B), setattr(c["ptrs"], "u", None)), -1),
     ("both_forced", _flags(scan.FORCE_GENERIC | scan.FORCE_TILED), -6),
     ("lanes_and_tiled_forced", _flags(scan.FORCE_LANES | scan.FORCE_TILED), -6),
-    # the lane-per-state kernel takes 16 states, the Euler input term, 31-bit row offsets
-    ("lanes_forced_32_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
-                                          setattr(c["shape"], "dstate", 32)), -8),
+    # the lane-per-state kernels take 16, 32 or 64 states, the Euler input term, 31-bit row offsets
+    ("lanes_forced_8_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
+                                         setattr(c["shape"], "dstate", 8)), -8),
+    ("lanes_forced_48_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
+                                          setattr(c["shape"], "dstate", 48)), -8),
     ("lanes_forced_zoh", _flags(scan.DELTA_SOFTPLUS | scan.FORCE_LANES | scan.ZOH_B), -8),
     ("lanes_forced_wide_rows", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
                                           setattr(c["st"], "u", (ctypes.c_int64 * 3)(1 << 31, 1 << 29, 1))), -8),

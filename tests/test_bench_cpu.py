@@ -28,7 +28,7 @@ def test_traffic_is_reported_only_for_the_profiled_sources():
     assert bench.measured_traffic(w3, "auto") == bench.measured_traffic(w3, "lanes")
     assert bench.resolved_kernel(w3, "auto") == "lanes"
     assert bench.resolved_kernel(w3, "auto", zoh=True) == "tiled"
-    assert bench.resolved_kernel(workloads.WORKLOADS[5], "auto") == "tiled"
+    assert bench.resolved_kernel(workloads.WORKLOADS[5], "auto") == "lanes"
     assert bench.measured_traffic(w3, "generic") is None
     assert bench.measured_traffic(w3, "auto", zoh=True) is None
     assert bench.measured_traffic(workloads.WORKLOADS[4], "auto") is None
