@@ -531,7 +531,7 @@ def upstream_bench(args):
     for i in range(len(sets)):
         eager[i] = [t.clone() for t in up(i)]
     torch.cuda.synchronize()
-    per_us = graph_timed(up, args.steps, args.warmup, stream)
+    per_us = graph_timed(up, args.steps, args.warmup, stream, reps=7, warm_reps=3)
     replay_equal = all(torch.equal(a, b) for i in range(len(sets)) for a, b in zip(sets[i][1], eager[i]))
     mean_us = float(np.median(per_us))
     span_us = mean_us
@@ -550,7 +550,7 @@ def upstream_bench(args):
         _, B, C = scan.split_xdbl(xdbl, w.dt_rank, w.dstate)
         scan.selective_scan_fn(u, delta, A, B, C, D=Dv, z=z, delta_bias=dt_bias, delta_softplus=True, out=y)
 
-    blk_us = graph_timed(block, args.steps, args.warmup, stream)
+    blk_us = graph_timed(block, args.steps, args.warmup, stream, reps=7, warm_reps=3)
     log(f"upstream + scan: graph replay {blk_us.round(2).tolist()} us per call")
 
     # parity of the last upstream outputs against the fp64 oracle, every element
@@ -604,7 +604,7 @@ def upstream_bench(args):
                    "dt_rank": w.dt_rank, "d_conv": w.d_conv, "seq_len": w.seqlen, "buffer_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": alg,
-                     "mean_launch_us": round(mean_us, 2), "timing": "median of 5 HIP-graph replays of "
+                     "mean_launch_us": round(mean_us, 2), "timing": "median of 7 HIP-graph replays (after 3 untimed) of "
                      f"{args.steps} captured calls, per call", "graph_replay_equals_eager": replay_equal,
                      "mfma": {"flops_per_launch": w.flops(), "achieved_TFLOP_s": round(tflops, 1),
                               "peak_TFLOP_s": MFMA_BF16_PEAK_TFLOPS,
