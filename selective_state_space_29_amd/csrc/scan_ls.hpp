@@ -64,17 +64,37 @@ __device__ __forceinline__ void ls_steps(LsRegs& r) {
     }
 }
 
-// Four consecutive elements of B or C with one 8-byte (bf16) or 16-byte (fp32) buffer load, as raw
-// fp32 / bf16 bits; the caller guarantees 4-element alignment.
+// Staged values of 4 consecutive steps of B or C, as raw bits. PACKED (bf16 rows staged with
+// vector loads): v[0], v[1] hold the 4 values as two bf16 pairs; otherwise one value per entry.
+// The bits are only unpacked / widened where they are written to LDS: an ALU operation next to
+// the load would make the compiler wait for the load there.
 template <typename T>
-__device__ __forceinline__ void load4_bits(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff, uint32_t (&v)[4]) {
+__device__ __forceinline__ void load4_raw(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff, uint32_t (&v)[4]) {
+    // one 8-byte (bf16) or 16-byte (fp32) buffer load; the caller guarantees 4-element alignment
     if constexpr (sizeof(T) == 2) {
         const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, (int)soff, 0);
-        v[0] = w[0] & 0xFFFFu, v[1] = w[0] >> 16, v[2] = w[1] & 0xFFFFu, v[3] = w[1] >> 16;
+        v[0] = w[0], v[1] = w[1], v[2] = 0u, v[3] = 0u;
     } else {
         const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, (int)soff, 0);
         v[0] = w[0], v[1] = w[1], v[2] = w[2], v[3] = w[3];
     }
+}
+
+template <typename T, bool PACKED>
+__device__ __forceinline__ float4 widen4(const uint32_t (&v)[4]) {
+    if constexpr (sizeof(T) == 2 && PACKED)
+        return float4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
+                      __uint_as_float(v[1] & 0xFFFF0000u)};
+    else if constexpr (sizeof(T) == 2)
+        return float4{__uint_as_float(v[0] << 16), __uint_as_float(v[1] << 16), __uint_as_float(v[2] << 16),
+                      __uint_as_float(v[3] << 16)};
+    else
+        return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+}
+
+// element bits e0..e3 (bf16 zero-extended) into the PACKED layout
+__device__ __forceinline__ void pack4_bf16(uint32_t (&v)[4]) {
+    v[0] = v[0] | (v[1] << 16), v[1] = v[2] | (v[3] << 16), v[2] = 0u, v[3] = 0u;
 }
 
 // VEC: B and C rows 4-element aligned, staged with one vector load per 4 steps
@@ -151,7 +171,7 @@ void scan_ls_kernel(ScanParams p) {
         const uint32_t t0 = (uint32_t)(k * kLsT);
         if (!tail) {
             if constexpr (VEC) {
-                load4_bits<T>(bcr, obc_l, t0 * es, v);
+                load4_raw<T>(bcr, obc_l, t0 * es, v);
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v[j] = load_el(bcr, obc_l + j * es, t0 * es);
@@ -163,6 +183,7 @@ void scan_ls_kernel(ScanParams p) {
                 const uint32_t tj = t0 + st4 + j < (uint32_t)L ? t0 + st4 + j : (uint32_t)L - 1;
                 v[j] = load_el(bcr, obc + tj * es, 0);
             }
+            if constexpr (VEC && sizeof(T) == 2) pack4_bf16(v);
         }
     };
 
@@ -235,7 +256,7 @@ void scan_ls_kernel(ScanParams p) {
         fetch(0, ragged && nch == 1, w0);
         uint32_t v[4];
         stage_load(0, ragged && nch == 1, v);
-        *reinterpret_cast<float4*>(sdst) = float4{widen(v[0]), widen(v[1]), widen(v[2]), widen(v[3])};
+        *reinterpret_cast<float4*>(sdst) = widen4<T, VEC>(v);
         prologue(w0);
     }
     for (int64_t k = 0; k < nch; ++k) {
@@ -254,7 +275,7 @@ void scan_ls_kernel(ScanParams p) {
         ls_steps<1, 1, 0>(r);
         // the next chunk's B / C into the other buffer (its last readers passed the barrier above)
         *reinterpret_cast<float4*>(sdst + (buf ^ 1) * kBufStride) =
-            float4{widen(sv[0]), widen(sv[1]), widen(sv[2]), widen(sv[3])};
+            widen4<T, VEC>(sv);
         const float u0 = uv[0], u1 = uv[1], g0 = gz[0], g1 = gz[1];
         prologue(nx);
         __builtin_amdgcn_wave_barrier();
@@ -406,7 +427,7 @@ void scan_ls_wide_kernel(ScanParams p) {
 #pragma unroll
             for (int s = 0; s < SPT; ++s) {
                 if constexpr (VEC) {
-                    load4_bits<T>(bcr[s], sofs[s], t0 * es, v[s]);
+                    load4_raw<T>(bcr[s], sofs[s], t0 * es, v[s]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[s][i] = load_el(bcr[s], sofs[s] + i * es, t0 * es);
@@ -422,13 +443,15 @@ void scan_ls_wide_kernel(ScanParams p) {
                     const uint32_t tc = t < (uint32_t)L ? t : (uint32_t)L - 1;
                     v[s][i] = load_el(bcr[s], sofs_row[s] + tc * es, 0);
                 }
+            if constexpr (VEC && sizeof(T) == 2)
+#pragma unroll
+                for (int s = 0; s < SPT; ++s) pack4_bf16(v[s]);
         }
     };
     auto stage_store = [&](int buf, const uint32_t (&v)[SPT][4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < SPT; ++s)
-            *reinterpret_cast<float4*>(sdst[s] + buf * kBufStride) =
-                float4{widen(v[s][0]), widen(v[s][1]), widen(v[s][2]), widen(v[s][3])};
+            *reinterpret_cast<float4*>(sdst[s] + buf * kBufStride) = widen4<T, VEC>(v[s]);
     };
 
     // raw per-(channel, step) inputs of this lane's step j of a chunk, one chunk ahead
