@@ -33,6 +33,8 @@ SLOTS_PER_ROW_STEP = 30    # softplus, dt*u, bias, skip, silu gate
 # zero-order-hold B adds, per element: dt*A, the 4-term series and dt*p, dA - 1 and * 1/A, the
 # compare and select, and * u
 SLOTS_PER_ELEMENT_ZOH = SLOTS_PER_ELEMENT + 11
+SLOTS_PER_ELEMENT_BWD = 26     # backward: 2 x 7 forward recurrence + 10 reverse + 2 channel sums
+SLOTS_PER_ROW_STEP_BWD = 100
 # rocprofv3 FETCH_SIZE / WRITE_SIZE records of the forward kernels at the Mamba-130m shape, each
 # with a hash of the sources it was measured on
 TRAFFIC_RECORDS = {
@@ -468,6 +470,14 @@ def backward_bench(args):
     written = ((2 + nz) * w.rows * w.seqlen * 4 + 2 * w.batch * w.dstate * w.seqlen * 4
                + w.dim * (w.dstate + 2) * 4)
     gbs = (read + written) / (mean_us * 1e-6) / 1e9
+    # VALU work of the recompute-based backward, in issue slots (a transcendental counts 4): per
+    # element the forward recurrence twice (segment checkpoints, then the segment's states:
+    # 2 x 7) and the reverse recurrence (lam, dC, dB, sum lam B, lam a h, its A and dt terms,
+    # sum C h, the decay of lam: 10) plus the channel sums of dB / dC (2); per (b, d, t) the two
+    # prologues (softplus, sigmoid, gate and its derivative), the sums over states and the
+    # per-channel gradients (about 100)
+    bwd_slots = w.elements * SLOTS_PER_ELEMENT_BWD + w.rows * w.seqlen * SLOTS_PER_ROW_STEP_BWD
+    bwd_tflops = 2 * bwd_slots / (mean_us * 1e-6) / 1e12
     res = {
         "metric": "scan backward, Gelem/s (B*D*L*N) per mamba_scan_bwd call",
         "value": round(w.elements / (mean_us * 1e-6) / 1e9, 2),
@@ -483,10 +493,12 @@ def backward_bench(args):
         "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name + "-backward", "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seq_len": w.seqlen, "storage": w.dtype},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes": read + written, "mean_call_us": round(mean_us, 2),
-                     "min_call_us": round(float(per_us.min()), 2)},
+        "roofline": {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_tflops / VALU_PEAK_TFLOPS, 4), "traffic": None,
+                     "valu_slots_per_call": bwd_slots, "mean_call_us": round(mean_us, 2),
+                     "min_call_us": round(float(per_us.min()), 2),
+                     "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": read + written}},
         "parity": {"max_rel_err": errs},
     }
     print(json.dumps(res), flush=True)
