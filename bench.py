@@ -35,6 +35,7 @@ SLOTS_PER_ROW_STEP = 30    # softplus, dt*u, bias, skip, silu gate
 SLOTS_PER_ELEMENT_ZOH = SLOTS_PER_ELEMENT + 11
 SLOTS_PER_ELEMENT_BWD = 26     # backward: 2 x 7 forward recurrence + 10 reverse + 2 channel sums
 SLOTS_PER_ROW_STEP_BWD = 100
+SLOTS_PER_ELEMENT_FWD_RECURRENCE = 7  # one forward recurrence step of the backward's count
 # rocprofv3 FETCH_SIZE / WRITE_SIZE records of the forward kernels at the Mamba-130m shape, each
 # with a hash of the sources it was measured on
 TRAFFIC_RECORDS = {
@@ -59,6 +60,10 @@ def parse():
                          "the state by --chunk steps from the previous call's last_state")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward scan, time the backward pass (mamba_scan_bwd)")
+    ap.add_argument("--checkpoints", action="store_true",
+                    help="with --backward: the forward saves the state every 16 steps "
+                         "(MAMBA_SCAN_SAVE_CHECKPOINTS) and the backward starts from them; also "
+                         "times that forward")
     ap.add_argument("--upstream", action="store_true",
                     help="instead of the scan, time the block's upstream stages "
                          "(mamba_block_upstream: conv1d + SiLU, x_proj, dt_proj) at the Mamba-130m "
@@ -431,10 +436,31 @@ def backward_bench(args):
     dl_np = rng.standard_normal((w.batch, w.dim, w.dstate)).astype(np.float32)
     dy, dl = torch.from_numpy(dy_np).to(dev), torch.from_numpy(dl_np).to(dev)
 
+    ck, fwd_ck = None, None
+    if args.checkpoints:
+        # the forward that saves the segment states, graph-timed like the forward bench, then
+        # once more eagerly to leave the states for the backward
+        ck = torch.empty(scan.checkpoint_shape(w.batch, w.dim, w.seqlen, w.dstate), dtype=torch.float32,
+                         device=dev)
+        y = torch.empty((w.batch, w.dim, w.seqlen), dtype=torch.float32, device=dev)
+        ls = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+        def fwd(_i):
+            scan.selective_scan_fn(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                                   delta_bias=g["delta_bias"], delta_softplus=w.softplus,
+                                   return_last_state=True, out=y, last_state_out=ls, checkpoints_out=ck)
+
+        fwd_us = graph_timed(fwd, 4, 1, torch.cuda.current_stream(dev), reps=7, warm_reps=3)
+        fwd(0)
+        torch.cuda.synchronize()
+        fwd_ck = {"median_call_us": round(float(np.median(fwd_us)), 2),
+                  "checkpoint_bytes": ck.numel() * 4}
+
     def step():
         return scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"],
                                        z=g["z"], delta_bias=g["delta_bias"],
-                                       delta_softplus=w.softplus, dlast_state=dl, want_dh0=False)
+                                       delta_softplus=w.softplus, dlast_state=dl, want_dh0=False,
+                                       checkpoints=ck)
 
     for _ in range(args.warmup):
         step()
@@ -469,6 +495,8 @@ def backward_bench(args):
             + w.rows * w.seqlen * 4 + w.rows * w.dstate * 4 + w.dim * (w.dstate + 2) * 4)
     written = ((2 + nz) * w.rows * w.seqlen * 4 + 2 * w.batch * w.dstate * w.seqlen * 4
                + w.dim * (w.dstate + 2) * 4)
+    if ck is not None:
+        read += ck.numel() * 4
     gbs = (read + written) / (mean_us * 1e-6) / 1e9
     # VALU work of the recompute-based backward, in issue slots (a transcendental counts 4): per
     # element the forward recurrence twice (segment checkpoints, then the segment's states:
@@ -476,7 +504,10 @@ def backward_bench(args):
     # sum C h, the decay of lam: 10) plus the channel sums of dB / dC (2); per (b, d, t) the two
     # prologues (softplus, sigmoid, gate and its derivative), the sums over states and the
     # per-channel gradients (about 100)
-    bwd_slots = w.elements * SLOTS_PER_ELEMENT_BWD + w.rows * w.seqlen * SLOTS_PER_ROW_STEP_BWD
+    # (given the forward's checkpoints, the first of the two forward recurrences is not run: 7
+    # slots fewer per element; the checkpoints are read instead of written and read back)
+    per_el = SLOTS_PER_ELEMENT_BWD - (SLOTS_PER_ELEMENT_FWD_RECURRENCE if ck is not None else 0)
+    bwd_slots = w.elements * per_el + w.rows * w.seqlen * SLOTS_PER_ROW_STEP_BWD
     bwd_tflops = 2 * bwd_slots / (mean_us * 1e-6) / 1e12
     res = {
         "metric": "scan backward, Gelem/s (B*D*L*N) per mamba_scan_bwd call",
@@ -491,7 +522,8 @@ def backward_bench(args):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded counter-based generator)",
-        "config": {"workload": w.name + "-backward", "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
+        "config": {"workload": w.name + ("-backward-from-checkpoints" if ck is not None else "-backward"),
+                   "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seq_len": w.seqlen, "storage": w.dtype},
         "roofline": {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": VALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / VALU_PEAK_TFLOPS, 4), "traffic": None,
@@ -501,6 +533,8 @@ def backward_bench(args):
                              "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": read + written}},
         "parity": {"max_rel_err": errs},
     }
+    if fwd_ck is not None:
+        res["forward_saving_checkpoints"] = fwd_ck
     print(json.dumps(res), flush=True)
 
 

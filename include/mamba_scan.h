@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 5
+#define MAMBA_SCAN_ABI_VERSION 6
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -61,6 +61,13 @@ typedef enum mamba_scan_dtype {
  * (dt * B * u where A[d,n] = 0) instead of dt * B * u. "手把手用PyTorch实现Mamba的SSM层…" §2.1:
  * B_d = A^-1 (e^{A dt} - I) B, for a diagonal A. Forward only (mamba_scan_bwd rejects it). */
 #define MAMBA_SCAN_ZOH_B (1u << 2)
+/* Save the state before every 16-step segment, for the backward pass: the forward writes
+ * h before steps 0, 16, 32, ... of every (b, d) row to the workspace, laid out (batch, dim,
+ * ceil(len/16), dstate) fp32 contiguous (mamba_scan_workspace_bytes gives its size with this
+ * flag), and mamba_scan_bwd, given them as `checkpoints`, skips recomputing them. The
+ * lane-per-state kernels only (dstate 16, 32 or 64, no ZOH_B): MAMBA_SCAN_ERR_UNSUPPORTED
+ * otherwise. ABI version 6. */
+#define MAMBA_SCAN_SAVE_CHECKPOINTS (1u << 3)
 /* Kernel selection, for testing and tuning; at most one of these bits (MAMBA_SCAN_ERR_ARGS
  * otherwise). Default (none): the lane-per-state kernel where it can run, else the tiled one,
  * else the generic one. */
@@ -68,7 +75,7 @@ typedef enum mamba_scan_dtype {
 #define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
 #define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one lane per (channel, state): dstate 16, 32 or
                                               64, no ZOH_B; error if it cannot run (ABI 5) */
-#define MAMBA_SCAN_KNOWN_FLAGS 0x707u
+#define MAMBA_SCAN_KNOWN_FLAGS 0x70Fu
 
 /* error codes */
 #define MAMBA_SCAN_OK 0
@@ -79,7 +86,8 @@ typedef enum mamba_scan_dtype {
 #define MAMBA_SCAN_ERR_DSTATE (-5)    /* dstate above MAMBA_SCAN_MAX_DSTATE */
 #define MAMBA_SCAN_ERR_ARGS (-6)      /* flags/pointer mismatch, unknown flag, overlapping buffers */
 #define MAMBA_SCAN_ERR_LAUNCH (-7)    /* the HIP runtime refused the launch */
-#define MAMBA_SCAN_ERR_UNSUPPORTED (-8) /* a forced kernel cannot run this shape/alignment */
+#define MAMBA_SCAN_ERR_UNSUPPORTED (-8) /* a forced kernel, or SAVE_CHECKPOINTS, cannot run
+                                           this shape/alignment */
 #define MAMBA_SCAN_ERR_WORKSPACE (-9) /* workspace too small for the requested plan */
 
 #define MAMBA_SCAN_MAX_DSTATE 256
@@ -122,7 +130,9 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s,
 
 /* Bytes of device workspace that let mamba_scan_fwd split long sequences across workgroups
  * (an exact two-pass carry of the state between segments of L). 0 when the plan needs none.
- * A call given less workspace than this still runs, unsplit. Negative on invalid arguments. */
+ * A call given less workspace than this still runs, unsplit. Negative on invalid arguments.
+ * With MAMBA_SCAN_SAVE_CHECKPOINTS: the size of the saved states instead, which the call then
+ * requires (MAMBA_SCAN_ERR_WORKSPACE below it; 4-byte alignment, MAMBA_SCAN_ERR_ARGS otherwise). */
 int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype,
                                    uint32_t flags);
 
@@ -155,6 +165,10 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *  - Any dstate up to MAMBA_SCAN_MAX_DSTATE. Above 16 the states are processed in blocks of at
  *    most 16, one launch each: du, ddelta and dz are accumulated in place across the blocks, in
  *    block order, so their values can differ in the last bits from a one-block sum.
+ *  - checkpoints (ABI 6): NULL, or the states that a forward call with
+ *    MAMBA_SCAN_SAVE_CHECKPOINTS saved for the same inputs (same h0 included), 4-byte aligned;
+ *    the scan then starts from them instead of recomputing them. The caller guarantees that they
+ *    belong to these inputs: nothing checks it.
  *  - Outputs may not overlap each other, any input or the workspace (MAMBA_SCAN_ERR_ARGS).
  *  - Enqueued on `stream`; B/C widening, the scan (one launch per block of states), a
  *    fixed-order reduction.
@@ -183,6 +197,9 @@ typedef struct mamba_scan_bwd_ptrs {
     float* dh0;                   /* (batch, dim, dstate) or NULL */
     void* workspace;
     int64_t workspace_bytes;
+    const float* checkpoints;     /* (batch, dim, ceil(len/16), dstate) fp32 states saved by the
+                                     forward (MAMBA_SCAN_SAVE_CHECKPOINTS) on the same inputs, or
+                                     NULL: recomputed (ABI version 6) */
 } mamba_scan_bwd_ptrs;
 
 int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,

@@ -27,6 +27,8 @@ struct ScanParams {
     int64_t sA_d, sD, sbias;
     int softplus;
     int zoh_b;  // B discretised by zero-order hold instead of dt * B
+    float* ck;        // or NULL: the state before every 16-step segment, (batch, dim, ck_nseg, dstate)
+    int64_t ck_nseg;  // ceil(len / 16)
 };
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -141,6 +141,8 @@ ScanParams make_params(const mamba_scan_ptrs* p, const mamba_scan_shape* s, cons
     q.sD = st->D;
     q.sbias = st->delta_bias;
     q.softplus = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) ? 1 : 0;
+    q.ck = (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) ? static_cast<float*>(p->workspace) : nullptr;
+    q.ck_nseg = (s->len + 15) / 16;
     return q;
 }
 
@@ -191,6 +193,7 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
     if (flags & ~MAMBA_SCAN_KNOWN_FLAGS) return MAMBA_SCAN_ERR_ARGS;
     if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
+    if (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) return s->batch * s->dim * ((s->len + 15) / 16) * s->dstate * 4;
     return tiled_workspace_bytes(*s, flags);
 }
 
@@ -217,6 +220,7 @@ int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     if (p->workspace_bytes < 0 || (p->workspace_bytes > 0 && !p->workspace)) return MAMBA_SCAN_ERR_ARGS;
     if (!p->workspace || p->workspace_bytes < need) return MAMBA_SCAN_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(p->workspace) % 256 != 0) return MAMBA_SCAN_ERR_ARGS;
+    if (reinterpret_cast<uintptr_t>(p->checkpoints) % 4 != 0) return MAMBA_SCAN_ERR_ARGS;
     if (s->batch * ((s->dim + 63) / 64) > 0x7fffffff) return MAMBA_SCAN_ERR_UNSUPPORTED;
 
     const int64_t es = dtype == MAMBA_SCAN_BF16 ? 2 : 4;
@@ -233,7 +237,8 @@ int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     const Span ins[] = {span(p->u, DL * es), span(p->delta, DL * es), span(p->z, DL * es), span(p->B, NL * es),
                         span(p->C, NL * es), span(p->A, s->dim * s->dstate * 4), span(p->D, s->dim * 4),
                         span(p->delta_bias, s->dim * 4), span(p->h0, DN * 4), span(p->dy, DL * 4),
-                        span(p->dlast_state, DN * 4), span(p->workspace, p->workspace_bytes)};
+                        span(p->dlast_state, DN * 4), span(p->workspace, p->workspace_bytes),
+                        span(p->checkpoints, s->batch * s->dim * ((s->len + 15) / 16) * s->dstate * 4)};
     const Span outs[] = {span(p->du, DL * 4), span(p->ddelta, DL * 4), span(p->dz, DL * 4),
                          span(p->dB, NL * 4), span(p->dC, NL * 4), span(p->dA, s->dim * s->dstate * 4),
                          span(p->dD, s->dim * 4), span(p->ddelta_bias, s->dim * 4), span(p->dh0, DN * 4)};
@@ -317,7 +322,15 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const ma
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool bf16 = dtype == MAMBA_SCAN_BF16;
 
-    // default order: lane-per-state (16 states), then the tiled kernel, then the generic one
+    if (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) {
+        // saved by the lane-per-state kernels only, into a workspace of the queried size
+        const int64_t need = s->batch * s->dim * ((s->len + 15) / 16) * s->dstate * 4;
+        if (!p->workspace || p->workspace_bytes < need) return MAMBA_SCAN_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(p->workspace) % 4) return MAMBA_SCAN_ERR_ARGS;
+        if (flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+        return bf16 ? launch_ls<bf16_t>(q, hs) : launch_ls<float>(q, hs);
+    }
+    // default order: lane-per-state (16, 32, 64 states), then the tiled kernel, then the generic one
     if (!(flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED))) {
         const int lrc = bf16 ? launch_ls<bf16_t>(q, hs) : launch_ls<float>(q, hs);
         if (lrc != MAMBA_SCAN_ERR_UNSUPPORTED || (flags & MAMBA_SCAN_FORCE_LANES)) return lrc;

@@ -58,7 +58,9 @@ struct BwdParams {
     float* bpart;   // (batch, dim)
     int64_t batch, dim, len, dstate, lp, nseg, groups;
     int64_t n0, nb, ckn;  // this launch's states n0 .. n0 + nb - 1; ck's state stride
+    int64_t ck_n0;        // ck's state index of this block's first state
     int first, last;      // first / last block of states: initialises / finishes the sums
+    int have_ck;          // ck holds the forward pass's states (all N): no recomputation
 };
 
 constexpr int kBwdW = 8;     // waves per workgroup
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
     const float* Brow = p.bc + (b * N + nbase) * p.lp;              // state nbase + s at + s*lp
     const float* Crow = p.bc + ((p.batch + b) * N + nbase) * p.lp;
     const int64_t ckn = p.ckn;
-    float* ckrow = p.ck + (b * p.dim + (mvalid ? dm : 0)) * p.nseg * ckn + (wave_live ? nloc : 0);
+    float* ckrow = p.ck + (b * p.dim + (mvalid ? dm : 0)) * p.nseg * ckn + p.ck_n0 + (wave_live ? nloc : 0);
 
     // zero partials for waves that hold no states (read by the epilogue, never written after)
     if (!wave_live)
@@ -155,10 +157,11 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
         }
     };
 
-    // ---- phase 1: forward, state before each segment to the workspace ----
+    // ---- phase 1: forward, state before each segment to the workspace (skipped when the
+    // forward pass saved them) ----
     Raw1 nx1;
     fetch1(0, nx1);
-    for (int64_t k = 0; k < p.nseg; ++k) {
+    for (int64_t k = 0; k < (p.have_ck ? 0 : p.nseg); ++k) {
         __syncthreads();
         const Raw1 r1 = nx1;
         fetch1(k + 1, nx1);
@@ -564,9 +567,12 @@ int launch_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool sof
                             dim3((unsigned)((nwide + 255) / 256)), dim3(256), args, 0, stream) != hipSuccess)
             return MAMBA_SCAN_ERR_LAUNCH;
     }
-    q.ckn = bwd_block_states(s.dstate);
+    q.have_ck = p->checkpoints != nullptr;
+    if (q.have_ck) q.ck = const_cast<float*>(p->checkpoints);
+    q.ckn = q.have_ck ? s.dstate : bwd_block_states(s.dstate);
     for (int64_t n0 = 0; n0 < s.dstate; n0 += q.nb) {
         q.n0 = n0;
+        q.ck_n0 = q.have_ck ? n0 : 0;
         q.nb = bwd_next_block(s.dstate - n0);
         q.first = n0 == 0;
         q.last = n0 + q.nb == s.dstate;

@@ -98,7 +98,7 @@ __device__ __forceinline__ void pack4_bf16(uint32_t (&v)[4]) {
 }
 
 // VEC: B and C rows 4-element aligned, staged with one vector load per 4 steps
-template <typename T, bool SOFTPLUS, bool HAS_Z, bool VEC>
+template <typename T, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK>
 __global__ __launch_bounds__(64 * kLsWaves) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_ls_kernel(ScanParams p) {
     __shared__ __align__(16) float s_p[kLsWaves * 4 * kLsChanP];
@@ -143,6 +143,12 @@ void scan_ls_kernel(ScanParams p) {
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         p.y + b * p.sy_b + d0c * p.sy_d, 0, (int)(((dl - d0c) * p.sy_d + L) * 4), kLsWord3);
     const uint32_t oy_l = valid ? (dr * (uint32_t)p.sy_d + 2 * n) * 4u : kLsDropBase;
+    // saved states (CK): the state before every 16-step segment, (row, segment, state) from the
+    // wave's first row, stored at the end of each chunk beside y
+    const __amdgpu_buffer_rsrc_t ckr = __builtin_amdgcn_make_buffer_rsrc(
+        CK ? p.ck + (b * p.dim + d0c) * p.ck_nseg * 16 : p.y, 0,
+        CK ? (int)((dl - d0c + 1) * p.ck_nseg * 16 * 4) : 0, kLsWord3);
+    const uint32_t ock = valid ? (dr * (uint32_t)p.ck_nseg * 16 + n) * 4u : kLsDropBase;
 
     // raw bits of one element; widened to fp32 (widen) only where the value is used, so that a
     // load inside a branch is not waited for inside it
@@ -271,7 +277,10 @@ void scan_ls_kernel(ScanParams p) {
         fetch(kn, next_tail, nx);
         read_bc(buf, 0);
         read_bc(buf, 1);
+        // the states before steps t0 and t0 + 16 (segments 2k and 2k + 1), stored with y
+        const float hk0 = r.h;
         ls_steps<0, 0, 0>(r);
+        const float hk1 = r.h;
         ls_steps<1, 1, 0>(r);
         // the next chunk's B / C into the other buffer (its last readers passed the barrier above)
         *reinterpret_cast<float4*>(sdst + (buf ^ 1) * kBufStride) =
@@ -303,6 +312,12 @@ void scan_ls_kernel(ScanParams p) {
             const uint32_t a1 = t + 1 < (uint32_t)L ? oy_l + 4u : kLsDropBase;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o0), yr, (int)a0, (int)(t0 * 4u), 0);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o1), yr, (int)a1, (int)(t0 * 4u), 0);
+        }
+        if constexpr (CK) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hk0), ckr, (int)ock, (int)(t0 * 4u), 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hk1), ckr,
+                                                  (int)(t0 + kLsH < (uint32_t)L ? ock + 64u : kLsDropBase),
+                                                  (int)(t0 * 4u), 0);
         }
     }
     if (p.last_state && valid) p.last_state[b * p.sls_b + d * p.sls_d + n] = r.h;
@@ -344,7 +359,7 @@ __device__ __forceinline__ void lw_steps(LwRegs<N>& r) {
     }
 }
 
-template <typename T, int N, bool SOFTPLUS, bool HAS_Z, bool VEC>
+template <typename T, int N, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK>
 __global__ __launch_bounds__(64 * kLsWaves) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_ls_wide_kernel(ScanParams p) {
     static_assert(N == 32 || N == 64, "wide lane-per-state kernel: 32 or 64 states");
@@ -390,6 +405,11 @@ void scan_ls_wide_kernel(ScanParams p) {
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         p.y + b * p.sy_b + d0c * p.sy_d, 0, (int)(((dl - d0c) * p.sy_d + L) * 4), kLsWord3);
     const uint32_t oy_l = (valid && first_row) ? (dr * (uint32_t)p.sy_d + j) * 4u : kLsDropBase;
+    // saved states (CK), as in the 16-state kernel: one segment per chunk
+    const __amdgpu_buffer_rsrc_t ckr = __builtin_amdgcn_make_buffer_rsrc(
+        CK ? p.ck + (b * p.dim + d0c) * p.ck_nseg * N : p.y, 0,
+        CK ? (int)((dl - d0c + 1) * p.ck_nseg * N * 4) : 0, kLsWord3);
+    const uint32_t ock = valid ? (dr * (uint32_t)p.ck_nseg * N + n) * 4u : kLsDropBase;
 
     auto load_el = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff) __attribute__((always_inline)) {
         if constexpr (sizeof(T) == 2)
@@ -518,6 +538,7 @@ void scan_ls_wide_kernel(ScanParams p) {
         Raw nx;
         fetch(kn, next_tail, nx);
         read_bc(buf);
+        const float hk = r.h;  // the state before step t0 (segment k), stored with y
         lw_steps<N, 0>(r);
         stage_store(buf ^ 1, sv);
         const float u0 = uv, g0 = gz;
@@ -543,6 +564,8 @@ void scan_ls_wide_kernel(ScanParams p) {
             const uint32_t a = t0 + j < (uint32_t)L ? oy_l : kLsDropBase;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), yr, (int)a, (int)(t0 * 4u), 0);
         }
+        if constexpr (CK)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hk), ckr, (int)ock, (int)(t0 * (N / 4)), 0);
     }
     if (p.last_state && valid) p.last_state[b * p.sls_b + d * p.sls_d + n] = r.h;
 }
@@ -562,17 +585,18 @@ inline bool ls_eligible(const ScanParams& q, int64_t es) {
     if (!rows_ok(q.y, q.sy_d, 4)) return false;
     if (((q.dstate - 1) * q.sB_n + q.len) * es >= lim || ((q.dstate - 1) * q.sC_n + q.len) * es >= lim) return false;
     if (q.batch * q.dim > 0x7fffffff) return false;
+    if (q.ck && q.ck_nseg * 256 >= lim) return false;  // a wave's saved states: 64 lanes x nseg floats
     return true;
 }
 
-template <typename T, bool SP, bool HZ, bool VEC>
+template <typename T, bool SP, bool HZ, bool VEC, bool CK>
 int launch_ls_cfg(const ScanParams& q, hipStream_t stream) {
     const void* fn;
     int64_t per_group;
     switch (q.dstate) {
-        case 16: fn = reinterpret_cast<const void*>(&scan_ls_kernel<T, SP, HZ, VEC>); per_group = 16; break;
-        case 32: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 32, SP, HZ, VEC>); per_group = 8; break;
-        default: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 64, SP, HZ, VEC>); per_group = 4; break;
+        case 16: fn = reinterpret_cast<const void*>(&scan_ls_kernel<T, SP, HZ, VEC, CK>); per_group = 16; break;
+        case 32: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 32, SP, HZ, VEC, CK>); per_group = 8; break;
+        default: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 64, SP, HZ, VEC, CK>); per_group = 4; break;
     }
     void* args[] = {const_cast<ScanParams*>(&q)};
     const int64_t groups = q.batch * ((q.dim + per_group - 1) / per_group);
@@ -581,14 +605,20 @@ int launch_ls_cfg(const ScanParams& q, hipStream_t stream) {
                : MAMBA_SCAN_ERR_LAUNCH;
 }
 
+template <typename T, bool SP, bool HZ, bool VEC>
+int launch_ls_ck(const ScanParams& q, hipStream_t stream) {
+    // saving the segment states is a separate instantiation: the plain forward issues no stores for it
+    return q.ck ? launch_ls_cfg<T, SP, HZ, VEC, true>(q, stream) : launch_ls_cfg<T, SP, HZ, VEC, false>(q, stream);
+}
+
 template <typename T, bool SP, bool HZ>
 int launch_ls_vec(const ScanParams& q, hipStream_t stream) {
     // B / C rows 4-element aligned: one vector load per 4 staged steps
     const auto al = [](const void* ptr, int64_t sb, int64_t sn) {
         return reinterpret_cast<uintptr_t>(ptr) % (4 * sizeof(T)) == 0 && sb % 4 == 0 && sn % 4 == 0;
     };
-    if (al(q.B, q.sB_b, q.sB_n) && al(q.C, q.sC_b, q.sC_n)) return launch_ls_cfg<T, SP, HZ, true>(q, stream);
-    return launch_ls_cfg<T, SP, HZ, false>(q, stream);
+    if (al(q.B, q.sB_b, q.sB_n) && al(q.C, q.sC_b, q.sC_n)) return launch_ls_ck<T, SP, HZ, true>(q, stream);
+    return launch_ls_ck<T, SP, HZ, false>(q, stream);
 }
 
 template <typename T>

@@ -25,6 +25,7 @@ F32, BF16 = 0, 1
 DELTA_SOFTPLUS = 1 << 0
 RETURN_LAST_STATE = 1 << 1
 ZOH_B = 1 << 2
+SAVE_CHECKPOINTS = 1 << 3
 FORCE_GENERIC = 1 << 8
 FORCE_TILED = 1 << 9
 FORCE_LANES = 1 << 10
@@ -52,7 +53,8 @@ class Strides(ctypes.Structure):
 class BwdPtrs(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("u", "delta", "z", "B", "C", "A", "D", "delta_bias", "h0", "dy",
                                   "dlast_state", "du", "ddelta", "dz", "dB", "dC", "dA", "dD",
-                                  "ddelta_bias", "dh0", "workspace")] + [("workspace_bytes", _I64)]
+                                  "ddelta_bias", "dh0", "workspace")] + [("workspace_bytes", _I64),
+                                                                          ("checkpoints", _P)]
 
 
 class UpPtrs(ctypes.Structure):
@@ -130,7 +132,7 @@ def _s3(x, fallback=(0, 0, 1)):
 
 def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
                       return_last_state=False, h0=None, *, kernel=None, out=None,
-                      last_state_out=None, zoh_b=False):
+                      last_state_out=None, zoh_b=False, checkpoints_out=None):
     """y = selective_scan(...), fp32 (batch, dim, L); with ``return_last_state`` also the final
     state (batch, dim, N) fp32. ``zoh_b``: B discretised by zero-order hold,
     (e^{dt A} - 1) / A * B, instead of dt * B (forward only).
@@ -138,7 +140,9 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     u, delta, z: (batch, dim, L); B, C: (batch, N, L); one storage dtype for all five
     (torch.float32 or torch.bfloat16). A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N);
     these are taken in fp32. ``kernel``: None (library picks), "generic", "tiled" or "lanes"
-    (one lane per (channel, state); 16, 32 or 64 states).
+    (one lane per (channel, state); 16, 32 or 64 states). ``checkpoints_out``: a contiguous fp32
+    (batch, dim, ceil(L/16), N) tensor that receives the state before every 16-step segment, for
+    ``selective_scan_bwd(checkpoints=...)`` (lane-per-state kernels only).
     """
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):
@@ -189,10 +193,15 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
 
     shape = Shape(batch, dim, L, N)
     dtype = BF16 if u.dtype == torch.bfloat16 else F32
-    ws_bytes = lib.mamba_scan_workspace_bytes(ctypes.byref(shape), dtype, flags)
-    if ws_bytes < 0:
-        raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
-    ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+    if checkpoints_out is not None:
+        _check_checkpoints(checkpoints_out, batch, dim, L, N, dev)
+        flags |= SAVE_CHECKPOINTS
+        ws, ws_bytes = checkpoints_out, checkpoints_out.numel() * 4
+    else:
+        ws_bytes = lib.mamba_scan_workspace_bytes(ctypes.byref(shape), dtype, flags)
+        if ws_bytes < 0:
+            raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
+        ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
 
     st = Strides()
     st.u, st.delta, st.z = _s3(u), _s3(delta), _s3(z)
@@ -212,18 +221,31 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
         if rc in (-1, -2, -3, -4, -5, -6, -8):
             raise ValueError(str(err)) from err
         raise err
-    if ws is not None:
+    if ws is not None and checkpoints_out is None:
         ws.record_stream(torch.cuda.current_stream(dev))
     return (y, ls) if return_last_state else y
 
 
+def checkpoint_shape(batch, dim, L, N):
+    """Shape of the saved segment states: (batch, dim, ceil(L/16), N)."""
+    return (batch, dim, (L + 15) // 16, N)
+
+
+def _check_checkpoints(ck, batch, dim, L, N, dev):
+    if (ck.dtype != torch.float32 or ck.device != dev or tuple(ck.shape) != checkpoint_shape(batch, dim, L, N)
+            or not ck.is_contiguous()):
+        raise ValueError(f"checkpoints must be a contiguous float32 tensor of shape "
+                         f"{checkpoint_shape(batch, dim, L, N)} on u's device")
+
+
 def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False,
-                       h0=None, dlast_state=None, want_dh0=True):
+                       h0=None, dlast_state=None, want_dh0=True, checkpoints=None):
     """Gradients of the scan (``mamba_scan_bwd``) for incoming gradients dy (batch, dim, L) and,
     optionally, dlast_state (batch, dim, N). Inputs as for ``selective_scan_fn``; all tensors are
     made contiguous first. Returns a dict of fp32 gradients: u, delta, B, C, A, and z, D,
     delta_bias when given, h0 when ``want_dh0`` (the gradient of the initial state, which is zero
-    when h0 is None).
+    when h0 is None). ``checkpoints``: the segment states that ``selective_scan_fn(checkpoints_out=)``
+    saved for the same inputs; the backward then does not recompute them.
     """
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):
@@ -275,6 +297,9 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
                    _ptr(h0), _ptr(dy), _ptr(dlast_state), _ptr(g["u"]), _ptr(g["delta"]), _ptr(g.get("z")),
                    _ptr(g["B"]), _ptr(g["C"]), _ptr(g["A"]), _ptr(g.get("D")), _ptr(g.get("delta_bias")),
                    _ptr(g.get("h0")), _ptr(ws), int(ws_bytes))
+    if checkpoints is not None:
+        _check_checkpoints(checkpoints, batch, dim, L, N, dev)
+        ptrs.checkpoints = _ptr(checkpoints)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.mamba_scan_bwd(ctypes.byref(ptrs), ctypes.byref(shape), dtype, flags, stream)
@@ -290,26 +315,38 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
 class SelectiveScan(torch.autograd.Function):
     """y (and last_state) = selective_scan(...) with a backward pass through ``mamba_scan_bwd``.
 
-    Only the inputs are saved; the backward recomputes the states ("手把手用PyTorch实现Mamba的SSM层…"
-    §4.2). Gradients come back in each input's dtype.
+    The inputs are saved, and, where the lane-per-state forward runs (16, 32 or 64 states), the
+    state before every 16-step segment; the backward recomputes the states inside each segment
+    from there ("手把手用PyTorch实现Mamba的SSM层…" §4.2), or from the start without them.
+    Gradients come back in each input's dtype.
     """
 
     @staticmethod
     def forward(ctx, u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus):
-        y, ls = selective_scan_fn(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
-                                  delta_softplus=delta_softplus, return_last_state=True, h0=h0)
-        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0)
+        kw = dict(D=D, z=z, delta_bias=delta_bias, delta_softplus=delta_softplus, return_last_state=True, h0=h0)
+        ck = None
+        if A.shape[1] in (16, 32, 64) and u.dtype in (torch.float32, torch.bfloat16):
+            ck = torch.empty(checkpoint_shape(*u.shape, A.shape[1]), dtype=torch.float32, device=u.device)
+            try:
+                y, ls = selective_scan_fn(u, delta, A, B, C, checkpoints_out=ck, **kw)
+            except ValueError as e:
+                if not isinstance(e.__cause__, MambaScanError) or e.__cause__.code != -8:
+                    raise
+                ck = None  # shape outside the lane-per-state kernels: no saved states
+        if ck is None:
+            y, ls = selective_scan_fn(u, delta, A, B, C, **kw)
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0, ck)
         ctx.delta_softplus = delta_softplus
         return y, ls
 
     @staticmethod
     def backward(ctx, gy, gls):
-        u, delta, A, B, C, D, z, delta_bias, h0 = ctx.saved_tensors
+        u, delta, A, B, C, D, z, delta_bias, h0, ck = ctx.saved_tensors
         if gy is None:
             gy = torch.zeros(u.shape, dtype=torch.float32, device=u.device)
         g = selective_scan_bwd(u, delta, A, B, C, gy, D=D, z=z, delta_bias=delta_bias,
                                delta_softplus=ctx.delta_softplus, h0=h0, dlast_state=gls,
-                               want_dh0=h0 is not None and ctx.needs_input_grad[8])
+                               want_dh0=h0 is not None and ctx.needs_input_grad[8], checkpoints=ck)
 
         def cast(name, like):
             return None if like is None or name not in g else g[name].to(like.dtype)

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 5
+    assert scan.load_library().mamba_scan_abi_version() == 6
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -70,6 +70,13 @@ def _set(obj, field, value):
     def f(ctx):
         setattr(ctx[obj], field, value)
     return f
+
+
+def _ck_ws(ctx, nbytes, offset=0, extra=0):
+    """SAVE_CHECKPOINTS with a (fake) workspace of nbytes at a free address."""
+    ctx["flags"] = scan.DELTA_SOFTPLUS | scan.SAVE_CHECKPOINTS | extra
+    ctx["ptrs"].workspace = (1 << 40) + (20 << 32) + offset
+    ctx["ptrs"].workspace_bytes = nbytes
 
 
 def _flags(value):
@@ -110,6 +117,15 @@ CASES = [
     ("y_aliases_u", _set("ptrs", "y", (1 << 40) + (1 << 32) + 64), -6),
     ("y_aliases_A", _set("ptrs", "A", (1 << 40) + (10 << 32) + 4), -6),
     ("workspace_size_without_ptr", _set("ptrs", "workspace_bytes", 128), -6),
+    # saved segment states: a workspace of (batch, dim, ceil(len/16), dstate) floats, lane kernels only
+    ("checkpoints_without_workspace", _flags(scan.DELTA_SOFTPLUS | scan.SAVE_CHECKPOINTS), -9),
+    ("checkpoints_workspace_too_small", lambda c: _ck_ws(c, 2 * 3 * 3 * 16 * 4 - 4), -9),
+    ("checkpoints_misaligned", lambda c: _ck_ws(c, 1 << 20, offset=2), -6),
+    ("checkpoints_with_tiled", lambda c: _ck_ws(c, 1 << 20, extra=scan.FORCE_TILED), -8),
+    ("checkpoints_with_generic", lambda c: _ck_ws(c, 1 << 20, extra=scan.FORCE_GENERIC), -8),
+    ("checkpoints_24_states", lambda c: (_ck_ws(c, 1 << 20), setattr(c["shape"], "dstate", 24)), -8),
+    ("checkpoints_with_zoh", lambda c: _ck_ws(c, 1 << 20, extra=scan.ZOH_B), -8),
+    ("checkpoints_alias_y", lambda c: (_ck_ws(c, 1 << 20), setattr(c["ptrs"], "workspace", c["ptrs"].y)), -6),
 ]
 
 
@@ -137,6 +153,12 @@ def test_strerror_and_workspace_query():
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok), scan.BF16, 0) >= 0
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(scan.Shape(0, 1, 1, 1)), 0, 0) == -2
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok), 3, 0) == -4
+    # saved segment states: (batch, dim, ceil(len/16), dstate) fp32
+    for shp in ((2, 3, 40, 16), (1, 5, 16, 32), (3, 2, 17, 64)):
+        b, d, L, n = shp
+        assert lib.mamba_scan_workspace_bytes(ctypes.byref(scan.Shape(*shp)), scan.BF16,
+                                              scan.SAVE_CHECKPOINTS) == b * d * ((L + 15) // 16) * n * 4
+        assert scan.checkpoint_shape(b, d, L, n) == (b, d, (L + 15) // 16, n)
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(scan.Shape(1, 1, 1, 300)), 0, 0) == -5
 
 
@@ -178,6 +200,8 @@ BWD_CASES = [
     ("output_aliases_input", lambda c: setattr(c["ptrs"], "du", c["ptrs"].dy), -6),
     ("outputs_alias", lambda c: setattr(c["ptrs"], "dB", c["ptrs"].dC), -6),
     ("misaligned_workspace", lambda c: setattr(c["ptrs"], "workspace", c["ptrs"].workspace + 16), -6),
+    ("misaligned_checkpoints", lambda c: setattr(c["ptrs"], "checkpoints", c["ptrs"].checkpoints + 2), -6),
+    ("checkpoints_alias_output", lambda c: setattr(c["ptrs"], "checkpoints", c["ptrs"].dB), -6),
 ]
 
 

@@ -1,0 +1,135 @@
+"""Segment states saved by the forward pass (MAMBA_SCAN_SAVE_CHECKPOINTS) and the backward pass that
+starts from them instead of recomputing them ("手把手用PyTorch实现Mamba的SSM层…" §4.2 names both
+ways: store the states, or recompute them).
+
+  * checkpoint k is the state before step 16 k: the oracle's last state of the first 16 k steps
+    (h0 for k = 0), to the forward bar, and the GPU's own last state of that prefix, bit for bit;
+  * the backward given them matches the fp64 backward oracle to the backward bar (2e-3), and the
+    backward that recomputes them to 1e-5;
+  * the autograd function saves them where the lane-per-state forward runs and falls back to
+    recomputation where it does not.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+import oracle
+from selective_state_space_29_amd import scan
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (batch, dim, N, L, dtype, h0)
+    (2, 12, 16, 70, "bf16", False),   # ragged: last segment of 6 steps, last 32-step chunk of 6
+    (1, 5, 16, 64, "f32", True),      # exact chunks, initial state
+    (2, 9, 32, 47, "bf16", True),
+    (1, 4, 64, 33, "f32", False),
+    (1, 3, 16, 1, "bf16", False),     # one step: one checkpoint, the initial state
+]
+IDS = [f"b{c[0]}d{c[1]}n{c[2]}l{c[3]}{c[4]}{'h0' if c[5] else ''}" for c in CASES]
+
+
+def _dev(x):
+    return {k: gu.to_dev(v) if isinstance(v, np.ndarray) else v for k, v in x.items()}
+
+
+def _forward_with_checkpoints(x, h0):
+    g = _dev(x)
+    batch, dim, L = x["u"].shape
+    N = x["A"].shape[1]
+    ck = torch.full(scan.checkpoint_shape(batch, dim, L, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    y, ls = scan.selective_scan_fn(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                                   delta_bias=g["delta_bias"], delta_softplus=True, return_last_state=True,
+                                   h0=None if h0 is None else gu.to_dev(h0), checkpoints_out=ck)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ls.cpu().numpy(), ck
+
+
+@pytest.mark.parametrize("idx", range(len(CASES)), ids=IDS)
+def test_checkpoints_are_the_prefix_states(idx):
+    batch, dim, N, L, dtype, with_h0 = CASES[idx]
+    print(f"checkpoint case {CASES[idx]}", flush=True)
+    x = gu.case(8000 + idx, batch, dim, N, L, dtype=dtype)
+    h0 = np.random.default_rng(idx).standard_normal((batch, dim, N)).astype(np.float32) if with_h0 else None
+    y, ls, ck = _forward_with_checkpoints(x, h0)
+    ck = ck.cpu().numpy()
+    # the outputs are those of the forward without checkpoints, bit for bit
+    y2, ls2 = gu.gpu_scan(x, h0=h0)
+    assert np.array_equal(y, y2) and np.array_equal(ls, ls2)
+    tol = gu.FP32_TOL if dtype == "f32" else gu.BF16_TOL
+    start = np.zeros((batch, dim, N)) if h0 is None else h0
+    assert np.array_equal(ck[:, :, 0, :], start.astype(np.float32))
+    for k in range(1, ck.shape[2]):
+        pre = {kk: (np.ascontiguousarray(v[..., :16 * k]) if kk in ("u", "delta", "z", "B", "C") else v)
+               for kk, v in x.items()}
+        _, lr = gu.oracle_scan(pre, h0=h0)
+        err = gu.rel_err(ck[:, :, k, :], lr)
+        assert err <= tol, f"checkpoint {k}: {err:.3g}"
+        _, lg = gu.gpu_scan(pre, h0=h0)
+        assert np.array_equal(ck[:, :, k, :], lg), f"checkpoint {k} differs from the prefix scan"
+
+
+@pytest.mark.parametrize("idx", range(len(CASES)), ids=IDS)
+def test_backward_from_checkpoints(idx):
+    batch, dim, N, L, dtype, with_h0 = CASES[idx]
+    print(f"checkpoint backward case {CASES[idx]}", flush=True)
+    x = gu.case(8100 + idx, batch, dim, N, L, dtype=dtype)
+    rng = np.random.default_rng(100 + idx)
+    h0 = rng.standard_normal((batch, dim, N)).astype(np.float32) if with_h0 else None
+    dy = rng.standard_normal((batch, dim, L)).astype(np.float32)
+    dlast = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    _, _, ck = _forward_with_checkpoints(x, h0)
+    g = _dev(x)
+    kw = dict(D=g["D"], z=g["z"], delta_bias=g["delta_bias"], delta_softplus=True,
+              h0=None if h0 is None else gu.to_dev(h0), dlast_state=gu.to_dev(dlast), want_dh0=True)
+    with_ck = scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], gu.to_dev(dy), checkpoints=ck, **kw)
+    without = scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], gu.to_dev(dy), **kw)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(
+        x["u"], x["delta"], x["A"], x["B"], x["C"], dy.astype(np.float64), D=x["D"], z=x["z"],
+        delta_bias=x["delta_bias"], delta_softplus=True, h0=None if h0 is None else h0.astype(np.float64),
+        glast=dlast.astype(np.float64))
+    same = True
+    for k, v in with_ck.items():
+        a, b = v.cpu().numpy(), without[k].cpu().numpy()
+        assert np.all(np.isfinite(a)), k
+        if k in ref:
+            assert gu.rel_err(a, ref[k]) <= 2e-3, f"d{k} against the oracle"
+        assert gu.rel_err(a, b) <= 1e-5, f"d{k} with and without checkpoints"
+        same = same and np.array_equal(a, b)
+    print(f"   bit-identical to the recomputing backward: {same}", flush=True)
+
+
+def test_autograd_saves_checkpoints_where_lanes_run():
+    """selective_scan (autograd): 16 states go through the saved states, 24 through recomputation;
+    both give the gradients of selective_scan_bwd without checkpoints."""
+    for N, seed in ((16, 8200), (24, 8201)):
+        x = gu.case(seed, 2, 6, N, 40, dtype="f32")
+        g = _dev(x)
+        leaves = {k: g[k].clone().requires_grad_(True) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+        y, ls = scan.selective_scan(leaves["u"], leaves["delta"], leaves["A"], leaves["B"], leaves["C"],
+                                    D=leaves["D"], z=leaves["z"], delta_bias=leaves["delta_bias"],
+                                    delta_softplus=True, return_last_state=True)
+        dy = torch.randn_like(y)
+        dl = torch.randn_like(ls)
+        torch.autograd.backward([y, ls], [dy, dl])
+        ref = scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"], z=g["z"],
+                                      delta_bias=g["delta_bias"], delta_softplus=True, dlast_state=dl,
+                                      want_dh0=False)
+        torch.cuda.synchronize()
+        for k, leaf in leaves.items():
+            err = gu.rel_err(leaf.grad.cpu().numpy(), ref[k].cpu().numpy())
+            assert err <= 1e-5, f"N={N} d{k}: {err:.3g}"
+
+
+def test_checkpoint_argument_checks():
+    x = gu.case(8300, 1, 4, 16, 40, dtype="f32")
+    g = _dev(x)
+    bad = torch.empty((1, 4, 2, 16), dtype=torch.float32, device="cuda:0")  # needs 3 segments
+    with pytest.raises(ValueError, match="checkpoints"):
+        scan.selective_scan_fn(g["u"], g["delta"], g["A"], g["B"], g["C"], checkpoints_out=bad)
+    ck = torch.empty(scan.checkpoint_shape(1, 4, 40, 16), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ValueError, match=r"\(-8\)"):
+        scan.selective_scan_fn(g["u"], g["delta"], g["A"], g["B"], g["C"], checkpoints_out=ck, kernel="tiled")
