@@ -133,3 +133,34 @@ def test_checkpoint_argument_checks():
     ck = torch.empty(scan.checkpoint_shape(1, 4, 40, 16), dtype=torch.float32, device="cuda:0")
     with pytest.raises(ValueError, match=r"\(-8\)"):
         scan.selective_scan_fn(g["u"], g["delta"], g["A"], g["B"], g["C"], checkpoints_out=ck, kernel="tiled")
+
+
+@pytest.mark.parametrize("wid", [3, 4, 5])
+def test_full_size_backward_from_checkpoints_is_bit_identical(wid):
+    """At the full workload shapes (Mamba-130m layer; genomic L = 100 000; 64 states over four
+    blocks of 16): the backward from the forward's saved states gives the recomputing backward's
+    gradients bit for bit, so the parity of the latter (workloads 3 in full, 5 on sampled
+    channels) carries over."""
+    from selective_state_space_29_amd import workloads
+
+    w = workloads.WORKLOADS[wid]
+    print(f"checkpoint backward, workload {wid}: {w.name}", flush=True)
+    x = workloads.make_inputs(w)
+    g = _dev(x)
+    del x
+    gen = torch.Generator(device="cuda:0").manual_seed(29600 + wid)
+    dy = torch.randn((w.batch, w.dim, w.seqlen), device="cuda:0", generator=gen)
+    dl = torch.randn((w.batch, w.dim, w.dstate), device="cuda:0", generator=gen)
+    ck = torch.empty(scan.checkpoint_shape(w.batch, w.dim, w.seqlen, w.dstate), dtype=torch.float32,
+                     device="cuda:0")
+    scan.selective_scan_fn(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                           delta_bias=g["delta_bias"], delta_softplus=True, checkpoints_out=ck)
+    kw = dict(D=g["D"], z=g["z"], delta_bias=g["delta_bias"], delta_softplus=True, dlast_state=dl,
+              want_dh0=True)
+    a = scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, checkpoints=ck, **kw)
+    del ck
+    b = scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, **kw)
+    torch.cuda.synchronize()
+    for k in a:
+        assert bool(torch.isfinite(a[k]).all()), k
+        assert torch.equal(a[k], b[k]), f"d{k} differs"
