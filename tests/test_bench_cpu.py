@@ -34,6 +34,25 @@ def test_traffic_is_reported_only_for_the_profiled_sources():
     assert bench.measured_traffic(workloads.WORKLOADS[4], "auto") is None
 
 
+def test_backward_traffic_records_match_the_sources():
+    """The backward's rocprofv3 traffic records (recomputing / from saved states) were taken on
+    the current scan_bwd sources and are reported for the Mamba-130m workload only."""
+    import json
+
+    import bench
+    from selective_state_space_29_amd import workloads
+
+    w3 = workloads.WORKLOADS[3]
+    for ck in (False, True):
+        with open(bench.BWD_TRAFFIC_RECORDS[ck][0]) as f:
+            rec = json.load(f)
+        assert rec["source_sha256"] == bench.kernel_source_hash(ck, bench.BWD_TRAFFIC_RECORDS)
+        assert bench.measured_bwd_traffic(w3, ck) == rec["traffic_bytes_per_launch"] > 0
+        assert bench.measured_bwd_traffic(workloads.WORKLOADS[5], ck) is None
+    # starting from the saved states neither writes nor re-reads them
+    assert bench.measured_bwd_traffic(w3, True) < bench.measured_bwd_traffic(w3, False)
+
+
 def test_sampled_indices_exist_for_every_workload():
     """The rows / channels the bench reads back from the device exist in every workload (a
     device-side index_select does not check its indices)."""
