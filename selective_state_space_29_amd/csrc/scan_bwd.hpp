@@ -290,8 +290,14 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
             }
         }
 
+        // the segment's per-(channel, step) results and dB / dC sums, written once both halves are
+        // done: a channel's 16 steps (64 bytes) by two adjacent stores instead of 32 bytes per half
+        float o_u[2], o_x[2], o_z[2], o_bc[2];
+        bool o_ok[2], o_bcok[2];
 #pragma unroll
         for (int half = 1; half >= 0; --half) {
+            o_ok[half] = false;
+            o_bcok[half] = false;
             if (wave_live) {
                 float gBc[S][SUB], gCc[S][SUB];
 #pragma unroll
@@ -352,10 +358,11 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                         gxs += p.ddelta[prow + t];
                         if constexpr (HAS_Z) ys += p.dz[prow + t];
                     }
-                    p.du[prow + t] = gu;
-                    p.ddelta[prow + t] = gxs;
+                    o_ok[half] = true;
+                    o_u[half] = gu;
+                    o_x[half] = gxs;
                     if constexpr (HAS_Z)  // sum_n C h until the last block, then the gate's gradient
-                        p.dz[prow + t] = last ? s_seg[F_GZ][o] * __builtin_fmaf(pskip, uu, ys) : ys;
+                        o_z[half] = last ? s_seg[F_GZ][o] * __builtin_fmaf(pskip, uu, ys) : ys;
                     if (last) gbacc += gxs;  // dbias sums the finished ddelta
                 }
             }
@@ -375,11 +382,27 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                     acc += v.z;
                     acc += v.w;
                 }
-                const int n = w * S + s;
-                if (n < p.nb)
-                    p.bcpart[(((grp * p.batch + b) * 2 + q) * N + p.n0 + n) * p.lp + k * SEG + half * SUB + tt] = acc;
+                o_bcok[half] = w * S + s < p.nb;
+                o_bc[half] = acc;
             }
             __syncthreads();
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t t = k * SEG + half * SUB + k8;
+            if (o_ok[half]) {
+                p.du[prow + t] = o_u[half];
+                p.ddelta[prow + t] = o_x[half];
+                if constexpr (HAS_Z) p.dz[prow + t] = o_z[half];
+            }
+            if (o_bcok[half]) {
+                const int tt = tid % SUB;
+                const int s = (tid / SUB) % S;
+                const int w = (tid / (SUB * S)) % W;
+                const int q = tid / (SUB * S * W);
+                p.bcpart[(((grp * p.batch + b) * 2 + q) * N + p.n0 + w * S + s) * p.lp + k * SEG + half * SUB + tt] =
+                    o_bc[half];
+            }
         }
     }
 
