@@ -472,7 +472,7 @@ def backward_bench(args):
                                    delta_bias=g["delta_bias"], delta_softplus=w.softplus,
                                    return_last_state=True, out=y, last_state_out=ls, checkpoints_out=ck)
 
-        fwd_us = graph_timed(fwd, 4, 1, torch.cuda.current_stream(dev), reps=7, warm_reps=3)
+        fwd_us = graph_timed(fwd, 50, 5, torch.cuda.current_stream(dev), reps=7, warm_reps=3)
         fwd(0)
         torch.cuda.synchronize()
         fwd_ck = {"median_call_us": round(float(np.median(fwd_us)), 2),
