@@ -25,14 +25,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # VALU peak: 256 CUs x 128 fp32 lanes/clk x 2.4 GHz = 78.6 T lane-slots/s, i.e. the published
-# 157.3 TFLOP/s fp32 vector figure with one FMA = 2 flops. Work is counted in issue slots (one
-# lane-op = 1 slot, a transcendental = 4 slots at quarter rate) and reported as 2 flops per slot.
+# 157.3 TFLOP/s fp32 vector figure with one FMA = 2 flops.
 VALU_PEAK_TFLOPS = 157.3
-SLOTS_PER_ELEMENT = 8      # mul (dt*A), exp, mul (dt*u*B), fma (h), fma (y)
-SLOTS_PER_ROW_STEP = 30    # softplus, dt*u, bias, skip, silu gate
-# zero-order-hold B adds, per element: dt*A, the 4-term series and dt*p, dA - 1 and * 1/A, the
-# compare and select, and * u
-SLOTS_PER_ELEMENT_ZOH = SLOTS_PER_ELEMENT + 11
+# The method's arithmetic (forward): per element (b, d, t, n) one exp and dt*A, dt*u*B (2 mul),
+# the state update and the output term (2 FMA) = 6 flops; per row-step (b, d, t) about 10 more
+# fp32 operations (bias, the softplus besides its exp and log, dt*u, the skip FMA, the silu gate
+# besides its exp and reciprocal, the gate multiply) = 12 flops, and 2 transcendentals for the
+# softplus (exp, log) or 1 for exp mode, plus 2 for the gate (exp, reciprocal).
+FLOPS_PER_ELEMENT = 6
+VALU_OPS_PER_ELEMENT = 4
+FLOPS_PER_ROW_STEP = 12
+VALU_OPS_PER_ROW_STEP = 10
 SLOTS_PER_ELEMENT_BWD = 26     # backward: 2 x 7 forward recurrence + 10 reverse + 2 channel sums
 SLOTS_PER_ROW_STEP_BWD = 100
 SLOTS_PER_ELEMENT_FWD_RECURRENCE = 7  # one forward recurrence step of the backward's count
@@ -50,6 +53,14 @@ BWD_TRAFFIC_RECORDS = {
            ("common.hpp", "scan_bwd.hpp")),
 }
 RATES_LIB = os.path.join(ROOT, "selective_state_space_29_amd", "probe", "libmscan_rates.so")
+# the sources each forward kernel is built from (a profile or counter record names their hash)
+KERNEL_SOURCES = {
+    "generic": (None, ("common.hpp", "scan_generic.hpp")),
+    "tiled": (None, ("common.hpp", "scan_tiled.hpp")),
+    "lanes": (None, ("common.hpp", "scan_ls.hpp")),
+    "chunked": (None, ("common.hpp", "scan_ls.hpp", "scan_lp.hpp")),
+}
+WARM_MS = 400.0  # untimed sustained load before the timed graph replays
 
 
 def parse():
@@ -58,7 +69,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--kernel", choices=["auto", "generic", "tiled", "lanes"], default="auto")
+    ap.add_argument("--kernel", choices=["auto", "generic", "tiled", "lanes", "chunked"], default="auto")
     ap.add_argument("--sets", type=int, default=3, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
@@ -109,11 +120,15 @@ def copy_calibration(mb, steps, warmup):
 
 # The sources of the kernel whose HBM traffic the counter record measured (the forward tiled
 # kernel): the record only applies while these are unchanged.
-def resolved_kernel(w, kernel, zoh=False):
-    """The forward kernel the library runs for this workload: its default picks the
-    lane-per-state kernels for 16, 32 or 64 states (Euler B), else the tiled one."""
-    if kernel != "auto":
+def resolved_kernel(w, kernel, zoh=False, cus=256):
+    """The forward kernel the library's default picks for this workload on a GPU with `cus`
+    compute units (the bench itself asks the library, scan.forward_kernel): the chunked kernel
+    for 16 states, >= 1024 steps and fewer than 2 lane-per-state waves per SIMD; else the
+    lane-per-state kernels for 16, 32 or 64 states (Euler B); else the tiled one."""
+    if kernel not in ("auto", None):
         return kernel
+    if w.dstate == 16 and not zoh and w.seqlen >= 1024 and w.batch * ((w.dim + 3) // 4) < 8 * cus:
+        return "chunked"
     return "lanes" if w.dstate in (16, 32, 64) and not zoh else "tiled"
 
 
@@ -132,6 +147,8 @@ def measured_traffic(w, kernel, zoh=False):
     kernel that runs, or None when there is none for it, it was taken on other kernel sources,
     or on another workload."""
     k = resolved_kernel(w, kernel, zoh)
+    if k == "chunked":
+        return None
     if w.wid != 3 or zoh or k not in TRAFFIC_RECORDS:
         return None
     try:
@@ -159,12 +176,13 @@ def measured_bwd_traffic(w, from_checkpoints):
     return rec.get("traffic_bytes_per_launch")
 
 
-def graph_timed(fn, steps, warmup, stream, reps=5, warm_reps=1):
+def graph_timed(fn, steps, warmup, stream, reps=5, warm_reps=1, warm_ms=0.0):
     """Per-call GPU time of fn(0..steps-1): the calls captured once in a HIP graph (the library
-    allocates nothing and launches on the current stream), the graph replayed `warm_reps` times
-    untimed and then `reps` times, each replay timed with HIP events on the launch stream. The
-    host-side marshalling of one eager call takes about as long as a short kernel, so eager
-    timing would measure the host."""
+    allocates nothing and launches on the current stream), the graph replayed untimed at least
+    `warm_reps` times and for at least `warm_ms` milliseconds of sustained load (the clocks of a
+    fresh GPU settle under load), then `reps` times, each replay timed with HIP events on the
+    launch stream. The host-side marshalling of one eager call takes about as long as a short
+    kernel, so eager timing would measure the host."""
     import numpy as np
     import torch
 
@@ -175,8 +193,13 @@ def graph_timed(fn, steps, warmup, stream, reps=5, warm_reps=1):
     with torch.cuda.graph(graph):
         for i in range(steps):
             fn(i)
-    for _ in range(warm_reps):
+    t0 = time.perf_counter()
+    done = 0
+    while done < warm_reps or (time.perf_counter() - t0) * 1e3 < warm_ms:
         graph.replay()
+        done += 1
+        if done % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for r in range(reps):
@@ -188,8 +211,9 @@ def graph_timed(fn, steps, warmup, stream, reps=5, warm_reps=1):
 
 
 def measured_rates():
-    """Whole-GPU fp32 FMA and v_exp_f32 issue rates (lane-ops/s) from the microkernels, or None
-    when their library is not built."""
+    """Whole-GPU issue rates from the microkernels (lane-ops/s): fp32 FMA, v_exp_f32, a multiply
+    fed by a DPP row broadcast, and units of (4 FMA + 1 exp); None when their library is not
+    built."""
     import ctypes
 
     if not os.path.exists(RATES_LIB):
@@ -197,10 +221,38 @@ def measured_rates():
     lib = ctypes.CDLL(RATES_LIB)
     lib.mscan_measure_rates.restype = ctypes.c_int
     lib.mscan_measure_rates.argtypes = [ctypes.POINTER(ctypes.c_double)]
-    r = (ctypes.c_double * 2)()
+    r = (ctypes.c_double * 4)()
     if lib.mscan_measure_rates(r) != 0:
         return None
-    return {"fma_T_lane_ops_per_s": round(r[0] / 1e12, 2), "exp_T_lane_ops_per_s": round(r[1] / 1e12, 2)}
+    return {"fma_T_lane_ops_per_s": round(r[0] / 1e12, 3), "exp_T_lane_ops_per_s": round(r[1] / 1e12, 3),
+            "dpp_mul_T_lane_ops_per_s": round(r[2] / 1e12, 3),
+            "mix_4fma_1exp_T_units_per_s": round(r[3] / 1e12, 3)}
+
+
+def issue_floor(w, rates, mean_launch_us):
+    """The time the method's minimum arithmetic needs at the issue rates measured in this run:
+    per element 1 exp + 4 fp32 operations, per row-step the transcendentals of
+    transcendentals_per_launch and VALU_OPS_PER_ROW_STEP operations. The 4 FMA : 1 exp mix probe
+    says whether an exp issues alongside FMAs (co_issue > 1) or adds its own time (about 1); the
+    floor uses the element work at the mix's measured rate and the row-step work additively."""
+    if rates is None:
+        return None
+    r_fma = rates["fma_T_lane_ops_per_s"] * 1e12
+    r_exp = rates["exp_T_lane_ops_per_s"] * 1e12
+    r_mix = rates["mix_4fma_1exp_T_units_per_s"] * 1e12
+    row_steps = w.rows * w.seqlen
+    n_trans = transcendentals_per_launch(w)
+    n_valu = w.elements * VALU_OPS_PER_ELEMENT + row_steps * VALU_OPS_PER_ROW_STEP
+    t_trans = n_trans / r_exp
+    t_valu = n_valu / r_fma
+    co_issue = (4.0 / r_fma + 1.0 / r_exp) * r_mix  # additive time per unit / measured time per unit
+    t_rows = (n_trans - w.elements) / r_exp + row_steps * VALU_OPS_PER_ROW_STEP / r_fma
+    floor_us = (w.elements / r_mix + t_rows) * 1e6
+    return {"what": "minimum issue time of the method's arithmetic at rates measured in this run",
+            "transcendentals_per_launch": n_trans, "valu_ops_per_launch": n_valu,
+            "t_trans_us": round(t_trans * 1e6, 2), "t_valu_us": round(t_valu * 1e6, 2),
+            "co_issue_4fma_1exp": round(co_issue, 3), "floor_us": round(floor_us, 2),
+            "frac": round(floor_us / mean_launch_us, 4), "measured_rates": rates}
 
 
 def transcendentals_per_launch(w):
@@ -532,7 +584,7 @@ def backward_bench(args):
     # slots fewer per element; the checkpoints are read instead of written and read back)
     per_el = SLOTS_PER_ELEMENT_BWD - (SLOTS_PER_ELEMENT_FWD_RECURRENCE if ck is not None else 0)
     bwd_slots = w.elements * per_el + w.rows * w.seqlen * SLOTS_PER_ROW_STEP_BWD
-    bwd_tflops = 2 * bwd_slots / (mean_us * 1e-6) / 1e12
+    bwd_tflops = 2 * bwd_slots / (mean_us * 1e-6) / 1e12  # slot-equivalents, a secondary figure
     res = {
         "metric": "scan backward, Gelem/s (B*D*L*N) per mamba_scan_bwd call",
         "value": round(w.elements / (mean_us * 1e-6) / 1e9, 2),
@@ -549,13 +601,13 @@ def backward_bench(args):
         "config": {"workload": w.name + ("-backward-from-checkpoints" if ck is not None else "-backward"),
                    "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seq_len": w.seqlen, "storage": w.dtype},
-        "roofline": {"bound": "alu", "achieved": round(bwd_tflops, 2), "peak": VALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(bwd_tflops / VALU_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": read + written,
                      "traffic": measured_bwd_traffic(w, ck is not None),
-                     "valu_slots_per_call": bwd_slots, "mean_call_us": round(mean_us, 2),
-                     "min_call_us": round(float(per_us.min()), 2),
-                     "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": read + written}},
+                     "mean_call_us": round(mean_us, 2), "min_call_us": round(float(per_us.min()), 2),
+                     "valu_issue_slots": {"per_call": bwd_slots, "slot_equivalent_TFLOP_s": round(bwd_tflops, 2),
+                                          "peak_TFLOP_s": VALU_PEAK_TFLOPS,
+                                          "frac": round(bwd_tflops / VALU_PEAK_TFLOPS, 4)}},
         "parity": {"max_rel_err": errs},
     }
     if fwd_ck is not None:
@@ -746,6 +798,13 @@ def main():
                                return_last_state=w.last_state, kernel=kernel, out=s["y"],
                                last_state_out=s["ls"], zoh_b=args.zoh)
 
+    s0 = sets[0]
+    kname = scan.forward_kernel(s0["u"], s0["delta"], s0["A"], s0["B"], s0["C"], D=s0["D"], z=s0["z"],
+                                delta_bias=s0["delta_bias"], delta_softplus=w.softplus,
+                                return_last_state=w.last_state, kernel=kernel, out=s0["y"],
+                                last_state_out=s0["ls"], zoh_b=args.zoh)
+    log(f"kernel: {kname}")
+
     stream = torch.cuda.current_stream(dev)
     # eager calls, each bracketed by events: when the host-side marshalling of a call takes
     # longer than its kernel, these measure the host (reported for reference only)
@@ -762,26 +821,28 @@ def main():
     eager_span_ms = ev[0][0].elapsed_time(ev[-1][1])
     eager = [(s["y"].clone(), s["ls"].clone()) for s in sets]
 
-    # timed: the K steps captured once in a HIP graph, the graph replayed 3 times untimed (the
-    # clocks settle under sustained load) and then 7 times, each replay (exactly K steps, the
+    # timed: the K steps captured once in a HIP graph, the graph replayed untimed for at least
+    # WARM_MS of sustained load (the clocks of a fresh GPU settle) and then 7 times, each replay (exactly K steps, the
     # buffer sets rotating) timed with HIP events on the launch stream and bracketed by device
     # synchronisation; value and ms_per_step from the median replay
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    per_call_us = graph_timed(step, args.steps, 0, stream, reps=7, warm_reps=3)
+    per_call_us = graph_timed(step, args.steps, 0, stream, reps=7, warm_reps=3, warm_ms=WARM_MS)
     wall = time.perf_counter() - t_start
     replay_equal = all(torch.equal(s["y"], e[0]) and torch.equal(s["ls"], e[1]) for s, e in zip(sets, eager))
     mean_launch_ms = float(np.median(per_call_us)) / 1e3
     log(f"{args.steps} steps per replay: {np.round(per_call_us, 2).tolist()} us per call "
         f"(replays equal eager: {replay_equal}); eager span {eager_span_ms * 1e3 / args.steps:.1f} us "
-        f"per call; wall {wall * 1e3:.1f} ms for capture + 10 replays")
+        f"per call; wall {wall * 1e3:.1f} ms for capture, warm-up and 7 timed replays")
 
     ms_per_step = mean_launch_ms
     value = w.elements / (ms_per_step * 1e-3) / 1e9
     alg_bytes = w.algorithmic_bytes()
     achieved_gbs = alg_bytes / (mean_launch_ms * 1e-3) / 1e9
-    slots = w.elements * (SLOTS_PER_ELEMENT_ZOH if args.zoh else SLOTS_PER_ELEMENT) + w.rows * w.seqlen * SLOTS_PER_ROW_STEP
-    achieved_tflops = 2 * slots / (mean_launch_ms * 1e-3) / 1e12
+    row_steps = w.rows * w.seqlen
+    flops = w.elements * FLOPS_PER_ELEMENT + row_steps * FLOPS_PER_ROW_STEP
+    achieved_tflops = flops / (mean_launch_ms * 1e-3) / 1e12
+    spread = float((per_call_us.max() - per_call_us.min()) / np.median(per_call_us))
 
     check = None
     if not args.no_check:
@@ -823,6 +884,10 @@ def main():
     trans = {"ops_per_launch": n_trans, "achieved_T_per_s": round(trans_rate, 3),
              "measured_peak_T_per_s": None if rates is None else rates["exp_T_lane_ops_per_s"],
              "frac": None if rates is None else round(trans_rate / rates["exp_T_lane_ops_per_s"], 4)}
+    floor = issue_floor(w, rates, mean_launch_ms * 1e3) if not args.zoh else None
+    traffic = measured_traffic(w, kname, args.zoh)
+    hbm_floor_us = alg_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    binding = "hbm" if floor is None or hbm_floor_us >= floor["floor_us"] else "issue (exp + VALU)"
 
     out = {
         "metric": "scan Gelem/s (B*D*L*N) + % HBM roofline, Mamba-130m layer shape, L=2048"
@@ -840,23 +905,31 @@ def main():
         "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
                    "seq_len": w.seqlen, "storage": w.dtype, "z_gate": w.has_z,
-                   "last_state": w.last_state, "kernel": resolved_kernel(w, args.kernel, args.zoh),
+                   "last_state": w.last_state, "kernel": kname,
                    "buffer_sets": len(sets),
                    "zoh_b": args.zoh},
-        "roofline": {"bound": "alu", "achieved": round(achieved_tflops, 2),
-                     "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved_tflops / VALU_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(w, args.kernel, args.zoh),
-                     "valu_slots_per_launch": slots, "algorithmic_bytes": alg_bytes,
-                     "hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)},
-                     "transcendental": trans,
-                     "measured_rates": rates,
+        # the metric's roofline: the minimum bytes (inputs read once, outputs written once) over
+        # the scan kernel's mean launch time, against the published 8 TB/s
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": alg_bytes,
                      "mean_launch_us": round(mean_launch_ms * 1e3, 2),
-                     "timing": f"median of 7 HIP-graph replays (after 3 untimed) of {args.steps} captured calls, per call",
+                     "hbm_floor_us": round(hbm_floor_us, 2),
+                     "timing": f"median of 7 HIP-graph replays of {args.steps} captured calls, per call, "
+                               f"after >= {WARM_MS:.0f} ms of untimed replays",
                      "graph_replay_us_per_call": [round(float(v), 2) for v in per_call_us],
+                     "replay_spread": round(spread, 4),
                      "graph_replays_equal_eager": replay_equal,
                      "eager_us_per_call": round(eager_span_ms * 1e3 / args.steps, 2)},
+        # the other floor: the issue time of the method's arithmetic at the rates measured in this
+        # run; whichever of the two is longer binds
+        "issue_floor": floor,
+        "binding_floor": binding,
+        "exp_roofline": trans,
+        "alu": {"flops_per_launch": flops, "flops_per_element": FLOPS_PER_ELEMENT,
+                "flops_per_row_step": FLOPS_PER_ROW_STEP, "achieved_TFLOP_s": round(achieved_tflops, 3),
+                "peak_TFLOP_s": VALU_PEAK_TFLOPS, "frac": round(achieved_tflops / VALU_PEAK_TFLOPS, 4)},
+        "kernel_sources_sha256": kernel_source_hash(kname, KERNEL_SOURCES),
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
         "parity_sample": check,

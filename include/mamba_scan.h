@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 6
+#define MAMBA_SCAN_ABI_VERSION 7
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -69,13 +69,22 @@ typedef enum mamba_scan_dtype {
  * otherwise. ABI version 6. */
 #define MAMBA_SCAN_SAVE_CHECKPOINTS (1u << 3)
 /* Kernel selection, for testing and tuning; at most one of these bits (MAMBA_SCAN_ERR_ARGS
- * otherwise). Default (none): the lane-per-state kernel where it can run, else the tiled one,
- * else the generic one. */
+ * otherwise). Default (none): with 16 states, at least 1024 steps and too few (batch, channel)
+ * rows to give every SIMD of the GPU two waves of the lane-per-state kernel, the chunked kernel;
+ * otherwise the lane-per-state kernel where it can run, else the tiled one, else the generic
+ * one. */
 #define MAMBA_SCAN_FORCE_GENERIC (1u << 8) /* one lane per row, any shape and alignment */
 #define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
 #define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one lane per (channel, state): dstate 16, 32 or
                                               64, no ZOH_B; error if it cannot run (ABI 5) */
-#define MAMBA_SCAN_KNOWN_FLAGS 0x70Fu
+/* Chunked along the sequence (ABI 7): one wave per channel, its four 16-lane rows scan four
+ * consecutive 16-step runs of each 64-step chunk and are combined with the associative (a, b)
+ * operator of the parallel scan ("手把手用PyTorch实现Mamba的SSM层…" §3.2), the state carried
+ * from chunk to chunk in registers. dstate 16, no ZOH_B, no SAVE_CHECKPOINTS; error if it cannot
+ * run. Results agree with the sequential kernels to rounding (not bit for bit); a sequence split
+ * at a multiple of 64 steps and resumed from last_state gives the same bits as one call. */
+#define MAMBA_SCAN_FORCE_CHUNKED (1u << 11)
+#define MAMBA_SCAN_KNOWN_FLAGS 0xF0Fu
 
 /* error codes */
 #define MAMBA_SCAN_OK 0
@@ -104,7 +113,8 @@ typedef struct mamba_scan_ptrs {
     const float* h0;         /* (batch, dim, dstate) fp32, or NULL (zero initial state) */
     float* y;                /* (batch, dim, len) fp32, required, written */
     float* last_state;       /* (batch, dim, dstate) fp32, written iff RETURN_LAST_STATE */
-    void* workspace;         /* device scratch, or NULL; see mamba_scan_workspace_bytes */
+    void* workspace;         /* the saved states with MAMBA_SCAN_SAVE_CHECKPOINTS, else unused
+                                (may be NULL); see mamba_scan_workspace_bytes */
     int64_t workspace_bytes; /* its size in bytes */
 } mamba_scan_ptrs;
 
@@ -128,11 +138,22 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s,
                    const mamba_scan_strides* st, mamba_scan_dtype dtype, uint32_t flags,
                    void* stream);
 
-/* Bytes of device workspace that let mamba_scan_fwd split long sequences across workgroups
- * (an exact two-pass carry of the state between segments of L). 0 when the plan needs none.
- * A call given less workspace than this still runs, unsplit. Negative on invalid arguments.
- * With MAMBA_SCAN_SAVE_CHECKPOINTS: the size of the saved states instead, which the call then
- * requires (MAMBA_SCAN_ERR_WORKSPACE below it; 4-byte alignment, MAMBA_SCAN_ERR_ARGS otherwise). */
+/* The kernel mamba_scan_fwd would run for these arguments (ABI 7): one of the values below, or
+ * the error code mamba_scan_fwd would return before launching. Enqueues nothing; the pointers are
+ * only compared (overlaps, alignment), never dereferenced. The choice between the chunked and
+ * the lane-per-state kernel depends on the current device's compute-unit count. */
+#define MAMBA_SCAN_KERNEL_GENERIC 1
+#define MAMBA_SCAN_KERNEL_TILED 2
+#define MAMBA_SCAN_KERNEL_LANES 3
+#define MAMBA_SCAN_KERNEL_CHUNKED 4
+int mamba_scan_fwd_kernel(const mamba_scan_ptrs* p, const mamba_scan_shape* s,
+                          const mamba_scan_strides* st, mamba_scan_dtype dtype, uint32_t flags);
+
+/* Bytes of device workspace mamba_scan_fwd needs with these flags: 0 without
+ * MAMBA_SCAN_SAVE_CHECKPOINTS (no forward kernel uses scratch memory: the chunked kernel carries
+ * the state between chunks of the sequence in registers); with it, the size of the saved states,
+ * which the call then requires (MAMBA_SCAN_ERR_WORKSPACE below it; 4-byte alignment,
+ * MAMBA_SCAN_ERR_ARGS otherwise). Negative on invalid arguments. */
 int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype,
                                    uint32_t flags);
 
@@ -159,8 +180,10 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *    (batch, dim, len), required; dz (batch, dim, len), required exactly when z is given;
  *    dB, dC (batch, dstate, len), required; dA (dim, dstate), required; dD and ddelta_bias (dim),
  *    each required exactly when D / delta_bias is given; dh0 (batch, dim, dstate) or NULL.
- *  - Workspace: exactly mamba_scan_bwd_workspace_bytes() bytes or more, 256-byte aligned, device
- *    memory owned by the caller (states every 16 steps, fp32 copies of B and C, partial sums).
+ *  - Workspace: mamba_scan_bwd_workspace_bytes() bytes or more (queried with
+ *    MAMBA_SCAN_SAVE_CHECKPOINTS when `checkpoints` is given), 256-byte aligned, device memory
+ *    owned by the caller (states every 16 steps unless given, fp32 copies of B and C, partial
+ *    sums).
  *  - Flags: MAMBA_SCAN_DELTA_SOFTPLUS only.
  *  - Any dstate up to MAMBA_SCAN_MAX_DSTATE. Above 16 the states are processed in blocks of at
  *    most 16, one launch each: du, ddelta and dz are accumulated in place across the blocks, in
@@ -205,7 +228,9 @@ typedef struct mamba_scan_bwd_ptrs {
 int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
                    uint32_t flags, void* stream);
 
-/* Workspace bytes mamba_scan_bwd needs for this shape (> 0), or a negative error code. */
+/* Workspace bytes mamba_scan_bwd needs for this shape (> 0), or a negative error code. Flags:
+ * MAMBA_SCAN_DELTA_SOFTPLUS (ignored for the size) and MAMBA_SCAN_SAVE_CHECKPOINTS, meaning that
+ * the call will be given `checkpoints`: the size then leaves out the recomputed states (ABI 7). */
 int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype, uint32_t flags);
 
 /*

@@ -18,6 +18,7 @@ from . import gen as _gen
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmamba_scan.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mamba_scan.h")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -38,11 +39,37 @@ def sources():
     )
 
 
-def build_hip(out: str = LIB, extra=()) -> str:
+def units():
+    """Translation units: the C-ABI entry points and one per kernel family."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def build_hip(out: str = LIB, extra=(), jobs=None, incremental=False) -> str:
+    """Compile every translation unit to an object in parallel, then link the shared library.
+    ``incremental``: skip units whose object is newer than every source and the header (for
+    development; a plain build compiles everything)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+
+    newest = max(os.path.getmtime(f) for f in sources() + [HEADER])
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.basename(src)[:-4] + ".o")
+        if incremental and os.path.exists(obj) and os.path.getmtime(obj) > newest:
+            return obj
+        subprocess.run([hipcc, *compile_flags, *extra, "-c", "-o", obj, src], check=True)
+        return obj
+
+    srcs = units()
+    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, srcs))
     tmp = out + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-o", tmp, os.path.join(CSRC, "mamba_scan.hip")]
-    subprocess.run(cmd, check=True)
+    subprocess.run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
     os.replace(tmp, out)
     return out
 

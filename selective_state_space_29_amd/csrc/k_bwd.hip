@@ -1,0 +1,12 @@
+// Launchers of the backward pass (B/C widening, scan, fixed-order reduction).
+#include "launch.hpp"
+#include "scan_bwd.hpp"
+
+namespace mscan {
+
+int launch_bwd_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
+                   hipStream_t stream) {
+    return bf16 ? launch_bwd<bf16_t>(p, s, softplus, stream) : launch_bwd<float>(p, s, softplus, stream);
+}
+
+}  // namespace mscan

@@ -6,12 +6,15 @@
 #include <string.h>
 
 #include "../../include/mamba_scan.h"
-#include "block_upstream.hpp"
+#include "block_upstream.hpp"  // UpParams and its limits (its kernel is built in k_upstream.hip)
 #include "common.hpp"
-#include "scan_bwd.hpp"
-#include "scan_generic.hpp"
-#include "scan_ls.hpp"
-#include "scan_tiled.hpp"
+#include "launch.hpp"
+#include "bwd_layout.hpp"
+#include "scan_lp.hpp"   // lp_eligible
+#include "scan_ls.hpp"   // ls_eligible
+#include "scan_tiled.hpp"  // aligned
+
+#include <atomic>
 
 using namespace mscan;
 
@@ -62,7 +65,8 @@ int validate(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_sc
     if (!p || !s || !st) return MAMBA_SCAN_ERR_NULL;
     if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
     if (flags & ~MAMBA_SCAN_KNOWN_FLAGS) return MAMBA_SCAN_ERR_ARGS;
-    const uint32_t forced = flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_LANES);
+    const uint32_t forced =
+        flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_LANES | MAMBA_SCAN_FORCE_CHUNKED);
     if (forced & (forced - 1)) return MAMBA_SCAN_ERR_ARGS;  // at most one kernel may be forced
     if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
@@ -99,6 +103,12 @@ int validate(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_sc
     for (const Span& in : ins)
         if (overlaps(y, in) || overlaps(ls, in)) return MAMBA_SCAN_ERR_ARGS;
     if (overlaps(y, ls)) return MAMBA_SCAN_ERR_ARGS;
+    // with SAVE_CHECKPOINTS the workspace is written: it may not overlap any input either
+    if (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) {
+        const Span& ws = ins[sizeof ins / sizeof ins[0] - 1];
+        for (size_t i = 0; i + 1 < sizeof ins / sizeof ins[0]; ++i)
+            if (overlaps(ws, ins[i])) return MAMBA_SCAN_ERR_ARGS;
+    }
     return MAMBA_SCAN_OK;
 }
 
@@ -146,21 +156,59 @@ ScanParams make_params(const mamba_scan_ptrs* p, const mamba_scan_shape* s, cons
     return q;
 }
 
-template <typename T>
-int launch_generic(const ScanParams& q, hipStream_t stream) {
-    const int64_t rows = q.batch * q.dim;
-    const dim3 grid((unsigned)((rows + 63) / 64));
-    const dim3 block(64);
-    void* args[] = {const_cast<ScanParams*>(&q)};
-    const void* fn;
-    if (q.dstate <= 16)
-        fn = reinterpret_cast<const void*>(&scan_generic_kernel<T, 16>);
-    else if (q.dstate <= 32)
-        fn = reinterpret_cast<const void*>(&scan_generic_kernel<T, 32>);
-    else
-        fn = reinterpret_cast<const void*>(&scan_generic_kernel<T, 64>);
-    return hipLaunchKernel(fn, grid, block, args, 0, stream) == hipSuccess ? MAMBA_SCAN_OK
-                                                                           : MAMBA_SCAN_ERR_LAUNCH;
+// Compute units of the current device (cached per device; 0 if the runtime cannot say).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev < 0 || dev >= 64) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// The chunked kernel is the default for sequences of at least kChunkedMinLen steps where the
+// lane-per-state kernel (4 channels x 16 states per wave) would give the GPU's SIMDs fewer than
+// two waves each. (Shorter calls, such as the pieces of a streamed sequence, keep the sequential
+// kernel, whose results do not depend on where a sequence is split.)
+constexpr int64_t kChunkedMinLen = 1024;
+bool prefer_chunked(const ScanParams& q) {
+    if (q.dstate != 16 || q.zoh_b || q.ck || q.len < kChunkedMinLen) return false;
+    const int cus = device_cus();
+    if (cus <= 0) return false;
+    const int64_t ls_waves = q.batch * ((q.dim + 3) / 4);
+    return ls_waves < 2 * 4 * (int64_t)cus;
+}
+
+// With SAVE_CHECKPOINTS the states go to the workspace: it must hold them, 4-byte aligned.
+int check_checkpoint_workspace(const mamba_scan_ptrs* p, const mamba_scan_shape* s, uint32_t flags) {
+    if (!(flags & MAMBA_SCAN_SAVE_CHECKPOINTS)) return MAMBA_SCAN_OK;
+    const int64_t need = s->batch * s->dim * ((s->len + 15) / 16) * s->dstate * 4;
+    if (!p->workspace || p->workspace_bytes < need) return MAMBA_SCAN_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(p->workspace) % 4) return MAMBA_SCAN_ERR_ARGS;
+    return MAMBA_SCAN_OK;
+}
+
+// The forward kernel a call runs: a forced one if it can take the case, else the default order.
+// Shared by mamba_scan_fwd and mamba_scan_fwd_kernel so that the query and the launch agree.
+int choose_kernel(const ScanParams& q, uint32_t flags, bool bf16) {
+    const int64_t es = bf16 ? 2 : 4;
+    if (q.ck) {  // the saved states come from the lane-per-state kernels only
+        if (flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_CHUNKED))
+            return MAMBA_SCAN_ERR_UNSUPPORTED;
+        return ls_eligible(q, es) ? MAMBA_SCAN_KERNEL_LANES : MAMBA_SCAN_ERR_UNSUPPORTED;
+    }
+    if (flags & MAMBA_SCAN_FORCE_CHUNKED) return lp_eligible(q, es) ? MAMBA_SCAN_KERNEL_CHUNKED : MAMBA_SCAN_ERR_UNSUPPORTED;
+    if (flags & MAMBA_SCAN_FORCE_LANES) return ls_eligible(q, es) ? MAMBA_SCAN_KERNEL_LANES : MAMBA_SCAN_ERR_UNSUPPORTED;
+    if (flags & MAMBA_SCAN_FORCE_TILED) return tiled_can_run_any(q, bf16) ? MAMBA_SCAN_KERNEL_TILED : MAMBA_SCAN_ERR_UNSUPPORTED;
+    if (flags & MAMBA_SCAN_FORCE_GENERIC) return MAMBA_SCAN_KERNEL_GENERIC;
+    if (prefer_chunked(q) && lp_eligible(q, es)) return MAMBA_SCAN_KERNEL_CHUNKED;
+    if (ls_eligible(q, es)) return MAMBA_SCAN_KERNEL_LANES;
+    if (tiled_can_run_any(q, bf16)) return MAMBA_SCAN_KERNEL_TILED;
+    return MAMBA_SCAN_KERNEL_GENERIC;
 }
 
 }  // namespace
@@ -194,22 +242,24 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
     if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
     if (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) return s->batch * s->dim * ((s->len + 15) / 16) * s->dstate * 4;
-    return tiled_workspace_bytes(*s, flags);
+    return 0;
 }
 
 int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype, uint32_t flags) {
     if (!s) return MAMBA_SCAN_ERR_NULL;
     if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
-    if (flags & ~MAMBA_SCAN_DELTA_SOFTPLUS) return MAMBA_SCAN_ERR_ARGS;
+    if (flags & ~(MAMBA_SCAN_DELTA_SOFTPLUS | MAMBA_SCAN_SAVE_CHECKPOINTS)) return MAMBA_SCAN_ERR_ARGS;
     if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
-    return bwd_layout(*s).total;
+    return bwd_layout(*s, (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) != 0).total;
 }
 
 int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
                    uint32_t flags, void* stream) {
     if (!p || !s) return MAMBA_SCAN_ERR_NULL;
-    const int64_t need = mamba_scan_bwd_workspace_bytes(s, dtype, flags);
+    if (flags & ~MAMBA_SCAN_DELTA_SOFTPLUS) return MAMBA_SCAN_ERR_ARGS;
+    const int64_t need =
+        mamba_scan_bwd_workspace_bytes(s, dtype, flags | (p->checkpoints ? MAMBA_SCAN_SAVE_CHECKPOINTS : 0u));
     if (need < 0) return (int)need;
     if (!p->u || !p->delta || !p->B || !p->C || !p->A || !p->dy || !p->du || !p->ddelta || !p->dB ||
         !p->dC || !p->dA)
@@ -250,7 +300,7 @@ int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool sp = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) != 0;
-    return dtype == MAMBA_SCAN_BF16 ? launch_bwd<bf16_t>(p, *s, sp, hs) : launch_bwd<float>(p, *s, sp, hs);
+    return launch_bwd_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
 }
 
 int mamba_block_upstream(const mamba_upstream_ptrs* p, const mamba_upstream_shape* s, mamba_scan_dtype dtype,
@@ -303,7 +353,7 @@ int mamba_block_upstream(const mamba_upstream_ptrs* p, const mamba_upstream_shap
     q.len = s->len;
     q.dstate = (int)s->dstate;
     q.dt_rank = (int)s->dt_rank;
-    return launch_upstream(q, (int)s->d_conv, static_cast<hipStream_t>(stream));
+    return launch_upstream_any(q, (int)s->d_conv, static_cast<hipStream_t>(stream));
 }
 
 int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_scan_strides* st_in,
@@ -322,25 +372,34 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const ma
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool bf16 = dtype == MAMBA_SCAN_BF16;
 
-    if (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) {
-        // saved by the lane-per-state kernels only, into a workspace of the queried size
-        const int64_t need = s->batch * s->dim * ((s->len + 15) / 16) * s->dstate * 4;
-        if (!p->workspace || p->workspace_bytes < need) return MAMBA_SCAN_ERR_WORKSPACE;
-        if (reinterpret_cast<uintptr_t>(p->workspace) % 4) return MAMBA_SCAN_ERR_ARGS;
-        if (flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED)) return MAMBA_SCAN_ERR_UNSUPPORTED;
-        return bf16 ? launch_ls<bf16_t>(q, hs) : launch_ls<float>(q, hs);
+    const int wrc = check_checkpoint_workspace(p, s, flags);
+    if (wrc != MAMBA_SCAN_OK) return wrc;
+    const int kernel = choose_kernel(q, flags, bf16);
+    switch (kernel) {
+        case MAMBA_SCAN_KERNEL_CHUNKED: return launch_lp_any(q, bf16, hs);
+        case MAMBA_SCAN_KERNEL_LANES: return launch_ls_any(q, bf16, hs);
+        case MAMBA_SCAN_KERNEL_TILED: return launch_tiled_any(q, bf16, hs);
+        case MAMBA_SCAN_KERNEL_GENERIC: return launch_generic_any(q, bf16, hs);
+        default: return kernel;  // an error code
     }
-    // default order: lane-per-state (16, 32, 64 states), then the tiled kernel, then the generic one
-    if (!(flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED))) {
-        const int lrc = bf16 ? launch_ls<bf16_t>(q, hs) : launch_ls<float>(q, hs);
-        if (lrc != MAMBA_SCAN_ERR_UNSUPPORTED || (flags & MAMBA_SCAN_FORCE_LANES)) return lrc;
+}
+
+int mamba_scan_fwd_kernel(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_scan_strides* st_in,
+                          mamba_scan_dtype dtype, uint32_t flags) {
+    if (!p || !s) return MAMBA_SCAN_ERR_NULL;
+    mamba_scan_strides st;
+    if (st_in) {
+        st = *st_in;
+    } else {
+        if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+        contiguous_strides(*s, &st);
     }
-    if (!(flags & MAMBA_SCAN_FORCE_GENERIC)) {
-        const int trc = bf16 ? launch_tiled<bf16_t>(q, p, flags, hs) : launch_tiled<float>(q, p, flags, hs);
-        if (trc != MAMBA_SCAN_ERR_UNSUPPORTED) return trc;
-        if (flags & MAMBA_SCAN_FORCE_TILED) return trc;
-    }
-    return bf16 ? launch_generic<bf16_t>(q, hs) : launch_generic<float>(q, hs);
+    const int rc = validate(p, s, &st, dtype, flags);
+    if (rc != MAMBA_SCAN_OK) return rc;
+    const int wrc = check_checkpoint_workspace(p, s, flags);
+    if (wrc != MAMBA_SCAN_OK) return wrc;
+    const ScanParams q = make_params(p, s, &st, flags);
+    return choose_kernel(q, flags, dtype == MAMBA_SCAN_BF16);
 }
 
 }  // extern "C"

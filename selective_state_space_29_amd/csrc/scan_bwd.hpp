@@ -32,6 +32,7 @@
 #pragma once
 
 #include "../../include/mamba_scan.h"
+#include "bwd_layout.hpp"
 #include "common.hpp"
 
 namespace mscan {
@@ -64,7 +65,6 @@ struct BwdParams {
 };
 
 constexpr int kBwdW = 8;     // waves per workgroup
-constexpr int kBwdSeg = 16;  // steps per segment (checkpoint interval)
 constexpr int kBwdSub = 8;   // steps per LDS exchange
 
 typedef const __attribute__((address_space(4))) float* bwd_cptrf;
@@ -486,40 +486,6 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdReduceParams p) {
 // ---------------------------------------------------------------------------------------------
 // host side
 
-struct BwdLayout {
-    int64_t lp, nseg, groups;
-    int64_t off_bc, off_ck, off_bcpart, off_apart, off_dpart, off_bpart, total;
-};
-
-inline int64_t bwd_align(int64_t x) { return (x + 255) / 256 * 256; }
-
-// States per launch: blocks of 16; a remainder in (8, 16] that is odd (two states per wave would
-// leave one wave half used) is split into 8 and the rest.
-inline int64_t bwd_next_block(int64_t rem) { return rem > 16 ? 16 : (rem > 8 && rem % 2) ? 8 : rem; }
-inline int64_t bwd_block_states(int64_t N) { return bwd_next_block(N); }
-
-inline BwdLayout bwd_layout(const mamba_scan_shape& s) {
-    BwdLayout l;
-    l.lp = (s.len + kBwdSeg - 1) / kBwdSeg * kBwdSeg;
-    l.nseg = l.lp / kBwdSeg;
-    l.groups = (s.dim + 63) / 64;
-    int64_t o = 0;
-    l.off_bc = o;
-    o = bwd_align(o + 2 * s.batch * s.dstate * l.lp * 4);
-    l.off_ck = o;
-    o = bwd_align(o + s.batch * s.dim * l.nseg * bwd_block_states(s.dstate) * 4);
-    l.off_bcpart = o;
-    o = bwd_align(o + l.groups * s.batch * 2 * s.dstate * l.lp * 4);
-    l.off_apart = o;
-    o = bwd_align(o + s.batch * s.dim * s.dstate * 4);
-    l.off_dpart = o;
-    o = bwd_align(o + s.batch * s.dim * 4);
-    l.off_bpart = o;
-    o = bwd_align(o + s.batch * s.dim * 4);
-    l.total = o;
-    return l;
-}
-
 inline int bwd_states_per_wave(int64_t nb) { return nb <= 8 ? 1 : 2; }
 
 template <typename T, int S, bool SP, bool HZ>
@@ -549,7 +515,7 @@ int launch_bwd_s(const BwdParams& q, bool softplus, hipStream_t stream) {
 
 template <typename T>
 int launch_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool softplus, hipStream_t stream) {
-    const BwdLayout l = bwd_layout(s);
+    const BwdLayout l = bwd_layout(s, p->checkpoints != nullptr);
     char* ws = static_cast<char*>(p->workspace);
     BwdParams q;
     q.u = p->u;

@@ -511,8 +511,6 @@ __global__ __launch_bounds__(64 * W) void scan_tiled_kernel(ScanParams p) {
 // ---------------------------------------------------------------------------------------------
 // host side
 
-inline int64_t tiled_workspace_bytes(const mamba_scan_shape&, uint32_t) { return 0; }
-
 // States per wave for the 8-wave workgroup: N <= 8 -> 1 (waves n >= N idle), then 2, 4, 8.
 inline int tiled_states_per_wave(int64_t N) {
     if (N <= 8) return 1;
@@ -542,6 +540,17 @@ bool tiled_eligible(const ScanParams& q, int qs) {
     // y of one workgroup (64 rows) is addressed through a 32-bit buffer offset
     if ((63 * q.sy_d + q.len) * 4 >= ((int64_t)1 << 31)) return false;
     return true;
+}
+
+// Whether launch_tiled can run this case (its states-per-wave split and alignment rules).
+template <typename T>
+bool tiled_can_run(const ScanParams& q) {
+    switch (tiled_states_per_wave(q.dstate)) {
+        case 1: case 2: return tiled_eligible<T>(q, 4);
+        case 4: return tiled_eligible<T>(q, 2);
+        case 8: return tiled_eligible<T>(q, 1);
+        default: return false;
+    }
 }
 
 template <typename T, int S, int W, int TC, bool SP, bool HZ>

@@ -29,6 +29,7 @@ SAVE_CHECKPOINTS = 1 << 3
 FORCE_GENERIC = 1 << 8
 FORCE_TILED = 1 << 9
 FORCE_LANES = 1 << 10
+FORCE_CHUNKED = 1 << 11
 
 _I64 = ctypes.c_int64
 _P = ctypes.c_void_p
@@ -86,6 +87,9 @@ def load_library(path: str = LIB_PATH):
     lib.mamba_scan_fwd.restype = ctypes.c_int
     lib.mamba_scan_fwd.argtypes = [ctypes.POINTER(Ptrs), ctypes.POINTER(Shape),
                                    ctypes.POINTER(Strides), ctypes.c_int, ctypes.c_uint32, _P]
+    lib.mamba_scan_fwd_kernel.restype = ctypes.c_int
+    lib.mamba_scan_fwd_kernel.argtypes = [ctypes.POINTER(Ptrs), ctypes.POINTER(Shape),
+                                          ctypes.POINTER(Strides), ctypes.c_int, ctypes.c_uint32]
     lib.mamba_scan_workspace_bytes.restype = _I64
     lib.mamba_scan_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, ctypes.c_uint32]
     lib.mamba_scan_strerror.restype = ctypes.c_char_p
@@ -130,20 +134,14 @@ def _s3(x, fallback=(0, 0, 1)):
     return (_I64 * 3)(*(_strides(x) if x is not None else fallback))
 
 
-def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
-                      return_last_state=False, h0=None, *, kernel=None, out=None,
-                      last_state_out=None, zoh_b=False, checkpoints_out=None):
-    """y = selective_scan(...), fp32 (batch, dim, L); with ``return_last_state`` also the final
-    state (batch, dim, N) fp32. ``zoh_b``: B discretised by zero-order hold,
-    (e^{dt A} - 1) / A * B, instead of dt * B (forward only).
+KERNEL_NAMES = {1: "generic", 2: "tiled", 3: "lanes", 4: "chunked"}
 
-    u, delta, z: (batch, dim, L); B, C: (batch, N, L); one storage dtype for all five
-    (torch.float32 or torch.bfloat16). A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N);
-    these are taken in fp32. ``kernel``: None (library picks), "generic", "tiled" or "lanes"
-    (one lane per (channel, state); 16, 32 or 64 states). ``checkpoints_out``: a contiguous fp32
-    (batch, dim, ceil(L/16), N) tensor that receives the state before every 16-step segment, for
-    ``selective_scan_bwd(checkpoints=...)`` (lane-per-state kernels only).
-    """
+
+def _fwd_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_state, h0, kernel, out,
+              last_state_out, zoh_b, checkpoints_out, allocate=True):
+    """Validate and marshal the forward's arguments: (ptrs, shape, strides, dtype, flags, y, ls, ws).
+    With allocate=False no output or workspace is allocated (their pointers stay NULL unless
+    given), for the kernel query."""
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"u must be float32 or bfloat16, got {u.dtype}")
@@ -175,21 +173,21 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     if h0 is not None and h0.shape != (batch, dim, N):
         raise ValueError("h0 must be (batch, dim, N)")
 
-    y = out if out is not None else torch.empty((batch, dim, L), dtype=torch.float32, device=dev)
+    y = out
+    if y is None and allocate:
+        y = torch.empty((batch, dim, L), dtype=torch.float32, device=dev)
     ls = None
     flags = (DELTA_SOFTPLUS if delta_softplus else 0) | (ZOH_B if zoh_b else 0)
     if return_last_state:
-        ls = last_state_out if last_state_out is not None else torch.empty(
-            (batch, dim, N), dtype=torch.float32, device=dev)
+        ls = last_state_out
+        if ls is None and allocate:
+            ls = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
         flags |= RETURN_LAST_STATE
-    if kernel == "generic":
-        flags |= FORCE_GENERIC
-    elif kernel == "tiled":
-        flags |= FORCE_TILED
-    elif kernel == "lanes":
-        flags |= FORCE_LANES
-    elif kernel is not None:
-        raise ValueError("kernel must be None, 'generic', 'tiled' or 'lanes'")
+    forced = {None: 0, "generic": FORCE_GENERIC, "tiled": FORCE_TILED, "lanes": FORCE_LANES,
+              "chunked": FORCE_CHUNKED}
+    if kernel not in forced:
+        raise ValueError("kernel must be None, 'generic', 'tiled', 'lanes' or 'chunked'")
+    flags |= forced[kernel]
 
     shape = Shape(batch, dim, L, N)
     dtype = BF16 if u.dtype == torch.bfloat16 else F32
@@ -201,29 +199,82 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
         ws_bytes = lib.mamba_scan_workspace_bytes(ctypes.byref(shape), dtype, flags)
         if ws_bytes < 0:
             raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
-        ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+        ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev) if (ws_bytes > 0 and allocate) else None
 
     st = Strides()
     st.u, st.delta, st.z = _s3(u), _s3(delta), _s3(z)
-    st.B, st.C, st.y = _s3(B), _s3(C), _s3(y)
+    st.B, st.C = _s3(B), _s3(C)
+    st.y = _s3(y) if y is not None else (_I64 * 3)(dim * L, L, 1)
     st.h0, st.last_state = _s3(h0), _s3(ls)
     st.A = (_I64 * 2)(*_strides(A))
     st.D = _strides(D)[0] if D is not None else 1
     st.delta_bias = _strides(delta_bias)[0] if delta_bias is not None else 1
     ptrs = Ptrs(_ptr(u), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
                 _ptr(delta_bias), _ptr(h0), _ptr(y), _ptr(ls), _ptr(ws), int(ws_bytes))
+    keep = (u, delta, z, B, C, A, D, delta_bias, h0)  # the converted tensors must outlive the call
+    return ptrs, shape, st, dtype, flags, y, ls, ws, keep
+
+
+def _raise(rc):
+    err = MambaScanError(rc, strerror(rc))
+    if rc in (-1, -2, -3, -4, -5, -6, -8, -9):
+        raise ValueError(str(err)) from err
+    raise err
+
+
+def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                      return_last_state=False, h0=None, *, kernel=None, out=None,
+                      last_state_out=None, zoh_b=False, checkpoints_out=None):
+    """y = selective_scan(...), fp32 (batch, dim, L); with ``return_last_state`` also the final
+    state (batch, dim, N) fp32. ``zoh_b``: B discretised by zero-order hold,
+    (e^{dt A} - 1) / A * B, instead of dt * B (forward only).
+
+    u, delta, z: (batch, dim, L); B, C: (batch, N, L); one storage dtype for all five
+    (torch.float32 or torch.bfloat16). A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N);
+    these are taken in fp32. ``kernel``: None (library picks), "generic", "tiled", "lanes"
+    (one lane per (channel, state); 16, 32 or 64 states) or "chunked" (parallel along the
+    sequence: a wave per channel scanning 4 runs of each 64-step chunk; 16 states).
+    ``checkpoints_out``: a contiguous fp32 (batch, dim, ceil(L/16), N) tensor that receives the
+    state before every 16-step segment, for ``selective_scan_bwd(checkpoints=...)``
+    (lane-per-state kernels only).
+    """
+    lib = load_library()
+    ptrs, shape, st, dtype, flags, y, ls, ws, keep = _fwd_args(
+        u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_state, h0, kernel, out,
+        last_state_out, zoh_b, checkpoints_out)
+    dev = u.device
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib.mamba_scan_fwd(ctypes.byref(ptrs), ctypes.byref(shape), ctypes.byref(st),
                                 dtype, flags, stream)
+    del keep
     if rc != 0:
-        err = MambaScanError(rc, strerror(rc))
-        if rc in (-1, -2, -3, -4, -5, -6, -8):
-            raise ValueError(str(err)) from err
-        raise err
+        _raise(rc)
     if ws is not None and checkpoints_out is None:
         ws.record_stream(torch.cuda.current_stream(dev))
     return (y, ls) if return_last_state else y
+
+
+def forward_kernel(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                   return_last_state=False, h0=None, *, kernel=None, out=None, last_state_out=None,
+                   zoh_b=False, checkpoints_out=None):
+    """Name of the kernel ``selective_scan_fn`` would run with these arguments ("generic",
+    "tiled", "lanes" or "chunked"), from the library's own choice (``mamba_scan_fwd_kernel``);
+    raises as the call would for arguments it rejects. Launches nothing."""
+    lib = load_library()
+    ptrs, shape, st, dtype, flags, _, _, _, keep = _fwd_args(
+        u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_state, h0, kernel, out,
+        last_state_out, zoh_b, checkpoints_out, allocate=False)
+    if ptrs.y is None:
+        ptrs.y = 1 << 62  # any non-NULL address outside the inputs: compared, never dereferenced
+    if return_last_state and ptrs.last_state is None:
+        ptrs.last_state = (1 << 62) + (1 << 50)
+    with torch.cuda.device(u.device):
+        rc = lib.mamba_scan_fwd_kernel(ctypes.byref(ptrs), ctypes.byref(shape), ctypes.byref(st), dtype, flags)
+    del keep
+    if rc < 0:
+        _raise(rc)
+    return KERNEL_NAMES[rc]
 
 
 def checkpoint_shape(batch, dim, L, N):
@@ -289,7 +340,8 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     shape = Shape(batch, dim, L, N)
     dtype = BF16 if u.dtype == torch.bfloat16 else F32
     flags = DELTA_SOFTPLUS if delta_softplus else 0
-    ws_bytes = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(shape), dtype, flags)
+    ws_bytes = lib.mamba_scan_bwd_workspace_bytes(
+        ctypes.byref(shape), dtype, flags | (SAVE_CHECKPOINTS if checkpoints is not None else 0))
     if ws_bytes < 0:
         raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
     ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev)
@@ -357,7 +409,14 @@ class SelectiveScan(torch.autograd.Function):
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
                    return_last_state=False, h0=None):
-    """Differentiable form of ``selective_scan_fn`` (torch autograd through the HIP backward)."""
+    """Differentiable form of ``selective_scan_fn`` (torch autograd through the HIP backward).
+    When no gradient can flow (grad mode off, or no input requires one) it is the plain forward:
+    no states are saved for a backward that will not run."""
+    inputs = (u, delta, A, B, C, D, z, delta_bias, h0)
+    if not (torch.is_grad_enabled() and any(t is not None and t.requires_grad for t in inputs)):
+        return selective_scan_fn(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
+                                 delta_softplus=delta_softplus, return_last_state=return_last_state,
+                                 h0=h0)
     y, ls = SelectiveScan.apply(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
     return (y, ls) if return_last_state else y
 

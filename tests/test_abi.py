@@ -27,18 +27,19 @@ def header_functions():
 def test_header_declares_the_entry_points():
     assert header_functions() == ["mamba_block_upstream", "mamba_scan_abi_version", "mamba_scan_bwd",
                                   "mamba_scan_bwd_workspace_bytes", "mamba_scan_fwd",
-                                  "mamba_scan_strerror", "mamba_scan_workspace_bytes"]
+                                  "mamba_scan_fwd_kernel", "mamba_scan_strerror",
+                                  "mamba_scan_workspace_bytes"]
 
 
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 6
+    assert scan.load_library().mamba_scan_abi_version() == 7
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
-              strides=True):
+              strides=True, query=False):
     lib = scan.load_library()
     base = 1 << 40
     names = ["u", "delta", "z", "B", "C", "A", "D", "delta_bias", "h0", "y", "last_state"]
@@ -61,6 +62,10 @@ def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2,
     ctx = dict(ptrs=ptrs, shape=shp, st=st, flags=flags, dtype=dtype)
     if mutate:
         mutate(ctx)
+    if query:
+        return lib.mamba_scan_fwd_kernel(ctypes.byref(ctx["ptrs"]), ctypes.byref(ctx["shape"]),
+                                         ctypes.byref(ctx["st"]) if strides else None, ctx["dtype"],
+                                         ctx["flags"])
     return lib.mamba_scan_fwd(ctypes.byref(ctx["ptrs"]), ctypes.byref(ctx["shape"]),
                               ctypes.byref(ctx["st"]) if strides else None, ctx["dtype"],
                               ctx["flags"], None)
@@ -105,6 +110,12 @@ CASES = [
     # the flag check comes before the pointer checks: a known flag reaches the NULL-pointer error
     ("zoh_flag_is_known", lambda c: (c.__setitem__("flags", scan.ZOH_B), setattr(c["ptrs"], "u", None)), -1),
     ("both_forced", _flags(scan.FORCE_GENERIC | scan.FORCE_TILED), -6),
+    ("chunked_and_lanes_forced", _flags(scan.FORCE_CHUNKED | scan.FORCE_LANES), -6),
+    # the chunked kernel: 16 states, the Euler input term, no saved states
+    ("chunked_forced_32_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_CHUNKED),
+                                            setattr(c["shape"], "dstate", 32)), -8),
+    ("chunked_forced_zoh", _flags(scan.DELTA_SOFTPLUS | scan.FORCE_CHUNKED | scan.ZOH_B), -8),
+    ("checkpoints_with_chunked", lambda c: _ck_ws(c, 1 << 20, extra=scan.FORCE_CHUNKED), -8),
     ("lanes_and_tiled_forced", _flags(scan.FORCE_LANES | scan.FORCE_TILED), -6),
     # the lane-per-state kernels take 16, 32 or 64 states, the Euler input term, 31-bit row offsets
     ("lanes_forced_8_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
@@ -126,12 +137,36 @@ CASES = [
     ("checkpoints_24_states", lambda c: (_ck_ws(c, 1 << 20), setattr(c["shape"], "dstate", 24)), -8),
     ("checkpoints_with_zoh", lambda c: _ck_ws(c, 1 << 20, extra=scan.ZOH_B), -8),
     ("checkpoints_alias_y", lambda c: (_ck_ws(c, 1 << 20), setattr(c["ptrs"], "workspace", c["ptrs"].y)), -6),
+    # with SAVE_CHECKPOINTS the workspace is an output: it may not overlap an input either
+    ("checkpoints_alias_u", lambda c: (_ck_ws(c, 1 << 20), setattr(c["ptrs"], "workspace", c["ptrs"].u + 8)), -6),
+    ("checkpoints_alias_B", lambda c: (_ck_ws(c, 1 << 20), setattr(c["ptrs"], "workspace", c["ptrs"].B)), -6),
+    ("checkpoints_alias_h0", lambda c: (_ck_ws(c, 1 << 20), setattr(c["ptrs"], "workspace", c["ptrs"].h0 - 64)), -6),
 ]
 
 
 @pytest.mark.parametrize("name,mutate,code", CASES, ids=[c[0] for c in CASES])
 def test_invalid_arguments_are_rejected(name, mutate, code):
     assert fake_call(mutate) == code
+    # the kernel query validates the same way and reports the same error
+    assert fake_call(mutate, query=True) == code
+
+
+@pytest.mark.parametrize("extra,dstate,expect", [
+    (scan.FORCE_GENERIC, 16, 1), (scan.FORCE_TILED, 16, 2), (scan.FORCE_LANES, 16, 3),
+    (scan.FORCE_CHUNKED, 16, 4), (0, 24, 2), (0, 100, 1), (scan.ZOH_B, 16, 2),
+    (scan.FORCE_LANES, 64, 3)])
+def test_kernel_query(extra, dstate, expect):
+    """mamba_scan_fwd_kernel names the kernel a call would run (the forced one, or the default
+    order); it launches nothing, so it answers without a GPU too."""
+    def m(c):
+        c["flags"] = scan.DELTA_SOFTPLUS | extra
+        c["shape"].dstate = dstate
+        for k in ("B", "C"):
+            setattr(c["st"], k, (ctypes.c_int64 * 3)(dstate * 40, 40, 1))
+        for k in ("h0",):
+            setattr(c["st"], k, (ctypes.c_int64 * 3)(3 * dstate, dstate, 1))
+        c["st"].A = (ctypes.c_int64 * 2)(dstate, 1)
+    assert fake_call(m, query=True) == expect
 
 
 def test_null_struct_pointers_are_rejected():
@@ -150,7 +185,9 @@ def test_strerror_and_workspace_query():
         assert len(lib.mamba_scan_strerror(code)) > 5
     assert lib.mamba_scan_strerror(-1000) == b"unknown error code"
     ok = scan.Shape(8, 1536, 2048, 16)
-    assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok), scan.BF16, 0) >= 0
+    # no forward kernel uses scratch memory: only the saved states need a workspace
+    assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok), scan.BF16, 0) == 0
+    assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok), scan.BF16, scan.FORCE_CHUNKED) == 0
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(scan.Shape(0, 1, 1, 1)), 0, 0) == -2
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok), 3, 0) == -4
     # saved segment states: (batch, dim, ceil(len/16), dstate) fp32
@@ -232,6 +269,11 @@ def test_backward_workspace_query():
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(0, 1, 1, 1)), 0, 0) == -2
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 3, 0) == -4
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 0, 1 << 1) == -6
+    # given the forward's saved states, the backward needs no room for recomputed ones
+    with_ck = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), scan.BF16,
+                                                 scan.DELTA_SOFTPLUS | scan.SAVE_CHECKPOINTS)
+    assert 0 < with_ck < n
+    assert n - with_ck >= ok.batch * ok.dim * ((ok.len + 15) // 16) * 16 * 4
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(1, 1, 1, 300)), 0, 0) == -5
 
 

@@ -29,28 +29,55 @@ def test_traffic_is_reported_only_for_the_profiled_sources():
     assert bench.resolved_kernel(w3, "auto") == "lanes"
     assert bench.resolved_kernel(w3, "auto", zoh=True) == "tiled"
     assert bench.resolved_kernel(workloads.WORKLOADS[5], "auto") == "lanes"
+    # few long rows: the chunked kernel (4 x 1024 channels of 100 000 steps)
+    assert bench.resolved_kernel(workloads.WORKLOADS[4], "auto") == "chunked"
     assert bench.measured_traffic(w3, "generic") is None
     assert bench.measured_traffic(w3, "auto", zoh=True) is None
     assert bench.measured_traffic(workloads.WORKLOADS[4], "auto") is None
 
 
 def test_backward_traffic_records_match_the_sources():
-    """The backward's rocprofv3 traffic records (recomputing / from saved states) were taken on
-    the current scan_bwd sources and are reported for the Mamba-130m workload only."""
+    """The backward's rocprofv3 traffic records (recomputing / from saved states) are reported only
+    while the scan_bwd sources they were taken on are unchanged, and for the Mamba-130m workload
+    only."""
     import json
 
     import bench
     from selective_state_space_29_amd import workloads
 
     w3 = workloads.WORKLOADS[3]
+    recs = {}
     for ck in (False, True):
         with open(bench.BWD_TRAFFIC_RECORDS[ck][0]) as f:
             rec = json.load(f)
-        assert rec["source_sha256"] == bench.kernel_source_hash(ck, bench.BWD_TRAFFIC_RECORDS)
-        assert bench.measured_bwd_traffic(w3, ck) == rec["traffic_bytes_per_launch"] > 0
+        current = rec["source_sha256"] == bench.kernel_source_hash(ck, bench.BWD_TRAFFIC_RECORDS)
+        expect = rec["traffic_bytes_per_launch"] if current else None
+        assert bench.measured_bwd_traffic(w3, ck) == expect
         assert bench.measured_bwd_traffic(workloads.WORKLOADS[5], ck) is None
+        recs[ck] = rec["traffic_bytes_per_launch"]
     # starting from the saved states neither writes nor re-reads them
-    assert bench.measured_bwd_traffic(w3, True) < bench.measured_bwd_traffic(w3, False)
+    assert 0 < recs[True] < recs[False]
+
+
+def test_issue_floor_arithmetic():
+    """The issue floor: element work at the 4 FMA : 1 exp mix rate, row-step work additively;
+    co_issue compares the additive time of a unit with the mix's measured time."""
+    import bench
+    from selective_state_space_29_amd import workloads
+
+    w3 = workloads.WORKLOADS[3]
+    rates = {"fma_T_lane_ops_per_s": 50.0, "exp_T_lane_ops_per_s": 20.0,
+             "dpp_mul_T_lane_ops_per_s": 35.0, "mix_4fma_1exp_T_units_per_s": 8.0}
+    f = bench.issue_floor(w3, rates, 100.0)
+    rows = w3.rows * w3.seqlen
+    trans = bench.transcendentals_per_launch(w3)
+    assert trans == w3.elements + rows * 4  # softplus (exp, log) and gate (exp, rcp) per row-step
+    expect = (w3.elements / 8e12 + (trans - w3.elements) / 20e12
+              + rows * bench.VALU_OPS_PER_ROW_STEP / 50e12) * 1e6
+    assert abs(f["floor_us"] - round(expect, 2)) < 0.011
+    assert abs(f["co_issue_4fma_1exp"] - round((4 / 50 + 1 / 20) * 8, 3)) < 1e-9
+    assert abs(f["frac"] - round(expect / 100.0, 4)) < 1e-4
+    assert bench.issue_floor(w3, None, 100.0) is None
 
 
 def test_sampled_indices_exist_for_every_workload():

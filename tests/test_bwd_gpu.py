@@ -1,10 +1,12 @@
 """GPU parity of the backward pass (``mamba_scan_bwd`` through the C ABI) against the fp64 backward
 oracle on identical inputs.
 
-Bar: max|g - r| / (1 + |r|) <= 2e-3 for every gradient. The GPU accumulates in fp32: the reverse
-recurrence over up to 2048 steps like the forward, plus sums over up to 1536 channels (dB, dC) and
-over batch x steps (dA, dD, dbias); the oracle sums in fp64. Inputs are the same bits on both
-sides (bf16 cases are bf16 on both sides).
+Bar: max|g - r| / (1 + |r|) over every gradient, the forward's bars: <= 1e-4 when u, delta, z,
+B, C are fp32 and <= 2e-3 when they are bf16 (the same bits on both sides in either case). The
+GPU accumulates in fp32 (the reverse recurrence over up to L steps, sums over channels for dB, dC
+and over batch x steps for dA, dD, dbias, all in a fixed order) and the oracle in fp64; the
+inputs' storage precision does not enter the difference, so the fp32 bar is the forward's fp32
+bar, not the bf16 one.
 """
 
 import numpy as np
@@ -17,7 +19,12 @@ from selective_state_space_29_amd import scan, workloads
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-3
+TOL = 2e-3        # bf16 storage
+TOL_F32 = 1e-4    # fp32 storage
+
+
+def tol_of(x):
+    return TOL_F32 if x["u"].dtype == np.float32 else TOL
 NAMES = ("u", "delta", "z", "B", "C", "A", "D", "delta_bias", "h0")
 
 
@@ -40,7 +47,8 @@ def _grads_oracle(x, dy, dlast, softplus, h0=None):
         glast=None if dlast is None else dlast.astype(np.float32).astype(np.float64))
 
 
-def _check(x, softplus=True, with_h0=False, with_dlast=True, seed=0, tol=TOL):
+def _check(x, softplus=True, with_h0=False, with_dlast=True, seed=0, tol=None):
+    tol = tol_of(x) if tol is None else tol
     batch, dim, L = x["u"].shape
     N = x["A"].shape[1]
     rng = np.random.default_rng(seed)
@@ -54,6 +62,7 @@ def _check(x, softplus=True, with_h0=False, with_dlast=True, seed=0, tol=TOL):
             continue
         assert np.all(np.isfinite(gg[k])), k
         err = gu.rel_err(gg[k], gr[k])
+        print(f"  d{k}: max rel err {err:.3e} (bar {tol:g})", flush=True)
         assert err <= tol, f"d{k}: max rel err {err:.3g}"
     return gg
 
@@ -118,17 +127,18 @@ def test_state_blocks_are_independent():
     assert np.array_equal(full["h0"][..., :16], part["h0"])
 
 
-def test_wide_state_workload_sampled():
-    """Full-size backward of the 64-state workload (one launch per block of 16 states); the oracle
-    checks every channel-local gradient of sampled channels: du, ddelta, dz and dh0 of each
-    (batch, channel) row, and dA, dD, dbias of the channel (summed over the batch). dB and dC
-    sum over all channels and are checked at the smaller sizes above."""
-    w = workloads.WORKLOADS[5]
-    print(f"backward parity, workload 5: {w.name} (sampled channels)", flush=True)
+@pytest.mark.parametrize("wid", [4, 5])
+def test_large_workload_sampled_channels(wid):
+    """Full-size backward of the genomic workload (L = 100 000) and of the 64-state one (one launch
+    per block of 16 states); the oracle checks every channel-local gradient of sampled channels:
+    du, ddelta, dz and dh0 of each (batch, channel) row, and dA, dD, dbias of the channel (summed
+    over the batch). dB and dC sum over all channels and are checked at the smaller sizes above."""
+    w = workloads.WORKLOADS[wid]
+    print(f"backward parity, workload {wid}: {w.name} (sampled channels)", flush=True)
     x = workloads.make_inputs(w)
     g = {k: gu.to_dev(v) if isinstance(v, np.ndarray) else v for k, v in x.items()}
     del x
-    gen = torch.Generator(device="cuda:0").manual_seed(29505)
+    gen = torch.Generator(device="cuda:0").manual_seed(29500 + wid)
     dy = torch.randn((w.batch, w.dim, w.seqlen), device="cuda:0", generator=gen)
     dlast = torch.randn((w.batch, w.dim, w.dstate), device="cuda:0", generator=gen)
     out = scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"], z=g["z"],
@@ -202,5 +212,5 @@ def test_autograd_function_matches_the_oracle():
     loss.backward()
     gr = _grads_oracle(x, W, V, True, h0)
     for k in ("u", "delta", "z", "B", "C", "A", "D", "delta_bias"):
-        assert gu.rel_err(t[k].grad.cpu().numpy(), gr[k]) <= TOL, k
-    assert gu.rel_err(th0.grad.cpu().numpy(), gr["h0"]) <= TOL
+        assert gu.rel_err(t[k].grad.cpu().numpy(), gr[k]) <= TOL_F32, k
+    assert gu.rel_err(th0.grad.cpu().numpy(), gr["h0"]) <= TOL_F32

@@ -4,8 +4,8 @@ ways: store the states, or recompute them).
 
   * checkpoint k is the state before step 16 k: the oracle's last state of the first 16 k steps
     (h0 for k = 0), to the forward bar, and the GPU's own last state of that prefix, bit for bit;
-  * the backward given them matches the fp64 backward oracle to the backward bar (2e-3), and the
-    backward that recomputes them to 1e-5;
+  * the backward given them matches the fp64 backward oracle to the backward bars (1e-4 for fp32
+    inputs, 2e-3 for bf16 inputs), and the backward that recomputes them to 1e-5;
   * the autograd function saves them where the lane-per-state forward runs and falls back to
     recomputation where it does not.
 """
@@ -91,12 +91,13 @@ def test_backward_from_checkpoints(idx):
         x["u"], x["delta"], x["A"], x["B"], x["C"], dy.astype(np.float64), D=x["D"], z=x["z"],
         delta_bias=x["delta_bias"], delta_softplus=True, h0=None if h0 is None else h0.astype(np.float64),
         glast=dlast.astype(np.float64))
+    tol = gu.FP32_TOL if dtype == "f32" else gu.BF16_TOL
     same = True
     for k, v in with_ck.items():
         a, b = v.cpu().numpy(), without[k].cpu().numpy()
         assert np.all(np.isfinite(a)), k
         if k in ref:
-            assert gu.rel_err(a, ref[k]) <= 2e-3, f"d{k} against the oracle"
+            assert gu.rel_err(a, ref[k]) <= tol, f"d{k} against the oracle"
         assert gu.rel_err(a, b) <= 1e-5, f"d{k} with and without checkpoints"
         same = same and np.array_equal(a, b)
     print(f"   bit-identical to the recomputing backward: {same}", flush=True)
