@@ -98,6 +98,8 @@ typedef enum mamba_scan_dtype {
 #define MAMBA_SCAN_ERR_UNSUPPORTED (-8) /* a forced kernel, or SAVE_CHECKPOINTS, cannot run
                                            this shape/alignment */
 #define MAMBA_SCAN_ERR_WORKSPACE (-9) /* workspace too small for the requested plan */
+#define MAMBA_SCAN_ERR_SCRATCH (-10)  /* mamba_scan_bwd_static: the call needs more workspace than
+                                         MAMBA_SCAN_STATIC_SCRATCH_BYTES */
 
 #define MAMBA_SCAN_MAX_DSTATE 256
 
@@ -227,6 +229,27 @@ typedef struct mamba_scan_bwd_ptrs {
 
 int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
                    uint32_t flags, void* stream);
+
+/*
+ * Backward pass that allocates nothing (ABI 7), for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight training or serving loops, harnesses that forbid
+ * allocation. The same operation, arguments and results as mamba_scan_bwd (bit for bit), except
+ * that the workspace is the library's own static buffer of MAMBA_SCAN_STATIC_SCRATCH_BYTES on each
+ * device: p->workspace must be NULL and p->workspace_bytes 0 (MAMBA_SCAN_ERR_ARGS otherwise). A
+ * call whose workspace (mamba_scan_bwd_workspace_bytes, queried with MAMBA_SCAN_SAVE_CHECKPOINTS
+ * when checkpoints are given) exceeds it returns MAMBA_SCAN_ERR_SCRATCH before enqueuing anything.
+ * No call allocates or frees memory; the first call on a device looks up that device's buffer.
+ *  - The buffer of a GPU is held from the library's first use on it until the process ends.
+ *  - Every call on one GPU uses that GPU's buffer: calls that overlap in time on the same GPU
+ *    (on different streams, or from different host threads) race and must not be made; calls
+ *    one after another on a stream are fine. The buffer keeps the last call's contents; the
+ *    backward writes every part of it that it reads, so nothing has to be cleared.
+ * With checkpoints from the forward the Mamba-130m layer (batch 8, dim 1536, dstate 16,
+ * len 2048) needs 53 MB and fits; recomputing the states it needs 154 MB and does not.
+ */
+#define MAMBA_SCAN_STATIC_SCRATCH_BYTES (64ll << 20)
+int mamba_scan_bwd_static(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
+                          uint32_t flags, void* stream);
 
 /* Workspace bytes mamba_scan_bwd needs for this shape (> 0), or a negative error code. Flags:
  * MAMBA_SCAN_DELTA_SOFTPLUS (ignored for the size) and MAMBA_SCAN_SAVE_CHECKPOINTS, meaning that

@@ -15,6 +15,7 @@
 #include "scan_tiled.hpp"  // aligned
 
 #include <atomic>
+#include <mutex>
 
 using namespace mscan;
 
@@ -211,6 +212,46 @@ int choose_kernel(const ScanParams& q, uint32_t flags, bool bf16) {
     return MAMBA_SCAN_KERNEL_GENERIC;
 }
 
+int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
+                   uint32_t flags, void* stream);
+
+}  // namespace
+
+// The static workspace of mamba_scan_bwd_static: every GPU the library runs on holds its own copy
+// until the process ends. In host code this name is only a handle for hipGetSymbolAddress; the
+// device address it resolves to, per device, is what kernels and copies are given.
+static __device__ __align__(256) unsigned char scratch[MAMBA_SCAN_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    int rc = MAMBA_SCAN_OK;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The device address of the current device's scratch, looked up once per device (with that
+// device current) on the first call that needs it.
+int device_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MAMBA_SCAN_ERR_LAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return MAMBA_SCAN_ERR_UNSUPPORTED;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            slot.rc = MAMBA_SCAN_ERR_LAUNCH;
+            return;
+        }
+        slot.ptr = ptr;
+    });
+    if (slot.rc != MAMBA_SCAN_OK) return slot.rc;
+    *out = slot.ptr;
+    return MAMBA_SCAN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,6 +272,9 @@ const char* mamba_scan_strerror(int code) {
         case MAMBA_SCAN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
         case MAMBA_SCAN_ERR_UNSUPPORTED: return "the forced kernel cannot handle this shape or alignment";
         case MAMBA_SCAN_ERR_WORKSPACE: return "workspace too small";
+        case MAMBA_SCAN_ERR_SCRATCH:
+            return "the call needs more workspace than the static scratch buffer holds "
+                   "(MAMBA_SCAN_STATIC_SCRATCH_BYTES)";
         default: return "unknown error code";
     }
 }
@@ -255,6 +299,33 @@ int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dty
 }
 
 int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
+                   uint32_t flags, void* stream) {
+    return backward_entry(p, s, dtype, flags, stream);
+}
+
+int mamba_scan_bwd_static(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
+                          uint32_t flags, void* stream) {
+    if (!p || !s) return MAMBA_SCAN_ERR_NULL;
+    if (p->workspace || p->workspace_bytes != 0) return MAMBA_SCAN_ERR_ARGS;  // the scratch is the library's
+    if (flags & ~MAMBA_SCAN_DELTA_SOFTPLUS) return MAMBA_SCAN_ERR_ARGS;
+    const int64_t need =
+        mamba_scan_bwd_workspace_bytes(s, dtype, flags | (p->checkpoints ? MAMBA_SCAN_SAVE_CHECKPOINTS : 0u));
+    if (need < 0) return (int)need;
+    if (need > MAMBA_SCAN_STATIC_SCRATCH_BYTES) return MAMBA_SCAN_ERR_SCRATCH;
+    void* ws = nullptr;
+    const int rc = device_scratch(&ws);
+    if (rc != MAMBA_SCAN_OK) return rc;
+    mamba_scan_bwd_ptrs q = *p;
+    q.workspace = ws;
+    q.workspace_bytes = MAMBA_SCAN_STATIC_SCRATCH_BYTES;
+    return backward_entry(&q, s, dtype, flags, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
                    uint32_t flags, void* stream) {
     if (!p || !s) return MAMBA_SCAN_ERR_NULL;
     if (flags & ~MAMBA_SCAN_DELTA_SOFTPLUS) return MAMBA_SCAN_ERR_ARGS;
@@ -302,6 +373,10 @@ int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     const bool sp = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) != 0;
     return launch_bwd_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
 }
+
+}  // namespace
+
+extern "C" {
 
 int mamba_block_upstream(const mamba_upstream_ptrs* p, const mamba_upstream_shape* s, mamba_scan_dtype dtype,
                          void* stream) {

@@ -99,6 +99,9 @@ def load_library(path: str = LIB_PATH):
     lib.mamba_scan_bwd.restype = ctypes.c_int
     lib.mamba_scan_bwd.argtypes = [ctypes.POINTER(BwdPtrs), ctypes.POINTER(Shape), ctypes.c_int,
                                    ctypes.c_uint32, _P]
+    lib.mamba_scan_bwd_static.restype = ctypes.c_int
+    lib.mamba_scan_bwd_static.argtypes = [ctypes.POINTER(BwdPtrs), ctypes.POINTER(Shape), ctypes.c_int,
+                                          ctypes.c_uint32, _P]
     lib.mamba_scan_bwd_workspace_bytes.restype = _I64
     lib.mamba_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, ctypes.c_uint32]
     lib.mamba_block_upstream.restype = ctypes.c_int
@@ -290,13 +293,15 @@ def _check_checkpoints(ck, batch, dim, L, N, dev):
 
 
 def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False,
-                       h0=None, dlast_state=None, want_dh0=True, checkpoints=None):
+                       h0=None, dlast_state=None, want_dh0=True, checkpoints=None, static_scratch=False):
     """Gradients of the scan (``mamba_scan_bwd``) for incoming gradients dy (batch, dim, L) and,
     optionally, dlast_state (batch, dim, N). Inputs as for ``selective_scan_fn``; all tensors are
     made contiguous first. Returns a dict of fp32 gradients: u, delta, B, C, A, and z, D,
     delta_bias when given, h0 when ``want_dh0`` (the gradient of the initial state, which is zero
     when h0 is None). ``checkpoints``: the segment states that ``selective_scan_fn(checkpoints_out=)``
-    saved for the same inputs; the backward then does not recompute them.
+    saved for the same inputs; the backward then does not recompute them. ``static_scratch``: call
+    ``mamba_scan_bwd_static``, whose workspace is the library's own static per-device buffer (no
+    workspace is allocated here; calls overlapping in time on one GPU must not be made).
     """
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):
@@ -340,11 +345,14 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     shape = Shape(batch, dim, L, N)
     dtype = BF16 if u.dtype == torch.bfloat16 else F32
     flags = DELTA_SOFTPLUS if delta_softplus else 0
-    ws_bytes = lib.mamba_scan_bwd_workspace_bytes(
-        ctypes.byref(shape), dtype, flags | (SAVE_CHECKPOINTS if checkpoints is not None else 0))
-    if ws_bytes < 0:
-        raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
-    ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev)
+    if static_scratch:
+        ws, ws_bytes = None, 0
+    else:
+        ws_bytes = lib.mamba_scan_bwd_workspace_bytes(
+            ctypes.byref(shape), dtype, flags | (SAVE_CHECKPOINTS if checkpoints is not None else 0))
+        if ws_bytes < 0:
+            raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
+        ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev)
     ptrs = BwdPtrs(_ptr(u), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(delta_bias),
                    _ptr(h0), _ptr(dy), _ptr(dlast_state), _ptr(g["u"]), _ptr(g["delta"]), _ptr(g.get("z")),
                    _ptr(g["B"]), _ptr(g["C"]), _ptr(g["A"]), _ptr(g.get("D")), _ptr(g.get("delta_bias")),
@@ -354,13 +362,15 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
         ptrs.checkpoints = _ptr(checkpoints)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        rc = lib.mamba_scan_bwd(ctypes.byref(ptrs), ctypes.byref(shape), dtype, flags, stream)
+        entry = lib.mamba_scan_bwd_static if static_scratch else lib.mamba_scan_bwd
+        rc = entry(ctypes.byref(ptrs), ctypes.byref(shape), dtype, flags, stream)
     if rc != 0:
         err = MambaScanError(rc, strerror(rc))
-        if rc in (-1, -2, -3, -4, -5, -6, -8, -9):
+        if rc in (-1, -2, -3, -4, -5, -6, -8, -9, -10):
             raise ValueError(str(err)) from err
         raise err
-    ws.record_stream(torch.cuda.current_stream(dev))
+    if ws is not None:
+        ws.record_stream(torch.cuda.current_stream(dev))
     return g
 
 

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_header_declares_the_entry_points():
     assert header_functions() == ["mamba_block_upstream", "mamba_scan_abi_version", "mamba_scan_bwd",
-                                  "mamba_scan_bwd_workspace_bytes", "mamba_scan_fwd",
+                                  "mamba_scan_bwd_static", "mamba_scan_bwd_workspace_bytes", "mamba_scan_fwd",
                                   "mamba_scan_fwd_kernel", "mamba_scan_strerror",
                                   "mamba_scan_workspace_bytes"]
 
@@ -245,6 +245,30 @@ BWD_CASES = [
 @pytest.mark.parametrize("name,mutate,code", BWD_CASES, ids=[c[0] for c in BWD_CASES])
 def test_backward_invalid_arguments_are_rejected(name, mutate, code):
     assert fake_bwd(mutate) == code
+
+
+def test_static_backward_refusals():
+    """mamba_scan_bwd_static takes no workspace (its own static buffer is used) and refuses, before
+    touching the device, a caller workspace, unknown flags and problems larger than the buffer."""
+    lib = scan.load_library()
+
+    def call(mutate, shape=(2, 3, 40, 16)):
+        ptrs = scan.BwdPtrs(**{n: (1 << 40) + (i + 1) * (1 << 32) for i, (n, _) in enumerate(scan.BwdPtrs._fields_)
+                               if n not in ("workspace", "workspace_bytes", "checkpoints")})
+        ptrs.workspace, ptrs.workspace_bytes, ptrs.checkpoints = None, 0, None
+        shp = scan.Shape(*shape)
+        flags = scan.DELTA_SOFTPLUS
+        ctx = dict(ptrs=ptrs, flags=flags)
+        mutate(ctx)
+        return lib.mamba_scan_bwd_static(ctypes.byref(ctx["ptrs"]), ctypes.byref(shp), scan.BF16, ctx["flags"], None)
+
+    assert call(lambda c: setattr(c["ptrs"], "workspace", (1 << 40) + (30 << 32))) == -6
+    assert call(lambda c: setattr(c["ptrs"], "workspace_bytes", 64)) == -6
+    assert call(lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.SAVE_CHECKPOINTS)) == -6
+    # the Mamba-130m layer recomputing its states needs 154 MB of workspace
+    assert call(lambda c: None, shape=(8, 1536, 2048, 16)) == -10
+    assert lib.mamba_scan_bwd_static(None, None, 0, 0, None) == -1
+    assert len(lib.mamba_scan_strerror(-10)) > 20
 
 
 def test_backward_workspace_for_wide_states():
