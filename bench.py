@@ -44,6 +44,8 @@ SLOTS_PER_ELEMENT_FWD_RECURRENCE = 7  # one forward recurrence step of the backw
 TRAFFIC_RECORDS = {
     "lanes": (os.path.join(ROOT, "profiles", "scan_ls_mamba130m_traffic.json"), ("common.hpp", "scan_ls.hpp")),
     "tiled": (os.path.join(ROOT, "profiles", "scan_tiled_mamba130m_traffic.json"), ("common.hpp", "scan_tiled.hpp")),
+    "chunked": (os.path.join(ROOT, "profiles", "scan_chunked_genomic100k_traffic.json"),
+                ("common.hpp", "scan_ls.hpp", "scan_lp.hpp")),
 }
 # the same for the backward's scan kernel at the Mamba-130m shape: recomputing the segment states,
 # or starting from the forward's saved ones
@@ -147,16 +149,14 @@ def measured_traffic(w, kernel, zoh=False):
     kernel that runs, or None when there is none for it, it was taken on other kernel sources,
     or on another workload."""
     k = resolved_kernel(w, kernel, zoh)
-    if k == "chunked":
-        return None
-    if w.wid != 3 or zoh or k not in TRAFFIC_RECORDS:
+    if zoh or k not in TRAFFIC_RECORDS:
         return None
     try:
         with open(TRAFFIC_RECORDS[k][0]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash(k):
+    if rec.get("source_sha256") != kernel_source_hash(k) or rec.get("workload", "").split(":")[0] != w.name:
         return None
     return rec.get("traffic_bytes_per_launch")
 

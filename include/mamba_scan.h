@@ -69,10 +69,10 @@ typedef enum mamba_scan_dtype {
  * otherwise. ABI version 6. */
 #define MAMBA_SCAN_SAVE_CHECKPOINTS (1u << 3)
 /* Kernel selection, for testing and tuning; at most one of these bits (MAMBA_SCAN_ERR_ARGS
- * otherwise). Default (none): with 16 states, at least 1024 steps and too few (batch, channel)
- * rows to give every SIMD of the GPU two waves of the lane-per-state kernel, the chunked kernel;
- * otherwise the lane-per-state kernel where it can run, else the tiled one, else the generic
- * one. */
+ * otherwise). Default (none): with 16 states, the short-call kernel for at most 4 steps and the
+ * chunked kernel for at least 1024 steps when too few (batch, channel) rows would give every SIMD
+ * of the GPU two waves of the lane-per-state kernel; otherwise the lane-per-state kernel where it
+ * can run, else the tiled one, else the generic one. */
 #define MAMBA_SCAN_FORCE_GENERIC (1u << 8) /* one lane per row, any shape and alignment */
 #define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
 #define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one lane per (channel, state): dstate 16, 32 or
@@ -84,7 +84,14 @@ typedef enum mamba_scan_dtype {
  * run. Results agree with the sequential kernels to rounding (not bit for bit); a sequence split
  * at a multiple of 64 steps and resumed from last_state gives the same bits as one call. */
 #define MAMBA_SCAN_FORCE_CHUNKED (1u << 11)
-#define MAMBA_SCAN_KNOWN_FLAGS 0xF0Fu
+/* Short calls (ABI 7): one lane per (channel, state), each step in registers with no LDS staging
+ * and no barrier; for recurrent decode (one or a few steps per call from the previous call's
+ * last_state, "告别'炼丹'…" §2.1 times single-step inference). dstate 16, no ZOH_B, no
+ * SAVE_CHECKPOINTS, at most 64 steps; the default for calls of at most 4 steps. Its states are the
+ * same bits as the lane-per-state kernel's; y may differ in the last bits (the 16 states' terms
+ * are added in another order). */
+#define MAMBA_SCAN_FORCE_STEP (1u << 12)
+#define MAMBA_SCAN_KNOWN_FLAGS 0x1F0Fu
 
 /* error codes */
 #define MAMBA_SCAN_OK 0
@@ -148,6 +155,7 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s,
 #define MAMBA_SCAN_KERNEL_TILED 2
 #define MAMBA_SCAN_KERNEL_LANES 3
 #define MAMBA_SCAN_KERNEL_CHUNKED 4
+#define MAMBA_SCAN_KERNEL_STEP 5
 int mamba_scan_fwd_kernel(const mamba_scan_ptrs* p, const mamba_scan_shape* s,
                           const mamba_scan_strides* st, mamba_scan_dtype dtype, uint32_t flags);
 

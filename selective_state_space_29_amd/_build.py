@@ -46,8 +46,8 @@ def units():
 
 def build_hip(out: str = LIB, extra=(), jobs=None, incremental=False) -> str:
     """Compile every translation unit to an object in parallel, then link the shared library.
-    ``incremental``: skip units whose object is newer than every source and the header (for
-    development; a plain build compiles everything)."""
+    ``incremental``: skip units whose object is newer than every file its last compile read
+    (for development; a plain build compiles everything)."""
     from concurrent.futures import ThreadPoolExecutor
 
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -55,13 +55,23 @@ def build_hip(out: str = LIB, extra=(), jobs=None, incremental=False) -> str:
     os.makedirs(objdir, exist_ok=True)
     compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
 
-    newest = max(os.path.getmtime(f) for f in sources() + [HEADER])
+    def deps_of(obj, src):
+        """The files a unit was built from, from the dependency list its last compile wrote."""
+        try:
+            text = open(obj + ".d").read().replace("\\\n", " ")
+        except OSError:
+            return None
+        files = text.split(":", 1)[1].split() if ":" in text else []
+        return [f for f in files if os.path.exists(f)] or None
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src)[:-4] + ".o")
-        if incremental and os.path.exists(obj) and os.path.getmtime(obj) > newest:
-            return obj
-        subprocess.run([hipcc, *compile_flags, *extra, "-c", "-o", obj, src], check=True)
+        if incremental and os.path.exists(obj):
+            deps = deps_of(obj, src)
+            if deps and max(os.path.getmtime(f) for f in deps + [src]) < os.path.getmtime(obj):
+                return obj
+        subprocess.run([hipcc, *compile_flags, *extra, "-MMD", "-MF", obj + ".d", "-c", "-o", obj, src],
+                       check=True)
         return obj
 
     srcs = units()

@@ -19,6 +19,7 @@ bool tiled_can_run_f32(const ScanParams& q);
 int launch_ls_bf16(const ScanParams& q, hipStream_t stream);
 int launch_ls_f32(const ScanParams& q, hipStream_t stream);
 int launch_lp_any(const ScanParams& q, bool bf16, hipStream_t stream);
+int launch_step_any(const ScanParams& q, bool bf16, hipStream_t stream);
 
 inline int launch_tiled_any(const ScanParams& q, bool bf16, hipStream_t stream) {
     return bf16 ? launch_tiled_bf16(q, stream) : launch_tiled_f32(q, stream);

@@ -12,6 +12,7 @@
 #include "bwd_layout.hpp"
 #include "scan_lp.hpp"   // lp_eligible
 #include "scan_ls.hpp"   // ls_eligible
+#include "scan_step.hpp"  // step_eligible
 #include "scan_tiled.hpp"  // aligned
 
 #include <atomic>
@@ -66,8 +67,8 @@ int validate(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_sc
     if (!p || !s || !st) return MAMBA_SCAN_ERR_NULL;
     if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
     if (flags & ~MAMBA_SCAN_KNOWN_FLAGS) return MAMBA_SCAN_ERR_ARGS;
-    const uint32_t forced =
-        flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_LANES | MAMBA_SCAN_FORCE_CHUNKED);
+    const uint32_t forced = flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_LANES |
+                                     MAMBA_SCAN_FORCE_CHUNKED | MAMBA_SCAN_FORCE_STEP);
     if (forced & (forced - 1)) return MAMBA_SCAN_ERR_ARGS;  // at most one kernel may be forced
     if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
@@ -198,14 +199,17 @@ int check_checkpoint_workspace(const mamba_scan_ptrs* p, const mamba_scan_shape*
 int choose_kernel(const ScanParams& q, uint32_t flags, bool bf16) {
     const int64_t es = bf16 ? 2 : 4;
     if (q.ck) {  // the saved states come from the lane-per-state kernels only
-        if (flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_CHUNKED))
+        if (flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_CHUNKED |
+                     MAMBA_SCAN_FORCE_STEP))
             return MAMBA_SCAN_ERR_UNSUPPORTED;
         return ls_eligible(q, es) ? MAMBA_SCAN_KERNEL_LANES : MAMBA_SCAN_ERR_UNSUPPORTED;
     }
+    if (flags & MAMBA_SCAN_FORCE_STEP) return step_eligible(q) ? MAMBA_SCAN_KERNEL_STEP : MAMBA_SCAN_ERR_UNSUPPORTED;
     if (flags & MAMBA_SCAN_FORCE_CHUNKED) return lp_eligible(q, es) ? MAMBA_SCAN_KERNEL_CHUNKED : MAMBA_SCAN_ERR_UNSUPPORTED;
     if (flags & MAMBA_SCAN_FORCE_LANES) return ls_eligible(q, es) ? MAMBA_SCAN_KERNEL_LANES : MAMBA_SCAN_ERR_UNSUPPORTED;
     if (flags & MAMBA_SCAN_FORCE_TILED) return tiled_can_run_any(q, bf16) ? MAMBA_SCAN_KERNEL_TILED : MAMBA_SCAN_ERR_UNSUPPORTED;
     if (flags & MAMBA_SCAN_FORCE_GENERIC) return MAMBA_SCAN_KERNEL_GENERIC;
+    if (q.len <= kStepMaxLen && step_eligible(q)) return MAMBA_SCAN_KERNEL_STEP;
     if (prefer_chunked(q) && lp_eligible(q, es)) return MAMBA_SCAN_KERNEL_CHUNKED;
     if (ls_eligible(q, es)) return MAMBA_SCAN_KERNEL_LANES;
     if (tiled_can_run_any(q, bf16)) return MAMBA_SCAN_KERNEL_TILED;
@@ -452,6 +456,7 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const ma
     const int kernel = choose_kernel(q, flags, bf16);
     switch (kernel) {
         case MAMBA_SCAN_KERNEL_CHUNKED: return launch_lp_any(q, bf16, hs);
+        case MAMBA_SCAN_KERNEL_STEP: return launch_step_any(q, bf16, hs);
         case MAMBA_SCAN_KERNEL_LANES: return launch_ls_any(q, bf16, hs);
         case MAMBA_SCAN_KERNEL_TILED: return launch_tiled_any(q, bf16, hs);
         case MAMBA_SCAN_KERNEL_GENERIC: return launch_generic_any(q, bf16, hs);

@@ -30,6 +30,7 @@ FORCE_GENERIC = 1 << 8
 FORCE_TILED = 1 << 9
 FORCE_LANES = 1 << 10
 FORCE_CHUNKED = 1 << 11
+FORCE_STEP = 1 << 12
 
 _I64 = ctypes.c_int64
 _P = ctypes.c_void_p
@@ -137,7 +138,7 @@ def _s3(x, fallback=(0, 0, 1)):
     return (_I64 * 3)(*(_strides(x) if x is not None else fallback))
 
 
-KERNEL_NAMES = {1: "generic", 2: "tiled", 3: "lanes", 4: "chunked"}
+KERNEL_NAMES = {1: "generic", 2: "tiled", 3: "lanes", 4: "chunked", 5: "step"}
 
 
 def _fwd_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_state, h0, kernel, out,
@@ -187,9 +188,9 @@ def _fwd_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_s
             ls = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
         flags |= RETURN_LAST_STATE
     forced = {None: 0, "generic": FORCE_GENERIC, "tiled": FORCE_TILED, "lanes": FORCE_LANES,
-              "chunked": FORCE_CHUNKED}
+              "chunked": FORCE_CHUNKED, "step": FORCE_STEP}
     if kernel not in forced:
-        raise ValueError("kernel must be None, 'generic', 'tiled', 'lanes' or 'chunked'")
+        raise ValueError("kernel must be None, 'generic', 'tiled', 'lanes', 'chunked' or 'step'")
     flags |= forced[kernel]
 
     shape = Shape(batch, dim, L, N)
@@ -235,8 +236,9 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     u, delta, z: (batch, dim, L); B, C: (batch, N, L); one storage dtype for all five
     (torch.float32 or torch.bfloat16). A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N);
     these are taken in fp32. ``kernel``: None (library picks), "generic", "tiled", "lanes"
-    (one lane per (channel, state); 16, 32 or 64 states) or "chunked" (parallel along the
-    sequence: a wave per channel scanning 4 runs of each 64-step chunk; 16 states).
+    (one lane per (channel, state); 16, 32 or 64 states), "chunked" (parallel along the
+    sequence: a wave per channel scanning 4 runs of each 64-step chunk; 16 states) or "step"
+    (short calls such as decode, at most 64 steps; 16 states).
     ``checkpoints_out``: a contiguous fp32 (batch, dim, ceil(L/16), N) tensor that receives the
     state before every 16-step segment, for ``selective_scan_bwd(checkpoints=...)``
     (lane-per-state kernels only).

@@ -116,6 +116,13 @@ CASES = [
                                             setattr(c["shape"], "dstate", 32)), -8),
     ("chunked_forced_zoh", _flags(scan.DELTA_SOFTPLUS | scan.FORCE_CHUNKED | scan.ZOH_B), -8),
     ("checkpoints_with_chunked", lambda c: _ck_ws(c, 1 << 20, extra=scan.FORCE_CHUNKED), -8),
+    # the short-call kernel: 16 states, Euler, at most 64 steps, no saved states
+    ("step_forced_32_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_STEP),
+                                         setattr(c["shape"], "dstate", 32)), -8),
+    ("step_forced_65_steps", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_STEP),
+                                        setattr(c["shape"], "len", 65)), -8),
+    ("step_and_chunked_forced", _flags(scan.FORCE_STEP | scan.FORCE_CHUNKED), -6),
+    ("checkpoints_with_step", lambda c: _ck_ws(c, 1 << 20, extra=scan.FORCE_STEP), -8),
     ("lanes_and_tiled_forced", _flags(scan.FORCE_LANES | scan.FORCE_TILED), -6),
     # the lane-per-state kernels take 16, 32 or 64 states, the Euler input term, 31-bit row offsets
     ("lanes_forced_8_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
@@ -154,7 +161,7 @@ def test_invalid_arguments_are_rejected(name, mutate, code):
 @pytest.mark.parametrize("extra,dstate,expect", [
     (scan.FORCE_GENERIC, 16, 1), (scan.FORCE_TILED, 16, 2), (scan.FORCE_LANES, 16, 3),
     (scan.FORCE_CHUNKED, 16, 4), (0, 24, 2), (0, 100, 1), (scan.ZOH_B, 16, 2),
-    (scan.FORCE_LANES, 64, 3)])
+    (scan.FORCE_LANES, 64, 3), (scan.FORCE_STEP, 16, 5)])
 def test_kernel_query(extra, dstate, expect):
     """mamba_scan_fwd_kernel names the kernel a call would run (the forced one, or the default
     order); it launches nothing, so it answers without a GPU too."""

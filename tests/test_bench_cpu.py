@@ -20,10 +20,15 @@ def test_traffic_is_reported_only_for_the_profiled_sources():
     from selective_state_space_29_amd import workloads
 
     w3 = workloads.WORKLOADS[3]
+    by_name = {w.name: w for w in workloads.WORKLOADS.values()}
     for kernel, (path, _) in bench.TRAFFIC_RECORDS.items():
         rec = json.load(open(path))
+        w = by_name[rec["workload"].split(":")[0]]
         expect = rec["traffic_bytes_per_launch"] if rec["source_sha256"] == bench.kernel_source_hash(kernel) else None
-        assert bench.measured_traffic(w3, kernel) == expect, kernel
+        assert bench.measured_traffic(w, kernel) == expect, kernel
+        # a record applies to its own workload only
+        other = workloads.WORKLOADS[1]
+        assert bench.measured_traffic(other, kernel) is None, kernel
     # the default at 16 states is the lane-per-state kernel
     assert bench.measured_traffic(w3, "auto") == bench.measured_traffic(w3, "lanes")
     assert bench.resolved_kernel(w3, "auto") == "lanes"
@@ -33,7 +38,9 @@ def test_traffic_is_reported_only_for_the_profiled_sources():
     assert bench.resolved_kernel(workloads.WORKLOADS[4], "auto") == "chunked"
     assert bench.measured_traffic(w3, "generic") is None
     assert bench.measured_traffic(w3, "auto", zoh=True) is None
-    assert bench.measured_traffic(workloads.WORKLOADS[4], "auto") is None
+    # the genomic workload runs the chunked kernel, whose record is taken there
+    assert bench.measured_traffic(workloads.WORKLOADS[4], "auto") == bench.measured_traffic(
+        workloads.WORKLOADS[4], "chunked")
 
 
 def test_backward_traffic_records_match_the_sources():

@@ -55,8 +55,8 @@ def test_checkpoints_are_the_prefix_states(idx):
     h0 = np.random.default_rng(idx).standard_normal((batch, dim, N)).astype(np.float32) if with_h0 else None
     y, ls, ck = _forward_with_checkpoints(x, h0)
     ck = ck.cpu().numpy()
-    # the outputs are those of the forward without checkpoints, bit for bit
-    y2, ls2 = gu.gpu_scan(x, h0=h0)
+    # the outputs are those of the same (lane-per-state) kernel without checkpoints, bit for bit
+    y2, ls2 = gu.gpu_scan(x, h0=h0, kernel="lanes")
     assert np.array_equal(y, y2) and np.array_equal(ls, ls2)
     tol = gu.FP32_TOL if dtype == "f32" else gu.BF16_TOL
     start = np.zeros((batch, dim, N)) if h0 is None else h0
@@ -67,7 +67,7 @@ def test_checkpoints_are_the_prefix_states(idx):
         _, lr = gu.oracle_scan(pre, h0=h0)
         err = gu.rel_err(ck[:, :, k, :], lr)
         assert err <= tol, f"checkpoint {k}: {err:.3g}"
-        _, lg = gu.gpu_scan(pre, h0=h0)
+        _, lg = gu.gpu_scan(pre, h0=h0, kernel="lanes")
         assert np.array_equal(ck[:, :, k, :], lg), f"checkpoint {k} differs from the prefix scan"
 
 

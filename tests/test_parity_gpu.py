@@ -18,8 +18,8 @@ from selective_state_space_29_amd import scan, workloads
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = [None, "generic", "tiled", "lanes", "chunked"]
-FORCED = ("tiled", "lanes", "chunked")  # forced kernels that may refuse a case (-8)
+KERNELS = [None, "generic", "tiled", "lanes", "chunked", "step"]
+FORCED = ("tiled", "lanes", "chunked", "step")  # forced kernels that may refuse a case (-8)
 
 
 def _log(msg):

@@ -131,3 +131,23 @@ def test_decode_calls_captured_in_a_graph_replay_exactly():
         torch.cuda.synchronize()
         assert torch.equal(torch.cat(ys, -1), y_eager), f"replay {rep}"
         assert torch.equal(hs[L % 2], ls_eager), f"replay {rep}"
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 4, 7])
+def test_short_call_kernel_carries_the_same_state(chunk):
+    """The short-call kernel (the default for calls of at most 4 steps) advances the state with
+    the lane-per-state kernel's arithmetic: decoding a sequence in calls of `chunk` steps gives
+    the last state of the lane-per-state kernel fed the same pieces bit for bit, and y to within
+    the order of the sum over states."""
+    x = gu.case(67 + chunk, 2, 70, 16, 48, dtype="bf16")
+    g = _dev_case(x)
+    cuts = list(range(0, 48, chunk)) + [48]
+    y_s, ls_s = _stream(g, cuts, "step")
+    y_l, ls_l = _stream(g, cuts, "lanes")
+    assert np.array_equal(ls_s, ls_l)
+    assert gu.rel_err(y_s, y_l) <= 1e-6
+    if chunk <= 4:  # the library's own choice for such calls: the short-call kernel
+        y_a, ls_a = _stream(g, cuts, None)
+        assert np.array_equal(y_a, y_s) and np.array_equal(ls_a, ls_s)
+    yr, lr = gu.oracle_scan(x)
+    assert gu.rel_err(y_s, yr) <= gu.BF16_TOL and gu.rel_err(ls_s, lr) <= gu.BF16_TOL
