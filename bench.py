@@ -61,6 +61,7 @@ KERNEL_SOURCES = {
     "tiled": (None, ("common.hpp", "scan_tiled.hpp")),
     "lanes": (None, ("common.hpp", "scan_ls.hpp")),
     "chunked": (None, ("common.hpp", "scan_ls.hpp", "scan_lp.hpp")),
+    "step": (None, ("common.hpp", "scan_step.hpp")),
 }
 WARM_MS = 400.0  # untimed sustained load before the timed graph replays
 
@@ -339,6 +340,10 @@ def decode_bench(args):
         for i in range(calls):
             call(i, None if i == 0 else hs[i % 2])
 
+    p0 = pieces[0]
+    kname = scan.forward_kernel(p0["u"], p0["delta"], p0["A"], p0["B"], p0["C"], D=p0["D"], z=p0["z"],
+                                delta_bias=p0["delta_bias"], delta_softplus=w.softplus,
+                                return_last_state=True, h0=hs[0], out=ys[0], last_state_out=hs[1])
     for i in range(min(args.warmup, calls)):
         call(i, hs[i % 2])
     torch.cuda.synchronize()
@@ -406,7 +411,8 @@ def decode_bench(args):
         "dtype": "f32",
         "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name + "-decode", "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
-                   "steps_per_call": C, "storage": w.dtype},
+                   "steps_per_call": C, "storage": w.dtype, "kernel": kname},
+        "kernel_sources_sha256": kernel_source_hash(kname, KERNEL_SOURCES),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
                      "algorithmic_bytes_per_call": nbytes},

@@ -264,7 +264,7 @@ def forward_kernel(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
                    return_last_state=False, h0=None, *, kernel=None, out=None, last_state_out=None,
                    zoh_b=False, checkpoints_out=None):
     """Name of the kernel ``selective_scan_fn`` would run with these arguments ("generic",
-    "tiled", "lanes" or "chunked"), from the library's own choice (``mamba_scan_fwd_kernel``);
+    "tiled", "lanes", "chunked" or "step"), from the library's own choice (``mamba_scan_fwd_kernel``);
     raises as the call would for arguments it rejects. Launches nothing."""
     lib = load_library()
     ptrs, shape, st, dtype, flags, _, _, _, keep = _fwd_args(
