@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="instead of the one-shot scan, time recurrent decode: each call advances "
                          "the state by --chunk steps from the previous call's last_state")
+    ap.add_argument("--bwd-kernel", choices=("auto", "lanes", "tiled"), default="auto",
+                    help="with --backward: the backward kernel (auto: the library's choice)")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward scan, time the backward pass (mamba_scan_bwd)")
     ap.add_argument("--checkpoints", action="store_true",
@@ -516,6 +518,9 @@ def backward_bench(args):
     dl_np = rng.standard_normal((w.batch, w.dim, w.dstate)).astype(np.float32)
     dy, dl = torch.from_numpy(dy_np).to(dev), torch.from_numpy(dl_np).to(dev)
 
+    bwd_kernel = None if args.bwd_kernel == "auto" else args.bwd_kernel
+    # the kernel that runs: the library's default is the lane-per-state one at 16 states
+    bwd_kname = bwd_kernel or ("lanes" if w.dstate == 16 else "tiled")
     ck, fwd_ck = None, None
     if args.checkpoints:
         # the forward that saves the segment states, graph-timed like the forward bench, then
@@ -540,7 +545,7 @@ def backward_bench(args):
         return scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"],
                                        z=g["z"], delta_bias=g["delta_bias"],
                                        delta_softplus=w.softplus, dlast_state=dl, want_dh0=False,
-                                       checkpoints=ck)
+                                       checkpoints=ck, kernel=bwd_kernel)
 
     for _ in range(args.warmup):
         step()
@@ -606,7 +611,7 @@ def backward_bench(args):
         "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name + ("-backward-from-checkpoints" if ck is not None else "-backward"),
                    "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
-                   "seq_len": w.seqlen, "storage": w.dtype},
+                   "seq_len": w.seqlen, "storage": w.dtype, "kernel": bwd_kname},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": read + written,
                      "traffic": measured_bwd_traffic(w, ck is not None),

@@ -1,5 +1,5 @@
-// Workspace layout of the backward pass (host side), shared by its launcher and the C-ABI entry
-// points that size and check the caller's workspace.
+// Workspace layouts of the backward pass (host side), shared by its launchers and the C-ABI entry
+// points that size and check the caller's workspace, and the choice between its two kernels.
 #pragma once
 
 #include <stdint.h>
@@ -37,6 +37,68 @@ inline BwdLayout bwd_layout(const mamba_scan_shape& s, bool given_ck = false) {
     o = bwd_align(o + l.groups * s.batch * 2 * s.dstate * l.lp * 4);
     l.off_apart = o;
     o = bwd_align(o + s.batch * s.dim * s.dstate * 4);
+    l.off_dpart = o;
+    o = bwd_align(o + s.batch * s.dim * 4);
+    l.off_bpart = o;
+    o = bwd_align(o + s.batch * s.dim * 4);
+    l.total = o;
+    return l;
+}
+
+// The fixed-order reduction that finishes both backward kernels: dB, dC over the channel groups'
+// partials, dA, dD, dbias over the batch.
+struct BwdReduceParams {
+    const float* bcpart;
+    const float* apart;
+    const float* dpart;
+    const float* bpart;
+    float* dB;
+    float* dC;
+    float* dA;
+    float* dD;
+    float* dbias;
+    int64_t batch, dim, len, dstate, lp, groups;
+};
+
+// Lane-per-state backward (16 states): workgroups of kBlsW waves, 4 channels per wave.
+constexpr int kBlsW = 4;
+
+// Its byte offsets fit 31 bits: a wave's 4 fp32 rows, a batch's B / C, a wave's saved states
+// (the forward lane-per-state kernel that writes them has the same limits).
+inline bool bwd_ls_fits(const mamba_scan_shape& s, int64_t es) {
+    if (s.dstate != 16) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t nseg = (s.len + kBwdSeg - 1) / kBwdSeg;
+    if (4 * s.len * 4 >= lim || 16 * s.len * es >= lim || 4 * nseg * 16 * 4 >= lim) return false;
+    return s.batch * s.dim <= 0x7fffffff;
+}
+
+// 1: the lane-per-state kernel, 0: the segment-tiled one, < 0: an error code. By default the
+// lane-per-state kernel wherever it can run.
+inline int bwd_pick(const mamba_scan_shape& s, int64_t es, uint32_t flags) {
+    const bool fl = (flags & MAMBA_SCAN_FORCE_LANES) != 0, ft = (flags & MAMBA_SCAN_FORCE_TILED) != 0;
+    if (fl && ft) return MAMBA_SCAN_ERR_ARGS;
+    if (ft) return 0;
+    const bool ok = bwd_ls_fits(s, es);
+    if (fl && !ok) return MAMBA_SCAN_ERR_UNSUPPORTED;
+    return ok ? 1 : 0;
+}
+
+// The lane-per-state kernel's workspace: the recomputed states (unless given), the dB / dC
+// partials of its channel groups (4 kBlsW channels each), the dA / dD / dbias partials.
+inline BwdLayout bwd_ls_layout(const mamba_scan_shape& s, bool given_ck = false) {
+    BwdLayout l;
+    l.lp = (s.len + kBwdSeg - 1) / kBwdSeg * kBwdSeg;
+    l.nseg = l.lp / kBwdSeg;
+    l.groups = (s.dim + 4 * kBlsW - 1) / (4 * kBlsW);
+    int64_t o = 0;
+    l.off_bc = 0;  // no widened copy of B / C
+    l.off_ck = o;
+    if (!given_ck) o = bwd_align(o + s.batch * s.dim * l.nseg * 16 * 4);
+    l.off_bcpart = o;
+    o = bwd_align(o + l.groups * s.batch * 2 * 16 * l.lp * 4);
+    l.off_apart = o;
+    o = bwd_align(o + s.batch * s.dim * 16 * 4);
     l.off_dpart = o;
     o = bwd_align(o + s.batch * s.dim * 4);
     l.off_bpart = o;

@@ -30,8 +30,14 @@ inline bool tiled_can_run_any(const ScanParams& q, bool bf16) {
 inline int launch_ls_any(const ScanParams& q, bool bf16, hipStream_t stream) {
     return bf16 ? launch_ls_bf16(q, stream) : launch_ls_f32(q, stream);
 }
-int launch_bwd_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
-                   hipStream_t stream);
+struct BwdReduceParams;
+// the backward: the segment-tiled kernel (any dstate) or the lane-per-state one (16 states), each
+// finished by the fixed-order reduction
+int launch_bwd_tiled_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
+                         hipStream_t stream);
+int launch_bwd_ls_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
+                      hipStream_t stream);
+int launch_bwd_reduce_any(const BwdReduceParams& r, hipStream_t stream);
 int launch_upstream_any(const UpParams& q, int d_conv, hipStream_t stream);
 
 }  // namespace mscan

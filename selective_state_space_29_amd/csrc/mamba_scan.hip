@@ -20,6 +20,9 @@
 
 using namespace mscan;
 
+// flags the backward entry points take
+constexpr uint32_t kBwdFlags = MAMBA_SCAN_DELTA_SOFTPLUS | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_LANES;
+
 namespace {
 
 struct Span {
@@ -296,10 +299,13 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
 int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype, uint32_t flags) {
     if (!s) return MAMBA_SCAN_ERR_NULL;
     if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
-    if (flags & ~(MAMBA_SCAN_DELTA_SOFTPLUS | MAMBA_SCAN_SAVE_CHECKPOINTS)) return MAMBA_SCAN_ERR_ARGS;
+    if (flags & ~(kBwdFlags | MAMBA_SCAN_SAVE_CHECKPOINTS)) return MAMBA_SCAN_ERR_ARGS;
     if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
-    return bwd_layout(*s, (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) != 0).total;
+    const int pick = bwd_pick(*s, dtype == MAMBA_SCAN_BF16 ? 2 : 4, flags);
+    if (pick < 0) return pick;
+    const bool given_ck = (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) != 0;
+    return pick ? bwd_ls_layout(*s, given_ck).total : bwd_layout(*s, given_ck).total;
 }
 
 int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
@@ -311,7 +317,7 @@ int mamba_scan_bwd_static(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* 
                           uint32_t flags, void* stream) {
     if (!p || !s) return MAMBA_SCAN_ERR_NULL;
     if (p->workspace || p->workspace_bytes != 0) return MAMBA_SCAN_ERR_ARGS;  // the scratch is the library's
-    if (flags & ~MAMBA_SCAN_DELTA_SOFTPLUS) return MAMBA_SCAN_ERR_ARGS;
+    if (flags & ~kBwdFlags) return MAMBA_SCAN_ERR_ARGS;
     const int64_t need =
         mamba_scan_bwd_workspace_bytes(s, dtype, flags | (p->checkpoints ? MAMBA_SCAN_SAVE_CHECKPOINTS : 0u));
     if (need < 0) return (int)need;
@@ -332,7 +338,7 @@ namespace {
 int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
                    uint32_t flags, void* stream) {
     if (!p || !s) return MAMBA_SCAN_ERR_NULL;
-    if (flags & ~MAMBA_SCAN_DELTA_SOFTPLUS) return MAMBA_SCAN_ERR_ARGS;
+    if (flags & ~kBwdFlags) return MAMBA_SCAN_ERR_ARGS;
     const int64_t need =
         mamba_scan_bwd_workspace_bytes(s, dtype, flags | (p->checkpoints ? MAMBA_SCAN_SAVE_CHECKPOINTS : 0u));
     if (need < 0) return (int)need;
@@ -346,9 +352,10 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     if (!p->workspace || p->workspace_bytes < need) return MAMBA_SCAN_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(p->workspace) % 256 != 0) return MAMBA_SCAN_ERR_ARGS;
     if (reinterpret_cast<uintptr_t>(p->checkpoints) % 4 != 0) return MAMBA_SCAN_ERR_ARGS;
-    if (s->batch * ((s->dim + 63) / 64) > 0x7fffffff) return MAMBA_SCAN_ERR_UNSUPPORTED;
-
     const int64_t es = dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+    const bool lanes = bwd_pick(*s, es, flags) == 1;  // an error was returned by the size query
+    if (!lanes && s->batch * ((s->dim + 63) / 64) > 0x7fffffff) return MAMBA_SCAN_ERR_UNSUPPORTED;
+
     const int64_t DL = s->batch * s->dim * s->len, NL = s->batch * s->dstate * s->len;
     const int64_t DN = s->batch * s->dim * s->dstate;
     auto span = [](const void* ptr, int64_t bytes) {
@@ -375,7 +382,8 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool sp = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) != 0;
-    return launch_bwd_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
+    return lanes ? launch_bwd_ls_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs)
+                 : launch_bwd_tiled_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
 }
 
 }  // namespace

@@ -439,19 +439,6 @@ __global__ __launch_bounds__(256) void bwd_bc_widen_kernel(const void* B, const 
     out[i] = t < len ? load_el<T>(q ? C : B, rr * len + t) : 0.0f;
 }
 
-struct BwdReduceParams {
-    const float* bcpart;
-    const float* apart;
-    const float* dpart;
-    const float* bpart;
-    float* dB;
-    float* dC;
-    float* dA;
-    float* dD;
-    float* dbias;
-    int64_t batch, dim, len, dstate, lp, groups;
-};
-
 // Fixed-order sums of the partials: dB, dC over channel groups; dA, dD, dbias over the batch.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdReduceParams p) {
     const int64_t nbc = p.batch * p.dstate * p.len;  // per output tensor
@@ -485,6 +472,15 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdReduceParams p) {
 
 // ---------------------------------------------------------------------------------------------
 // host side
+
+inline int launch_bwd_reduce(const BwdReduceParams& r, hipStream_t stream) {
+    const int64_t nred = 2 * r.batch * r.dstate * r.len + r.dim * r.dstate + r.dim;
+    void* rargs[] = {const_cast<BwdReduceParams*>(&r)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_reduce_kernel), dim3((unsigned)((nred + 255) / 256)),
+                           dim3(256), rargs, 0, stream) == hipSuccess
+               ? MAMBA_SCAN_OK
+               : MAMBA_SCAN_ERR_LAUNCH;
+}
 
 inline int bwd_states_per_wave(int64_t nb) { return nb <= 8 ? 1 : 2; }
 
@@ -585,12 +581,7 @@ int launch_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool sof
     r.dstate = s.dstate;
     r.lp = l.lp;
     r.groups = l.groups;
-    const int64_t nred = 2 * s.batch * s.dstate * s.len + s.dim * s.dstate + s.dim;
-    void* rargs[] = {&r};
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&bwd_reduce_kernel), dim3((unsigned)((nred + 255) / 256)),
-                        dim3(256), rargs, 0, stream) != hipSuccess)
-        return MAMBA_SCAN_ERR_LAUNCH;
-    return MAMBA_SCAN_OK;
+    return launch_bwd_reduce(r, stream);
 }
 
 }  // namespace mscan

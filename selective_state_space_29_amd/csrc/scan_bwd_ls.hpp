@@ -1,0 +1,471 @@
+// Lane-per-state backward pass for 16 states (gfx950).
+//
+// The same gradients as the segment-tiled backward (scan_bwd.hpp: the derivative of the forward
+// recurrence of "Mamba代码实战…" §3.1-§3.3 and §6, with the output contraction of "Mamba-minimal项目
+// 解析…" 关键技术点 1 and the initial state of "手把手用PyTorch实现Mamba的SSM层…" §3.1), computed with the
+// forward lane-per-state kernel's decomposition: one lane per (channel, state), a wave = 4
+// channels x 16 states (lane 16c + n), a workgroup = W waves of one batch. The states are not
+// kept from the forward pass, as "手把手用PyTorch实现Mamba的SSM层…" §4.2 prescribes: the state before
+// every 16-step segment comes from the forward lane-per-state kernel (saved by the forward call,
+// or written by a forward launch of the backward itself), and each segment's 16 states are
+// recomputed from it with exactly the forward kernel's arithmetic, so bit for bit.
+//
+// Per segment, walked in reverse:
+//   * Lane 16c + j computes the per-(channel, step) factors of step j of channel c (dt, dt u, the
+//     gated output gradient gp = dy silu(z), sigmoid(x) for softplus', dy silu'(z)); the other
+//     lanes of the row read them through the DPP row broadcast folded into the operation that
+//     consumes them, as in the forward kernel.
+//   * Forward: the segment's states and decays in registers, and C h into the wave's LDS area.
+//   * Reverse, lam = dLoss/dh: lam += gp C; dC += gp h; dB += lam dt u; lam B and
+//     q A with q = lam a h_{t-1} into LDS; dA += q dt; lam *= a.
+//   * The three sums over states per (channel, step) (sum C h, sum lam B, sum q A) are read back
+//     transposed, one step per lane, in state order; the lane then finishes du, ddelta, dz of its
+//     step and accumulates its shares of dD and ddelta_bias.
+//   * dB and dC are summed over the wave's 4 channels in LDS, then over the workgroup's W waves
+//     in wave order, and written as one partial per workgroup; a last kernel adds the partials
+//     of the channel groups in a fixed order (and dA, dD, dbias over the batch): deterministic.
+// Per element 14 VALU operations (forward 4, reverse 10), about 2.8 for the sums over states and
+// 1.9 for the channel sums; per (channel, step) about 35 for the factors and the finish.
+#pragma once
+
+#include "../../include/mamba_scan.h"
+#include "bwd_layout.hpp"
+#include "common.hpp"
+#include "launch.hpp"
+#include "scan_ls.hpp"
+
+namespace mscan {
+
+constexpr int kBlRowP = 20;                  // LDS floats per (channel, state) row of a segment
+constexpr int kBlChanP = 16 * kBlRowP + 16;  // per channel: 16 rows, skewed by 16 banks
+constexpr int kBlArea = 4 * kBlChanP;        // one quantity of a wave's 4 channels
+
+struct BlsParams {
+    const void* u;
+    const void* delta;
+    const void* z;
+    const void* B;
+    const void* C;
+    const float* A;
+    const float* D;
+    const float* bias;
+    const float* dy;
+    const float* dlast;
+    const float* ck;  // (batch, dim, nseg, 16): the state before every segment
+    float* du;
+    float* ddelta;
+    float* dz;
+    float* dh0;
+    float* bcpart;  // (groups, batch, 2, 16, lp) dB / dC partials of each channel group
+    float* apart;   // (batch, dim, 16)
+    float* dpart;   // (batch, dim)
+    float* bpart;   // (batch, dim)
+    int64_t batch, dim, len, lp, nseg, groups;
+};
+
+template <int V>
+struct BlIdx {
+    static constexpr int value = V;
+};
+
+// f(BlIdx<I>{}) for I = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ __forceinline__ void bl_for(F&& f) {
+    if constexpr (B < E) {
+        f(BlIdx<B>{});
+        bl_for<B + 1, E>(f);
+    }
+}
+
+template <typename T, int W, bool SOFTPLUS, bool HAS_Z>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3)))
+void scan_bwd_ls_kernel(BlsParams p) {
+    __shared__ __align__(16) float s_w[W][2][kBlArea];    // per wave: two quantity areas
+    __shared__ __align__(16) float s_bc[2][16 * kBlRowP];  // the segment's B | C: [state][step]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t b = blockIdx.x / p.groups;
+    const int64_t grp = blockIdx.x - b * p.groups;
+    const int64_t d0 = grp * (4 * W) + wave * 4;
+    const int c = lane >> 4, n = lane & 15;
+    const bool valid = d0 + c < p.dim;
+    const int64_t d = valid ? d0 + c : p.dim - 1;  // rows past dim: row dim-1's decay, no gradient
+    const int64_t L = p.len;
+    const int64_t nseg = p.nseg;
+
+    const float Av = p.A[d * 16 + n];
+    const float a2 = Av * kLog2e;
+    const float bias = p.bias ? p.bias[d] : 0.0f;
+    const float Dv = p.D ? p.D[d] : 0.0f;
+    float lam = (p.dlast && valid) ? p.dlast[(b * p.dim + d) * 16 + n] : 0.0f;
+    float gA = 0.0f, accD = 0.0f, accX = 0.0f;
+
+    // Buffer descriptors with 32-bit byte offsets (the host checks that they fit): the wave's 4
+    // rows of u / delta / z / dy / du / ddelta / dz and of the saved states, the batch's B / C;
+    // the segment's offset is an SGPR. Past len, loads read finite values of the next row (or 0
+    // past the range) that the step mask below discards; stores there get an offset past the
+    // range and are dropped.
+    constexpr uint32_t es = sizeof(T);
+    const int64_t d0c = d0 < p.dim ? d0 : p.dim - 1;
+    const int64_t dl = d0 + 3 < p.dim ? d0 + 3 : p.dim - 1;
+    const uint32_t dr = (uint32_t)(d - d0c);
+    const int64_t row0 = b * p.dim + d0c, nrows = dl - d0c + 1;
+    auto rows_rsrc = [&](const void* base, int64_t e) __attribute__((always_inline)) {
+        char* p0 = const_cast<char*>(static_cast<const char*>(base)) + row0 * L * e;
+        return __builtin_amdgcn_make_buffer_rsrc(p0, 0, (int)(nrows * L * e), kLsWord3);
+    };
+    const __amdgpu_buffer_rsrc_t ur = rows_rsrc(p.u, es), xr = rows_rsrc(p.delta, es);
+    const __amdgpu_buffer_rsrc_t zr = HAS_Z ? rows_rsrc(p.z, es) : ur;
+    const __amdgpu_buffer_rsrc_t gr = rows_rsrc(p.dy, 4);
+    const __amdgpu_buffer_rsrc_t our = rows_rsrc(p.du, 4), oxr = rows_rsrc(p.ddelta, 4);
+    const __amdgpu_buffer_rsrc_t ozr = HAS_Z ? rows_rsrc(p.dz, 4) : our;
+    const __amdgpu_buffer_rsrc_t ckr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.ck) + row0 * nseg * 16, 0, (int)(nrows * nseg * 64), kLsWord3);
+    const uint32_t oi = (dr * (uint32_t)L + n) * es;  // this lane's step n of a segment, inputs
+    const uint32_t of = (dr * (uint32_t)L + n) * 4u;  // and fp32 rows
+    const uint32_t ock = (dr * (uint32_t)nseg * 16u + n) * 4u;
+
+    auto load_el = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff) __attribute__((always_inline)) {
+        if constexpr (sizeof(T) == 2)
+            return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, (int)soff, 0);
+        else
+            return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, (int)soff, 0);
+    };
+    auto widen = [](uint32_t v) __attribute__((always_inline)) {
+        return __uint_as_float(sizeof(T) == 2 ? v << 16 : v);
+    };
+
+    // B / C staging: threads 0..255, two steps of one (B|C, state) row each; B|C wave-uniform
+    const bool stager = tid < 256;
+    const int sq = (wave >> 1) & 1, sn = (tid >> 3) & 15, st = (tid & 7) * 2;  // sq wave-uniform
+    const __amdgpu_buffer_rsrc_t bcr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(sq ? p.C : p.B)) + b * 16 * L * es, 0, (int)(16 * L * es),
+        kLsWord3);
+    const uint32_t obc = (uint32_t)(sn * L + st) * es;
+    float* const sdst = &s_bc[sq][sn * kBlRowP + st];
+    auto stage_fetch = [&](int64_t k, uint32_t (&v)[2]) __attribute__((always_inline)) {
+        const uint32_t so = (uint32_t)(k * 16) * es;
+        v[0] = load_el(bcr, obc, so);
+        v[1] = load_el(bcr, obc + es, so);
+    };
+    auto stage_store = [&](const uint32_t (&v)[2]) __attribute__((always_inline)) {
+        *reinterpret_cast<float2*>(sdst) = float2{widen(v[0]), widen(v[1])};
+    };
+
+    // raw inputs of this lane's step of a segment, and its state's saved value, one segment ahead
+    struct Raw {
+        uint32_t x, u, z, g, h;
+    };
+    auto fetch = [&](int64_t k, Raw& w) __attribute__((always_inline)) {
+        const uint32_t so = (uint32_t)(k * 16) * es, s4 = (uint32_t)(k * 64);
+        w.x = load_el(xr, oi, so);
+        w.u = load_el(ur, oi, so);
+        w.z = HAS_Z ? load_el(zr, oi, so) : 0u;
+        w.g = __builtin_amdgcn_raw_buffer_load_b32(gr, (int)of, (int)s4, 0);
+        w.h = __builtin_amdgcn_raw_buffer_load_b32(ckr, (int)ock, (int)s4, 0);
+    };
+
+    float* const area0 = &s_w[wave][0][0];
+    float* const area1 = &s_w[wave][1][0];
+    float* const row0p = area0 + c * kBlChanP + n * kBlRowP;  // this lane's (channel, state) rows
+    float* const row1p = area1 + c * kBlChanP + n * kBlRowP;
+    const float* const col0 = area0 + c * kBlChanP + n;  // step n of channel c, state m at m * kBlRowP
+    const float* const col1 = area1 + c * kBlChanP + n;
+    auto col_sum = [](const float* col) __attribute__((always_inline)) {
+        float s = col[0];
+#pragma unroll
+        for (int m = 1; m < 16; ++m) s += col[m * kBlRowP];
+        return s;
+    };
+
+    // per-(channel, step) factors of this lane's step of segment k (the forward kernel's dt and
+    // dt u, bit for bit)
+    struct Fac {
+        float dt, dtu, gp, uu, sg, gz, h;
+    };
+    auto factors = [&](const Raw& w, int64_t k) __attribute__((always_inline)) {
+        Fac f;
+        const bool live = k * 16 + n < L;
+        const float xb = widen(w.x) + bias;
+        const float x = live ? xb : -__builtin_inff();  // past len: dt = 0, the state carried
+        f.uu = widen(w.u);
+        const float gy = (live && valid) ? __uint_as_float(w.g) : 0.0f;
+        if constexpr (SOFTPLUS) {
+            f.dt = softplus_f(x);
+            f.sg = hw_rcp(1.0f + hw_exp2(-x * kLog2e));
+        } else {
+            f.dt = hw_exp2(x * kLog2e);
+            f.sg = 0.0f;
+        }
+        f.dtu = f.dt * f.uu;
+        if constexpr (HAS_Z) {
+            const float zz = widen(w.z);
+            const float sz = hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
+            f.gp = gy * zz * sz;
+            f.gz = gy * (sz + zz * sz * (1.0f - sz));
+        } else {
+            f.gp = gy;
+            f.gz = 0.0f;
+        }
+        f.h = __uint_as_float(w.h);
+        return f;
+    };
+
+    // Software pipeline: segment k-1's raw inputs and B / C are loaded at the top of segment k
+    // and turned into values before segment k's stores, so no wait for them covers a store.
+    Raw raw;
+    fetch(nseg - 1, raw);
+    uint32_t sv[2];
+    if (stager) {
+        stage_fetch(nseg - 1, sv);
+        stage_store(sv);
+    }
+    Fac cur = factors(raw, nseg - 1);
+    for (int64_t k = nseg - 1; k >= 0; --k) {
+        __syncthreads();  // the segment's B / C staged; the previous segment's LDS reads done
+        const uint32_t s4 = (uint32_t)(k * 64);
+        const bool live = k * 16 + n < L;
+        const int64_t kp = k > 0 ? k - 1 : 0;
+        fetch(kp, raw);
+        if (stager) stage_fetch(kp, sv);
+        const float dt = cur.dt, dtu = cur.dtu, gp = cur.gp;
+        float Bv[16], Cv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 vb = *reinterpret_cast<const float4*>(&s_bc[0][n * kBlRowP + 4 * q]);
+            const float4 vc = *reinterpret_cast<const float4*>(&s_bc[1][n * kBlRowP + 4 * q]);
+            Bv[4 * q] = vb.x, Bv[4 * q + 1] = vb.y, Bv[4 * q + 2] = vb.z, Bv[4 * q + 3] = vb.w;
+            Cv[4 * q] = vc.x, Cv[4 * q + 1] = vc.y, Cv[4 * q + 2] = vc.z, Cv[4 * q + 3] = vc.w;
+        }
+
+        // forward over the segment from its saved state: hp[j] = state before step j
+        float hp[16], dA[16];
+        float h = cur.h;
+        {
+            float yv[4];
+            bl_for<0, 16>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                hp[j] = h;
+                dA[j] = hw_exp2(row_bcast<j>(dt) * a2);
+                h = __builtin_fmaf(dA[j], h, row_bcast<j>(dtu) * Bv[j]);
+                yv[j % 4] = Cv[j] * h;
+                if constexpr (j % 4 == 3)
+                    *reinterpret_cast<float4*>(row0p + (j - 3)) = float4{yv[0], yv[1], yv[2], yv[3]};
+            });
+        }
+        const float hend = h;
+        __builtin_amdgcn_wave_barrier();
+        const float Ys = col_sum(col0);  // sum_n C h of step n
+        __builtin_amdgcn_wave_barrier();
+
+        // reverse over the segment
+        float dBp[16], dCp[16];
+        {
+            float p1[4], p2[4];
+            bl_for<0, 16>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int j = 15 - decltype(ic)::value;
+                const float hs = j == 15 ? hend : hp[j < 15 ? j + 1 : 15];  // state after step j
+                const float gpb = row_bcast<j>(gp);
+                lam = __builtin_fmaf(gpb, Cv[j], lam);
+                dCp[j] = gpb * hs;
+                dBp[j] = lam * row_bcast<j>(dtu);
+                p1[j % 4] = lam * Bv[j];
+                const float q = lam * dA[j] * hp[j];
+                p2[j % 4] = q * Av;
+                gA = __builtin_fmaf(q, row_bcast<j>(dt), gA);
+                lam *= dA[j];
+                if constexpr (j % 4 == 0) {
+                    *reinterpret_cast<float4*>(row0p + j) = float4{p1[0], p1[1], p1[2], p1[3]};
+                    *reinterpret_cast<float4*>(row1p + j) = float4{p2[0], p2[1], p2[2], p2[3]};
+                }
+            });
+        }
+        __builtin_amdgcn_wave_barrier();
+        const float P1 = col_sum(col0);  // sum_n lam B
+        const float P2 = col_sum(col1);  // sum_n lam a h_{t-1} A
+        __builtin_amdgcn_wave_barrier();
+
+        // dB / dC: over the wave's 4 channels; lane l then holds states l / 4, steps 4 (l % 4) ..
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<float4*>(row0p + 4 * q) = float4{dBp[4 * q], dBp[4 * q + 1], dBp[4 * q + 2], dBp[4 * q + 3]};
+            *reinterpret_cast<float4*>(row1p + 4 * q) = float4{dCp[4 * q], dCp[4 * q + 1], dCp[4 * q + 2], dCp[4 * q + 3]};
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int rn = lane >> 2, rj = (lane & 3) * 4;
+        float4 sB = *reinterpret_cast<const float4*>(area0 + rn * kBlRowP + rj);
+        float4 sC = *reinterpret_cast<const float4*>(area1 + rn * kBlRowP + rj);
+#pragma unroll
+        for (int cc = 1; cc < 4; ++cc) {
+            const float4 vb = *reinterpret_cast<const float4*>(area0 + cc * kBlChanP + rn * kBlRowP + rj);
+            const float4 vc = *reinterpret_cast<const float4*>(area1 + cc * kBlChanP + rn * kBlRowP + rj);
+            sB.x += vb.x, sB.y += vb.y, sB.z += vb.z, sB.w += vb.w;
+            sC.x += vc.x, sC.y += vc.y, sC.z += vc.z, sC.w += vc.w;
+        }
+        __builtin_amdgcn_wave_barrier();
+        // the wave's sums, [dB|dC][state][step], for the workgroup's sum below
+        *reinterpret_cast<float4*>(area1 + rn * 16 + rj) = sB;
+        *reinterpret_cast<float4*>(area1 + 256 + rn * 16 + rj) = sC;
+
+        // the next segment's values (its loads issued at the top), before this segment's stores
+        const Fac nxt = factors(raw, kp);
+        const float2 bcn = float2{widen(sv[0]), widen(sv[1])};
+
+        // finish step n of channel c
+        {
+            const float uu = cur.uu;
+            const float gdt = __builtin_fmaf(uu, P1, P2);
+            const float gx = SOFTPLUS ? gdt * cur.sg : gdt * dt;
+            const float gu = __builtin_fmaf(gp, Dv, dt * P1);
+            if (live) {
+                accD = __builtin_fmaf(gp, uu, accD);
+                accX += gx;
+            }
+            const bool st_ok = live && valid;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gu), our, (int)(st_ok ? of : kLsDropBase), (int)s4, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gx), oxr, (int)(st_ok ? of : kLsDropBase), (int)s4, 0);
+            if constexpr (HAS_Z) {
+                const float gzo = cur.gz * __builtin_fmaf(Dv, uu, Ys);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gzo), ozr, (int)(st_ok ? of : kLsDropBase), (int)s4, 0);
+            }
+        }
+        __syncthreads();  // every wave's dB / dC sums written; every wave done with s_bc
+        if (stager) {
+            // dB / dC of the workgroup: the W waves' sums in wave order, one partial per group
+            const int e = sq * 256 + sn * 16 + st;
+            float2 acc = *reinterpret_cast<const float2*>(&s_w[0][1][e]);
+#pragma unroll
+            for (int w = 1; w < W; ++w) {
+                const float2 v = *reinterpret_cast<const float2*>(&s_w[w][1][e]);
+                acc.x += v.x;
+                acc.y += v.y;
+            }
+            *reinterpret_cast<float2*>(p.bcpart + (((grp * p.batch + b) * 2 + sq) * 16 + sn) * p.lp + k * 16 + st) = acc;
+            *reinterpret_cast<float2*>(sdst) = bcn;  // the next segment's B / C
+        }
+        cur = nxt;
+    }
+
+    if (valid) {
+        const int64_t i = (b * p.dim + d) * 16 + n;
+        if (p.dh0) p.dh0[i] = lam;
+        p.apart[i] = gA;
+    }
+    // the channel's dD and dbias shares: its 16 lanes (one step of every segment each)
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        accD += __shfl_xor(accD, off, 64);
+        accX += __shfl_xor(accX, off, 64);
+    }
+    if (n == 0 && valid) {
+        p.dpart[b * p.dim + d] = accD;
+        p.bpart[b * p.dim + d] = accX;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// host side
+
+template <typename T, bool SP, bool HZ>
+int launch_bwd_ls_cfg(const BlsParams& q, hipStream_t stream) {
+    void* args[] = {const_cast<BlsParams*>(&q)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ>),
+                           dim3((unsigned)(q.batch * q.groups)), dim3(64 * kBlsW), args, 0, stream) == hipSuccess
+               ? MAMBA_SCAN_OK
+               : MAMBA_SCAN_ERR_LAUNCH;
+}
+
+template <typename T>
+int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool softplus, hipStream_t stream) {
+    if (!bwd_ls_fits(s, sizeof(T))) return MAMBA_SCAN_ERR_UNSUPPORTED;
+    const bool given = p->checkpoints != nullptr;
+    const BwdLayout l = bwd_ls_layout(s, given);
+    char* ws = static_cast<char*>(p->workspace);
+    float* ck = given ? const_cast<float*>(p->checkpoints) : reinterpret_cast<float*>(ws + l.off_ck);
+    const int64_t L = s.len, DL = s.dim * L;
+    if (!given) {
+        // the state before every segment, written by the forward lane-per-state kernel (the states
+        // a forward call saves, bit for bit); its y goes to du, which the backward overwrites
+        ScanParams f{};
+        f.u = p->u;
+        f.delta = p->delta;
+        f.z = p->z;
+        f.B = p->B;
+        f.C = p->C;
+        f.A = p->A;
+        f.D = p->D;
+        f.bias = p->delta_bias;
+        f.h0 = p->h0;
+        f.y = p->du;
+        f.last_state = nullptr;
+        f.batch = s.batch;
+        f.dim = s.dim;
+        f.len = L;
+        f.dstate = 16;
+        f.su_b = f.sdt_b = f.sz_b = f.sy_b = DL;
+        f.su_d = f.sdt_d = f.sz_d = f.sy_d = L;
+        f.sB_b = f.sC_b = 16 * L;
+        f.sB_n = f.sC_n = L;
+        f.sh0_b = s.dim * 16;
+        f.sh0_d = 16;
+        f.sA_d = 16;
+        f.sD = f.sbias = 1;
+        f.softplus = softplus ? 1 : 0;
+        f.zoh_b = 0;
+        f.ck = ck;
+        f.ck_nseg = l.nseg;
+        const int rc = launch_ls_any(f, sizeof(T) == 2, stream);
+        if (rc != MAMBA_SCAN_OK) return rc;
+    }
+    BlsParams q;
+    q.u = p->u;
+    q.delta = p->delta;
+    q.z = p->z;
+    q.B = p->B;
+    q.C = p->C;
+    q.A = p->A;
+    q.D = p->D;
+    q.bias = p->delta_bias;
+    q.dy = p->dy;
+    q.dlast = p->dlast_state;
+    q.ck = ck;
+    q.du = p->du;
+    q.ddelta = p->ddelta;
+    q.dz = p->dz;
+    q.dh0 = p->dh0;
+    q.bcpart = reinterpret_cast<float*>(ws + l.off_bcpart);
+    q.apart = reinterpret_cast<float*>(ws + l.off_apart);
+    q.dpart = reinterpret_cast<float*>(ws + l.off_dpart);
+    q.bpart = reinterpret_cast<float*>(ws + l.off_bpart);
+    q.batch = s.batch;
+    q.dim = s.dim;
+    q.len = L;
+    q.lp = l.lp;
+    q.nseg = l.nseg;
+    q.groups = l.groups;
+    const bool hz = p->z != nullptr;
+    const int rc = softplus ? (hz ? launch_bwd_ls_cfg<T, true, true>(q, stream) : launch_bwd_ls_cfg<T, true, false>(q, stream))
+                            : (hz ? launch_bwd_ls_cfg<T, false, true>(q, stream) : launch_bwd_ls_cfg<T, false, false>(q, stream));
+    if (rc != MAMBA_SCAN_OK) return rc;
+    BwdReduceParams r;
+    r.bcpart = q.bcpart;
+    r.apart = q.apart;
+    r.dpart = q.dpart;
+    r.bpart = q.bpart;
+    r.dB = p->dB;
+    r.dC = p->dC;
+    r.dA = p->dA;
+    r.dD = p->dD;
+    r.dbias = p->ddelta_bias;
+    r.batch = s.batch;
+    r.dim = s.dim;
+    r.len = L;
+    r.dstate = 16;
+    r.lp = l.lp;
+    r.groups = l.groups;
+    return launch_bwd_reduce_any(r, stream);
+}
+
+}  // namespace mscan

@@ -295,7 +295,8 @@ def _check_checkpoints(ck, batch, dim, L, N, dev):
 
 
 def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False,
-                       h0=None, dlast_state=None, want_dh0=True, checkpoints=None, static_scratch=False):
+                       h0=None, dlast_state=None, want_dh0=True, checkpoints=None, static_scratch=False,
+                       kernel=None):
     """Gradients of the scan (``mamba_scan_bwd``) for incoming gradients dy (batch, dim, L) and,
     optionally, dlast_state (batch, dim, N). Inputs as for ``selective_scan_fn``; all tensors are
     made contiguous first. Returns a dict of fp32 gradients: u, delta, B, C, A, and z, D,
@@ -304,6 +305,8 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     saved for the same inputs; the backward then does not recompute them. ``static_scratch``: call
     ``mamba_scan_bwd_static``, whose workspace is the library's own static per-device buffer (no
     workspace is allocated here; calls overlapping in time on one GPU must not be made).
+    ``kernel``: None (the library's choice: the lane-per-state kernel at 16 states, else the
+    segment-tiled one), "lanes" or "tiled" (forced; an error where it cannot run).
     """
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):
@@ -347,6 +350,9 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     shape = Shape(batch, dim, L, N)
     dtype = BF16 if u.dtype == torch.bfloat16 else F32
     flags = DELTA_SOFTPLUS if delta_softplus else 0
+    if kernel not in (None, "lanes", "tiled"):
+        raise ValueError(f"unknown backward kernel {kernel!r}: None, 'lanes' or 'tiled'")
+    flags |= {None: 0, "lanes": FORCE_LANES, "tiled": FORCE_TILED}[kernel]
     if static_scratch:
         ws, ws_bytes = None, 0
     else:

@@ -236,7 +236,11 @@ BWD_CASES = [
     ("dbias_without_bias", _set("ptrs", "delta_bias", None), -6),
     ("no_workspace", _set("ptrs", "workspace", None), -6),
     ("workspace_too_small", _set("ptrs", "workspace_bytes", 1024), -9),
-    ("unknown_flag", lambda c: c.__setitem__("flags", 1 << 9), -6),
+    ("unknown_flag", lambda c: c.__setitem__("flags", 1 << 13), -6),
+    ("forward_only_flag", lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_CHUNKED), -6),
+    ("both_kernels_forced", lambda c: c.__setitem__("flags", scan.FORCE_TILED | scan.FORCE_LANES), -6),
+    ("lanes_forced_at_8_states",
+     lambda c: (c.__setitem__("flags", scan.FORCE_LANES), setattr(c["shape"], "dstate", 8)), -8),
     ("zoh_not_in_backward", lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.ZOH_B), -6),
     ("bad_dtype", lambda c: c.__setitem__("dtype", 7), -4),
     ("zero_len", _set("shape", "len", 0), -2),
@@ -272,8 +276,12 @@ def test_static_backward_refusals():
     assert call(lambda c: setattr(c["ptrs"], "workspace", (1 << 40) + (30 << 32))) == -6
     assert call(lambda c: setattr(c["ptrs"], "workspace_bytes", 64)) == -6
     assert call(lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.SAVE_CHECKPOINTS)) == -6
-    # the Mamba-130m layer recomputing its states needs 154 MB of workspace
+    # the Mamba-130m layer recomputing its states needs 302 MB of workspace (lane-per-state
+    # kernel) or 154 MB (segment-tiled kernel)
     assert call(lambda c: None, shape=(8, 1536, 2048, 16)) == -10
+    assert call(lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_TILED),
+                shape=(8, 1536, 2048, 16)) == -10
+    assert call(lambda c: c.__setitem__("flags", scan.FORCE_TILED | scan.FORCE_LANES)) == -6
     assert lib.mamba_scan_bwd_static(None, None, 0, 0, None) == -1
     assert len(lib.mamba_scan_strerror(-10)) > 20
 
@@ -294,9 +302,18 @@ def test_backward_workspace_query():
     lib = scan.load_library()
     ok = scan.Shape(8, 1536, 2048, 16)
     n = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), scan.BF16, scan.DELTA_SOFTPLUS)
-    # states every 16 steps + fp32 B/C + per-group dB/dC partials + dA/dD/dbias partials
-    assert n >= 8 * 1536 * 16 * 128 * 4 + 2 * 8 * 16 * 2048 * 4 + 24 * 8 * 2 * 16 * 2048 * 4
-    assert n % 256 == 0
+    # lane-per-state kernel (the default at 16 states): states every 16 steps + dB/dC partials of
+    # each 16-channel group + dA/dD/dbias partials
+    need = 8 * 1536 * 16 * 128 * 4 + 96 * 8 * 2 * 16 * 2048 * 4 + 8 * 1536 * (16 + 2) * 4
+    assert need <= n < need + 6 * 256
+    assert n == lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), scan.BF16, scan.FORCE_LANES)
+    # segment-tiled kernel: states every 16 steps + fp32 B/C + dB/dC partials of each 64-channel group
+    nt = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), scan.BF16, scan.FORCE_TILED)
+    assert nt >= 8 * 1536 * 16 * 128 * 4 + 2 * 8 * 16 * 2048 * 4 + 24 * 8 * 2 * 16 * 2048 * 4
+    assert n % 256 == 0 and nt % 256 == 0
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), scan.BF16, scan.FORCE_TILED | scan.FORCE_LANES) == -6
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(2, 8, 40, 24)), scan.BF16,
+                                              scan.FORCE_LANES) == -8
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(0, 1, 1, 1)), 0, 0) == -2
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 3, 0) == -4
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 0, 1 << 1) == -6

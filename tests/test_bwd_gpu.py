@@ -28,13 +28,14 @@ def tol_of(x):
 NAMES = ("u", "delta", "z", "B", "C", "A", "D", "delta_bias", "h0")
 
 
-def _grads_gpu(x, dy, dlast, softplus, h0=None):
+def _grads_gpu(x, dy, dlast, softplus, h0=None, kernel=None):
     g = {k: gu.to_dev(v) if isinstance(v, np.ndarray) else v for k, v in x.items()}
     out = scan.selective_scan_bwd(
         g["u"], g["delta"], g["A"], g["B"], g["C"], gu.to_dev(dy.astype(np.float32)), D=g.get("D"),
         z=g.get("z"), delta_bias=g.get("delta_bias"), delta_softplus=softplus,
         h0=None if h0 is None else gu.to_dev(h0.astype(np.float32)),
-        dlast_state=None if dlast is None else gu.to_dev(dlast.astype(np.float32)), want_dh0=True)
+        dlast_state=None if dlast is None else gu.to_dev(dlast.astype(np.float32)), want_dh0=True,
+        kernel=kernel)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -47,7 +48,7 @@ def _grads_oracle(x, dy, dlast, softplus, h0=None):
         glast=None if dlast is None else dlast.astype(np.float32).astype(np.float64))
 
 
-def _check(x, softplus=True, with_h0=False, with_dlast=True, seed=0, tol=None):
+def _check(x, softplus=True, with_h0=False, with_dlast=True, seed=0, tol=None, kernel=None):
     tol = tol_of(x) if tol is None else tol
     batch, dim, L = x["u"].shape
     N = x["A"].shape[1]
@@ -55,7 +56,7 @@ def _check(x, softplus=True, with_h0=False, with_dlast=True, seed=0, tol=None):
     dy = rng.standard_normal((batch, dim, L)).astype(np.float32)
     dlast = rng.standard_normal((batch, dim, N)).astype(np.float32) if with_dlast else None
     h0 = rng.standard_normal((batch, dim, N)).astype(np.float32) if with_h0 else None
-    gg = _grads_gpu(x, dy, dlast, softplus, h0)
+    gg = _grads_gpu(x, dy, dlast, softplus, h0, kernel)
     gr = _grads_oracle(x, dy, dlast, softplus, h0)
     for k in NAMES:
         if k not in gr or (k != "h0" and x.get(k) is None):
@@ -67,12 +68,14 @@ def _check(x, softplus=True, with_h0=False, with_dlast=True, seed=0, tol=None):
     return gg
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3])
-def test_workload_backward_parity(wid):
+@pytest.mark.parametrize("wid,kernel", [(1, None), (2, None), (2, "tiled"), (3, None), (3, "tiled")])
+def test_workload_backward_parity(wid, kernel):
+    """Default: the lane-per-state kernel at 16 states (workloads 2, 3), the segment-tiled one at
+    32 (workload 1); the segment-tiled kernel forced at 16 states as well."""
     w = workloads.WORKLOADS[wid]
     x = workloads.make_inputs(w)
-    print(f"backward parity, workload {wid}: {w.name}", flush=True)
-    _check(x, softplus=w.softplus, with_dlast=w.last_state, seed=wid)
+    print(f"backward parity, workload {wid}: {w.name}, kernel {kernel or 'default'}", flush=True)
+    _check(x, softplus=w.softplus, with_dlast=w.last_state, seed=wid, kernel=kernel)
 
 
 EDGE = [
@@ -109,9 +112,39 @@ def test_backward_edge_cases(idx):
            with_dlast=fl.get("dlast", True), seed=idx)
 
 
+# 16 states with the lane-per-state kernel forced: ragged lengths (segments of 16 steps), channel
+# counts that leave workgroups (16 channels) and waves (4) partly empty, every optional input on
+# and off
+EDGE16 = [
+    # (batch, dim, L, dtype, flags)
+    (1, 1, 1, "f32", {}),
+    (1, 3, 2, "bf16", {"h0": True}),
+    (2, 16, 15, "f32", {}),
+    (1, 17, 16, "bf16", {"dlast": False}),
+    (3, 20, 17, "f32", {"h0": True}),
+    (2, 33, 31, "bf16", {"softplus": False}),
+    (1, 64, 33, "f32", {"z": False, "D": False, "bias": False}),
+    (2, 48, 100, "bf16", {"a_kind": "rand", "h0": True}),
+    (1, 130, 257, "f32", {"z": False}),
+    (2, 96, 64, "bf16", {"D": False, "dlast": False}),
+    (1, 40, 1000, "f32", {"softplus": False, "h0": True}),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(EDGE16)))
+def test_lane_backward_edge_cases(idx):
+    batch, dim, L, dtype, fl = EDGE16[idx]
+    print(f"lane-per-state backward edge case {EDGE16[idx]}", flush=True)
+    x = gu.case(700 + idx, batch, dim, 16, L, dtype=dtype, z=fl.get("z", True), D=fl.get("D", True),
+                bias=fl.get("bias", True), a_kind=fl.get("a_kind", "mamba"))
+    _check(x, softplus=fl.get("softplus", True), with_h0=fl.get("h0", False),
+           with_dlast=fl.get("dlast", True), seed=idx, kernel="lanes")
+
+
 def test_state_blocks_are_independent():
     """dB, dC, dA and dh0 of a state depend on no other state, so with 32 states the first 16
-    states' gradients are the bits of a 16-state run on those states alone (the same block)."""
+    states' gradients are the bits of a 16-state run on those states alone (the same block of the
+    segment-tiled kernel, which 32 states run on; forced for the 16-state run)."""
     x = gu.case(73, 2, 96, 32, 90, dtype="bf16")
     rng = np.random.default_rng(4)
     dy = rng.standard_normal((2, 96, 90)).astype(np.float32)
@@ -120,7 +153,8 @@ def test_state_blocks_are_independent():
     full = _grads_gpu(x, dy, dlast, True, h0)
     half = dict(x, A=np.ascontiguousarray(x["A"][:, :16]), B=np.ascontiguousarray(x["B"][:, :16]),
                 C=np.ascontiguousarray(x["C"][:, :16]))
-    part = _grads_gpu(half, dy, np.ascontiguousarray(dlast[..., :16]), True, np.ascontiguousarray(h0[..., :16]))
+    part = _grads_gpu(half, dy, np.ascontiguousarray(dlast[..., :16]), True, np.ascontiguousarray(h0[..., :16]),
+                      kernel="tiled")
     for k in ("B", "C"):
         assert np.array_equal(full[k][:, :16], part[k]), k
     assert np.array_equal(full["A"][:, :16], part["A"])
@@ -185,12 +219,13 @@ def test_large_workload_sampled_channels(wid):
         assert err <= TOL, k
 
 
-def test_backward_is_deterministic():
+@pytest.mark.parametrize("kernel", ["lanes", "tiled"])
+def test_backward_is_deterministic(kernel):
     x = gu.case(71, 2, 150, 16, 200, dtype="bf16")
     rng = np.random.default_rng(1)
     dy = rng.standard_normal((2, 150, 200)).astype(np.float32)
-    a = _grads_gpu(x, dy, None, True)
-    b = _grads_gpu(x, dy, None, True)
+    a = _grads_gpu(x, dy, None, True, kernel=kernel)
+    b = _grads_gpu(x, dy, None, True, kernel=kernel)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
 
