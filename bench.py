@@ -39,6 +39,12 @@ VALU_OPS_PER_ROW_STEP = 10
 SLOTS_PER_ELEMENT_BWD = 26     # backward: 2 x 7 forward recurrence + 10 reverse + 2 channel sums
 SLOTS_PER_ROW_STEP_BWD = 100
 SLOTS_PER_ELEMENT_FWD_RECURRENCE = 7  # one forward recurrence step of the backward's count
+# The lane-per-state backward, counted from its code (per wave and 16-step segment: 408 VALU
+# instructions, 22 of them transcendental; the per-(channel, step) work is spread over the lanes
+# and included), and the lane-per-state forward that writes the segment states when they are not
+# given (per wave and 32-step chunk: 251, 40 transcendental); a transcendental counts 4 slots.
+SLOTS_PER_ELEMENT_BWD_LANES = (408 - 22 + 4 * 22) / 16
+SLOTS_PER_ELEMENT_FWD_LANES = (251 - 40 + 4 * 40) / 32
 # rocprofv3 FETCH_SIZE / WRITE_SIZE records of the forward kernels at the Mamba-130m shape, each
 # with a hash of the sources it was measured on
 TRAFFIC_RECORDS = {
@@ -47,12 +53,18 @@ TRAFFIC_RECORDS = {
     "chunked": (os.path.join(ROOT, "profiles", "scan_chunked_genomic100k_traffic.json"),
                 ("common.hpp", "scan_ls.hpp", "scan_lp.hpp")),
 }
-# the same for the backward's scan kernel at the Mamba-130m shape: recomputing the segment states,
-# or starting from the forward's saved ones
+# the same for the backward's scan kernels at the Mamba-130m shape, by (kernel, from saved
+# states): the segment-tiled kernel recomputing the segment states or starting from the forward's
+# saved ones; the lane-per-state kernel, the same launch either way (recomputing, a forward
+# lane-per-state launch writes the states first)
+_BWD_LS = (os.path.join(ROOT, "profiles", "scan_bwd_ls_mamba130m_traffic.json"),
+           ("common.hpp", "scan_ls.hpp", "bwd_layout.hpp", "scan_bwd_ls.hpp"))
 BWD_TRAFFIC_RECORDS = {
-    False: (os.path.join(ROOT, "profiles", "scan_bwd_mamba130m_traffic.json"), ("common.hpp", "scan_bwd.hpp")),
-    True: (os.path.join(ROOT, "profiles", "scan_bwd_from_checkpoints_mamba130m_traffic.json"),
-           ("common.hpp", "scan_bwd.hpp")),
+    ("tiled", False): (os.path.join(ROOT, "profiles", "scan_bwd_mamba130m_traffic.json"), ("common.hpp", "scan_bwd.hpp")),
+    ("tiled", True): (os.path.join(ROOT, "profiles", "scan_bwd_from_checkpoints_mamba130m_traffic.json"),
+                      ("common.hpp", "scan_bwd.hpp")),
+    ("lanes", False): _BWD_LS,
+    ("lanes", True): _BWD_LS,
 }
 RATES_LIB = os.path.join(ROOT, "selective_state_space_29_amd", "probe", "libmscan_rates.so")
 # the sources each forward kernel is built from (a profile or counter record names their hash)
@@ -164,17 +176,18 @@ def measured_traffic(w, kernel, zoh=False):
     return rec.get("traffic_bytes_per_launch")
 
 
-def measured_bwd_traffic(w, from_checkpoints):
-    """HBM bytes per launch of the backward's scan kernel from its committed rocprofv3 record, or
-    None (no record, other kernel sources, or another workload)."""
-    if w.wid != 3:
+def measured_bwd_traffic(w, from_checkpoints, kernel="lanes"):
+    """HBM bytes per launch of the backward's scan kernel (`kernel`: "lanes" or "tiled") from its
+    committed rocprofv3 record, or None (no record, other kernel sources, or another workload)."""
+    key = (kernel, bool(from_checkpoints))
+    if w.wid != 3 or key not in BWD_TRAFFIC_RECORDS:
         return None
     try:
-        with open(BWD_TRAFFIC_RECORDS[from_checkpoints][0]) as f:
+        with open(BWD_TRAFFIC_RECORDS[key][0]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash(from_checkpoints, BWD_TRAFFIC_RECORDS):
+    if rec.get("source_sha256") != kernel_source_hash(key, BWD_TRAFFIC_RECORDS):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -593,8 +606,12 @@ def backward_bench(args):
     # per-channel gradients (about 100)
     # (given the forward's checkpoints, the first of the two forward recurrences is not run: 7
     # slots fewer per element; the checkpoints are read instead of written and read back)
-    per_el = SLOTS_PER_ELEMENT_BWD - (SLOTS_PER_ELEMENT_FWD_RECURRENCE if ck is not None else 0)
-    bwd_slots = w.elements * per_el + w.rows * w.seqlen * SLOTS_PER_ROW_STEP_BWD
+    if bwd_kname == "lanes":
+        per_el = SLOTS_PER_ELEMENT_BWD_LANES + (SLOTS_PER_ELEMENT_FWD_LANES if ck is None else 0)
+        bwd_slots = int(w.elements * per_el)
+    else:
+        per_el = SLOTS_PER_ELEMENT_BWD - (SLOTS_PER_ELEMENT_FWD_RECURRENCE if ck is not None else 0)
+        bwd_slots = w.elements * per_el + w.rows * w.seqlen * SLOTS_PER_ROW_STEP_BWD
     bwd_tflops = 2 * bwd_slots / (mean_us * 1e-6) / 1e12  # slot-equivalents, a secondary figure
     res = {
         "metric": "scan backward, Gelem/s (B*D*L*N) per mamba_scan_bwd call",
@@ -614,7 +631,7 @@ def backward_bench(args):
                    "seq_len": w.seqlen, "storage": w.dtype, "kernel": bwd_kname},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": read + written,
-                     "traffic": measured_bwd_traffic(w, ck is not None),
+                     "traffic": measured_bwd_traffic(w, ck is not None, bwd_kname),
                      "mean_call_us": round(mean_us, 2), "min_call_us": round(float(per_us.min()), 2),
                      "valu_issue_slots": {"per_call": bwd_slots, "slot_equivalent_TFLOP_s": round(bwd_tflops, 2),
                                           "peak_TFLOP_s": VALU_PEAK_TFLOPS,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 7
+#define MAMBA_SCAN_ABI_VERSION 8
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -72,7 +72,8 @@ typedef enum mamba_scan_dtype {
  * otherwise). Default (none): with 16 states, the short-call kernel for at most 4 steps and the
  * chunked kernel for at least 1024 steps when too few (batch, channel) rows would give every SIMD
  * of the GPU two waves of the lane-per-state kernel; otherwise the lane-per-state kernel where it
- * can run, else the tiled one, else the generic one. */
+ * can run, else the tiled one, else the generic one. The backward pass takes FORCE_TILED and
+ * FORCE_LANES too (ABI 8; see mamba_scan_bwd). */
 #define MAMBA_SCAN_FORCE_GENERIC (1u << 8) /* one lane per row, any shape and alignment */
 #define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
 #define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one lane per (channel, state): dstate 16, 32 or
@@ -190,22 +191,33 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *    (batch, dim, len), required; dz (batch, dim, len), required exactly when z is given;
  *    dB, dC (batch, dstate, len), required; dA (dim, dstate), required; dD and ddelta_bias (dim),
  *    each required exactly when D / delta_bias is given; dh0 (batch, dim, dstate) or NULL.
- *  - Workspace: mamba_scan_bwd_workspace_bytes() bytes or more (queried with
- *    MAMBA_SCAN_SAVE_CHECKPOINTS when `checkpoints` is given), 256-byte aligned, device memory
- *    owned by the caller (states every 16 steps unless given, fp32 copies of B and C, partial
- *    sums).
- *  - Flags: MAMBA_SCAN_DELTA_SOFTPLUS only.
+ *  - Workspace: mamba_scan_bwd_workspace_bytes() bytes or more (queried with the call's flags,
+ *    plus MAMBA_SCAN_SAVE_CHECKPOINTS when `checkpoints` is given), 256-byte aligned, device
+ *    memory owned by the caller (states every 16 steps unless given; partial sums of dB and dC
+ *    per group of channels, 16 channels for the lane-per-state kernel, 64 for the segment-tiled
+ *    one, which also keeps fp32 copies of B and C).
+ *  - Flags: MAMBA_SCAN_DELTA_SOFTPLUS, and at most one of the kernel choices (ABI 8;
+ *    MAMBA_SCAN_ERR_ARGS for both or any other flag):
+ *      MAMBA_SCAN_FORCE_LANES: the lane-per-state backward, one lane per (channel, state) as in
+ *        the forward lane-per-state kernel, 16-step segments walked in reverse from the states
+ *        saved every 16 steps (given, or written first by a forward lane-per-state launch whose
+ *        y goes to du); dstate 16 and row byte offsets within 31 bits (MAMBA_SCAN_ERR_UNSUPPORTED
+ *        otherwise). The default wherever it can run.
+ *      MAMBA_SCAN_FORCE_TILED: the segment-tiled backward (64 channels per workgroup, at most 2
+ *        states per wave), any dstate.
+ *    The two give the same gradients to rounding, not bit for bit; each is deterministic.
  *  - Any dstate up to MAMBA_SCAN_MAX_DSTATE. Above 16 the states are processed in blocks of at
- *    most 16, one launch each: du, ddelta and dz are accumulated in place across the blocks, in
- *    block order, so their values can differ in the last bits from a one-block sum.
+ *    most 16 by the segment-tiled kernel, one launch each: du, ddelta and dz are accumulated in
+ *    place across the blocks, in block order, so their values can differ in the last bits from a
+ *    one-block sum.
  *  - checkpoints (ABI 6): NULL, or the states that a forward call with
  *    MAMBA_SCAN_SAVE_CHECKPOINTS saved for the same inputs (same h0 included), 4-byte aligned;
  *    the scan then starts from them instead of recomputing them. The caller guarantees that they
  *    belong to these inputs: nothing checks it.
  *  - Outputs may not overlap each other, any input or the workspace (MAMBA_SCAN_ERR_ARGS).
- *  - Enqueued on `stream`; B/C widening, the scan (one launch per block of states), a
- *    fixed-order reduction.
- *    Results are bitwise deterministic.
+ *  - Enqueued on `stream`: lane-per-state, the forward that writes the states (unless given),
+ *    the backward scan, a fixed-order reduction; segment-tiled, B/C widening, the scan (one
+ *    launch per block of states), the same reduction. Results are bitwise deterministic.
  */
 typedef struct mamba_scan_bwd_ptrs {
     const void* u;                /* forward inputs */
@@ -252,16 +264,20 @@ int mamba_scan_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
  *    (on different streams, or from different host threads) race and must not be made; calls
  *    one after another on a stream are fine. The buffer keeps the last call's contents; the
  *    backward writes every part of it that it reads, so nothing has to be cleared.
- * With checkpoints from the forward the Mamba-130m layer (batch 8, dim 1536, dstate 16,
- * len 2048) needs 53 MB and fits; recomputing the states it needs 154 MB and does not.
+ * At the Mamba-130m layer (batch 8, dim 1536, dstate 16, len 2048) the segment-tiled kernel
+ * (MAMBA_SCAN_FORCE_TILED) from the forward's saved states needs 53 MB and fits; the lane-per-state
+ * kernel needs 201 MB there (its dB / dC partial sums) and recomputing the states 154 MB
+ * (segment-tiled) or 302 MB: those are refused.
  */
 #define MAMBA_SCAN_STATIC_SCRATCH_BYTES (64ll << 20)
 int mamba_scan_bwd_static(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamba_scan_dtype dtype,
                           uint32_t flags, void* stream);
 
 /* Workspace bytes mamba_scan_bwd needs for this shape (> 0), or a negative error code. Flags:
- * MAMBA_SCAN_DELTA_SOFTPLUS (ignored for the size) and MAMBA_SCAN_SAVE_CHECKPOINTS, meaning that
- * the call will be given `checkpoints`: the size then leaves out the recomputed states (ABI 7). */
+ * MAMBA_SCAN_DELTA_SOFTPLUS (ignored for the size), the call's kernel choice (FORCE_LANES or
+ * FORCE_TILED, ABI 8; none: the default kernel's size; MAMBA_SCAN_ERR_UNSUPPORTED where the
+ * forced kernel cannot run) and MAMBA_SCAN_SAVE_CHECKPOINTS, meaning that the call will be given
+ * `checkpoints`: the size then leaves out the recomputed states (ABI 7). */
 int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype dtype, uint32_t flags);
 
 /*

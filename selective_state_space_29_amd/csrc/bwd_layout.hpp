@@ -60,7 +60,10 @@ struct BwdReduceParams {
     int64_t batch, dim, len, dstate, lp, groups;
 };
 
-// Lane-per-state backward (16 states): workgroups of kBlsW waves, 4 channels per wave.
+// Lane-per-state backward (16 states): workgroups of kBlsW waves, 4 channels per wave. Four waves:
+// a SIMD's 3 waves then belong to 3 workgroups, whose barriers do not wait together (measured at
+// the Mamba-130m shape: 518 us per launch against 637 us with 6-wave workgroups, whose smaller
+// dB / dC partials did not make up for it).
 constexpr int kBlsW = 4;
 
 // Its byte offsets fit 31 bits: a wave's 4 fp32 rows, a batch's B / C, a wave's saved states

@@ -21,11 +21,13 @@
 //   * The three sums over states per (channel, step) (sum C h, sum lam B, sum q A) are read back
 //     transposed, one step per lane, in state order; the lane then finishes du, ddelta, dz of its
 //     step and accumulates its shares of dD and ddelta_bias.
-//   * dB and dC are summed over the wave's 4 channels in LDS, then over the workgroup's W waves
-//     in wave order, and written as one partial per workgroup; a last kernel adds the partials
-//     of the channel groups in a fixed order (and dA, dD, dbias over the batch): deterministic.
+//   * dB and dC are summed over the wave's 4 channels across its rows (v_permlane32_swap, then
+//     v_permlane16_swap, each lane keeping a quarter of the sums), then over the workgroup's W
+//     waves in LDS in wave order, and written as one partial per workgroup; a last kernel adds
+//     the partials of the channel groups in a fixed order (and dA, dD, dbias over the batch):
+//     deterministic.
 // Per element 14 VALU operations (forward 4, reverse 10), about 2.8 for the sums over states and
-// 1.9 for the channel sums; per (channel, step) about 35 for the factors and the finish.
+// 3 for the channel sums; per (channel, step) about 35 for the factors and the finish.
 #pragma once
 
 #include "../../include/mamba_scan.h"
@@ -287,27 +289,30 @@ void scan_bwd_ls_kernel(BlsParams p) {
         const float P2 = col_sum(col1);  // sum_n lam a h_{t-1} A
         __builtin_amdgcn_wave_barrier();
 
-        // dB / dC: over the wave's 4 channels; lane l then holds states l / 4, steps 4 (l % 4) ..
+        // dB / dC over the wave's 4 channels (rows), reduce-scattered across the rows: rows r and
+        // r + 2 added by v_permlane32_swap (lower half keeps dB, upper half dC), then rows r and
+        // r ^ 1 by v_permlane16_swap (even rows keep steps 0-7, odd rows steps 8-15). Lane 16r + n
+        // ends with the 4-channel sums of state n, quantity r / 2, steps 8 (r % 2) .. + 7.
+        float s1[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<float4*>(row0p + 4 * q) = float4{dBp[4 * q], dBp[4 * q + 1], dBp[4 * q + 2], dBp[4 * q + 3]};
-            *reinterpret_cast<float4*>(row1p + 4 * q) = float4{dCp[4 * q], dCp[4 * q + 1], dCp[4 * q + 2], dCp[4 * q + 3]};
+        for (int j = 0; j < 16; ++j) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dBp[j]), __float_as_uint(dCp[j]), false, false);
+            s1[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
-        __builtin_amdgcn_wave_barrier();
-        const int rn = lane >> 2, rj = (lane & 3) * 4;
-        float4 sB = *reinterpret_cast<const float4*>(area0 + rn * kBlRowP + rj);
-        float4 sC = *reinterpret_cast<const float4*>(area1 + rn * kBlRowP + rj);
+        float s2[8];
 #pragma unroll
-        for (int cc = 1; cc < 4; ++cc) {
-            const float4 vb = *reinterpret_cast<const float4*>(area0 + cc * kBlChanP + rn * kBlRowP + rj);
-            const float4 vc = *reinterpret_cast<const float4*>(area1 + cc * kBlChanP + rn * kBlRowP + rj);
-            sB.x += vb.x, sB.y += vb.y, sB.z += vb.z, sB.w += vb.w;
-            sC.x += vc.x, sC.y += vc.y, sC.z += vc.z, sC.w += vc.w;
+        for (int j = 0; j < 8; ++j) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s1[j]), __float_as_uint(s1[j + 8]), false, false);
+            s2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
+        // the wave's sums, [dB|dC][state][step], for the workgroup's sum below (after the column
+        // reads of area1 above: a wave's LDS accesses are performed in order)
         __builtin_amdgcn_wave_barrier();
-        // the wave's sums, [dB|dC][state][step], for the workgroup's sum below
-        *reinterpret_cast<float4*>(area1 + rn * 16 + rj) = sB;
-        *reinterpret_cast<float4*>(area1 + 256 + rn * 16 + rj) = sC;
+        {
+            float* const ws = area1 + (c >> 1) * 256 + n * 16 + (c & 1) * 8;
+            *reinterpret_cast<float4*>(ws) = float4{s2[0], s2[1], s2[2], s2[3]};
+            *reinterpret_cast<float4*>(ws + 4) = float4{s2[4], s2[5], s2[6], s2[7]};
+        }
 
         // the next segment's values (its loads issued at the top), before this segment's stores
         const Fac nxt = factors(raw, kp);

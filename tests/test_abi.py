@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 7
+    assert scan.load_library().mamba_scan_abi_version() == 8
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
