@@ -42,6 +42,20 @@ __device__ __forceinline__ float row_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + LANE, 0xF, 0xF, true));
 }
 
+template <int V>
+struct LsIdx {
+    static constexpr int value = V;
+};
+
+// f(LsIdx<I>{}) for I = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ __forceinline__ void bl_for_ls(F&& f) {
+    if constexpr (B < E) {
+        f(LsIdx<B>{});
+        bl_for_ls<B + 1, E>(f);
+    }
+}
+
 struct LsRegs {
     float h, a2;
     float dt[2], dtu[2];
@@ -324,74 +338,60 @@ void scan_ls_kernel(ScanParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// 32 and 64 states: the same lane-per-state scheme with a channel spread over N / 16 rows of
-// 16 lanes (a wave = 64 / N channels), in chunks of 16 steps.
-//   * Every row of a channel computes the channel's per-(channel, step) factors for the chunk,
-//     one step per lane, so that the row broadcast still reaches every lane of the channel.
-//   * Row r of a wave owns the 16 states 16 (r mod N/16) ... of its channel and one LDS block:
-//     each lane writes its C h terms there, then lane j of the row sums the row's 16 states for
-//     step j; the N / 16 row sums of a channel are added across rows with v_permlane16_swap
-//     (row pairs) and v_permlane32_swap (wave halves), in a fixed order. The channel's first row
-//     stores y.
-//   * B / C: the workgroup (4 waves) stages N states x 16 steps of each per chunk in LDS.
+// 32 and 64 states: S = N / 16 states per lane, so that a channel still fills one 16-lane row.
+//   * A wave = 4 channels (rows), as at 16 states; lane j of a row holds states j, j + 16, ...,
+//     j + 16 (S - 1) of its channel, in chunks of 16 steps.
+//   * Lane j computes the per-(channel, step) factors of step j of the chunk; the row reads them
+//     through one DPP row broadcast per factor and step, which then serves the lane's S states.
+//   * Per step a lane adds its S states' C h terms (in state order) and writes one value per step
+//     to the wave's LDS area; lane j then sums step j over the row's 16 lanes, in lane order, and
+//     finishes and stores y. The sum over states is thus taken in the order: states n, n + 16, ..
+//     within a lane, then lanes 0 .. 15.
+//   * B / C: the workgroup (4 waves, 16 channels of one batch) stages N states x 16 steps of each
+//     per chunk in LDS, one chunk ahead; a lane reads its states' rows 4 steps at a time.
 constexpr int kLwT = 16;                      // steps per chunk
-constexpr int kLwRowP = kLwT + 4;             // LDS floats per state row
-constexpr int kLwBlkP = 16 * kLwRowP + 16;    // one row's block of 16 states, skewed 16 banks
+constexpr int kLwRowP = kLwT + 4;             // LDS floats per lane row of C h sums
+constexpr int kLwChanP = 16 * kLwRowP + 16;   // one channel's 16 lane rows, skewed by 16 banks
 
-template <int N>
-struct LwRegs {
-    float h, a2;
-    float dt, dtu;
-    float Bv[kLwT], Cv[kLwT];
-    float pv[4];
-    float* sp;  // this lane's state row in its row's LDS block
-};
-
-template <int N, int S>
-__device__ __forceinline__ void lw_steps(LwRegs<N>& r) {
-    if constexpr (S < kLwT) {
-        const float dA = hw_exp2(row_bcast<S>(r.dt) * r.a2);
-        r.h = __builtin_fmaf(dA, r.h, row_bcast<S>(r.dtu) * r.Bv[S]);
-        r.pv[S % 4] = r.Cv[S] * r.h;
-        if constexpr (S % 4 == 3)
-            *reinterpret_cast<float4*>(r.sp + (S - 3)) = float4{r.pv[0], r.pv[1], r.pv[2], r.pv[3]};
-        lw_steps<N, S + 1>(r);
-    }
-}
+// Staged B / C: unpadded rows of 16 steps (so that 4 workgroups fit a CU at 64 states), the 4-step
+// group g of state row m at group (g ^ (m / 4)) % 4: a lane's 16-byte read of one group of its
+// state rows, and a staging thread's 16-byte write, touch distinct banks across 16 lanes.
+__device__ __forceinline__ int lw_bc_at(int m, int g) { return m * kLwT + (((g ^ (m >> 2)) & 3) << 2); }
 
 template <typename T, int N, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK>
-__global__ __launch_bounds__(64 * kLsWaves) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(64 * kLsWaves) __attribute__((amdgpu_waves_per_eu(4)))
 void scan_ls_wide_kernel(ScanParams p) {
     static_assert(N == 32 || N == 64, "wide lane-per-state kernel: 32 or 64 states");
-    constexpr int CW = 64 / N;        // channels per wave
-    constexpr int RPC = N / 16;       // rows per channel
-    constexpr int CG = kLsWaves * CW; // channels per workgroup
-    __shared__ __align__(16) float s_p[kLsWaves * 4 * kLwBlkP];
-    __shared__ __align__(16) float s_bc[2][2][N * kLwRowP];  // [chunk parity][B|C][state][step]
+    constexpr int S = N / 16;          // states per lane
+    constexpr int CG = kLsWaves * 4;   // channels per workgroup
+    __shared__ __align__(16) float s_p[kLsWaves * 4 * kLwChanP];
+    __shared__ __align__(16) float s_bc[2][2][N * kLwT];  // [chunk parity][B|C][state][step], swizzled
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t blocks = (p.dim + CG - 1) / CG;
     const int64_t b = blockIdx.x / blocks;
-    const int64_t d0 = (blockIdx.x - b * blocks) * CG + wave * CW;
-    const int c = lane / N, n = lane % N, row = lane >> 4, j = lane & 15;
-    const bool first_row = (n >> 4) == 0;
+    const int64_t d0 = (blockIdx.x - b * blocks) * CG + wave * 4;
+    const int c = lane >> 4, j = lane & 15;
     const bool valid = d0 + c < p.dim;
     const int64_t d = valid ? d0 + c : p.dim - 1;
     const int64_t L = p.len;
 
-    LwRegs<N> r;
-    r.a2 = p.A[d * p.sA_d + n] * kLog2e;
-    r.h = p.h0 ? p.h0[b * p.sh0_b + d * p.sh0_d + n] : 0.0f;
+    float h[S], a2[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+        a2[k] = p.A[d * p.sA_d + j + 16 * k] * kLog2e;
+        h[k] = p.h0 ? p.h0[b * p.sh0_b + d * p.sh0_d + j + 16 * k] : 0.0f;
+    }
     const float bias = p.bias ? p.bias[d * p.sbias] : 0.0f;
     const float Dv = p.D ? p.D[d * p.sD] : 0.0f;  // no skip term: D = 0
-    float* const blk = s_p + (wave * 4 + row) * kLwBlkP;
-    r.sp = blk + j * kLwRowP;
+    float* const chan = s_p + (wave * 4 + c) * kLwChanP;
+    float* const sp = chan + j * kLwRowP;  // this lane's row of C h sums
 
     constexpr uint32_t es = sizeof(T);
     const int64_t d0c = d0 < p.dim ? d0 : p.dim - 1;
-    const int64_t dl = d0 + CW - 1 < p.dim ? d0 + CW - 1 : p.dim - 1;
+    const int64_t dl = d0 + 3 < p.dim ? d0 + 3 : p.dim - 1;
     const uint32_t dr = (uint32_t)(d - d0c);
     auto rows_rsrc = [&](const void* base, int64_t sb, int64_t sd) __attribute__((always_inline)) {
         const T* row0 = static_cast<const T*>(base) + b * sb + d0c * sd;
@@ -404,12 +404,12 @@ void scan_ls_wide_kernel(ScanParams p) {
     const uint32_t oz = HAS_Z ? dr * (uint32_t)p.sz_d * es : 0u;
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         p.y + b * p.sy_b + d0c * p.sy_d, 0, (int)(((dl - d0c) * p.sy_d + L) * 4), kLsWord3);
-    const uint32_t oy_l = (valid && first_row) ? (dr * (uint32_t)p.sy_d + j) * 4u : kLsDropBase;
-    // saved states (CK), as in the 16-state kernel: one segment per chunk
+    const uint32_t oy_l = valid ? (dr * (uint32_t)p.sy_d + j) * 4u : kLsDropBase;
+    // saved states (CK): the state before every 16-step segment, one segment per chunk
     const __amdgpu_buffer_rsrc_t ckr = __builtin_amdgcn_make_buffer_rsrc(
         CK ? p.ck + (b * p.dim + d0c) * p.ck_nseg * N : p.y, 0,
         CK ? (int)((dl - d0c + 1) * p.ck_nseg * N * 4) : 0, kLsWord3);
-    const uint32_t ock = valid ? (dr * (uint32_t)p.ck_nseg * N + n) * 4u : kLsDropBase;
+    const uint32_t ock = valid ? (dr * (uint32_t)p.ck_nseg * N + j) * 4u : kLsDropBase;
 
     auto load_el = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff) __attribute__((always_inline)) {
         if constexpr (sizeof(T) == 2)
@@ -438,9 +438,9 @@ void scan_ls_wide_kernel(ScanParams p) {
             (int)(((N - 1) * snn + L) * es), kLsWord3);
         sofs_row[k] = (uint32_t)(sn * snn) * es;
         sofs[k] = sofs_row[k] + st4 * es;
-        sdst[k] = &s_bc[0][q][sn * kLwRowP + st4];
+        sdst[k] = &s_bc[0][q][lw_bc_at(sn, st4 / 4)];
     }
-    constexpr int kBufStride = 2 * N * kLwRowP;
+    constexpr int kBufStride = 2 * N * kLwT;
     auto stage_load = [&](int64_t k, bool tail, uint32_t (&v)[SPT][4]) __attribute__((always_inline)) {
         const uint32_t t0 = (uint32_t)(k * kLwT);
         if (!tail) {
@@ -496,24 +496,40 @@ void scan_ls_wide_kernel(ScanParams p) {
             w.z = HAS_Z ? load_el(zr, oz + tj * es, 0) : 0u;
         }
     };
-    auto read_bc = [&](int buf) __attribute__((always_inline)) {
-        const float* sb = &s_bc[buf][0][n * kLwRowP];
-        const float* sc = &s_bc[buf][1][n * kLwRowP];
-#pragma unroll
-        for (int q = 0; q < kLwT / 4; ++q) {
-            const float4 vb = *reinterpret_cast<const float4*>(sb + 4 * q);
-            const float4 vc = *reinterpret_cast<const float4*>(sc + 4 * q);
-            r.Bv[4 * q] = vb.x, r.Bv[4 * q + 1] = vb.y, r.Bv[4 * q + 2] = vb.z, r.Bv[4 * q + 3] = vb.w;
-            r.Cv[4 * q] = vc.x, r.Cv[4 * q + 1] = vc.y, r.Cv[4 * q + 2] = vc.z, r.Cv[4 * q + 3] = vc.w;
-        }
-    };
-    float uv, gz;
+    float dt, dtu, uv, gz;
     auto prologue = [&](const Raw& w) __attribute__((always_inline)) {
         const float xb = widen(w.x) + bias;
-        r.dt = SOFTPLUS ? softplus_f(xb) : hw_exp2(xb * kLog2e);
+        dt = SOFTPLUS ? softplus_f(xb) : hw_exp2(xb * kLog2e);
         uv = widen(w.u);
-        r.dtu = r.dt * uv;
+        dtu = dt * uv;
         gz = HAS_Z ? silu_f(widen(w.z)) : 1.0f;
+    };
+
+    // 4 steps Q*4 .. Q*4+3 of the chunk: the lane's S states from B / C staged in buffer buf
+    auto steps4 = [&](int buf, auto qc) __attribute__((always_inline)) {
+        constexpr int Q = decltype(qc)::value;
+        float4 bv[S], cv[S];
+#pragma unroll
+        for (int k = 0; k < S; ++k) {
+            bv[k] = *reinterpret_cast<const float4*>(&s_bc[buf][0][lw_bc_at(j + 16 * k, Q)]);
+            cv[k] = *reinterpret_cast<const float4*>(&s_bc[buf][1][lw_bc_at(j + 16 * k, Q)]);
+        }
+        float pv[4];
+        bl_for_ls<0, 4>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int st = 4 * Q + i;
+            const float dtb = row_bcast<st>(dt), dtub = row_bcast<st>(dtu);
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < S; ++k) {
+                const float bb = i == 0 ? bv[k].x : i == 1 ? bv[k].y : i == 2 ? bv[k].z : bv[k].w;
+                const float cc = i == 0 ? cv[k].x : i == 1 ? cv[k].y : i == 2 ? cv[k].z : cv[k].w;
+                h[k] = __builtin_fmaf(hw_exp2(dtb * a2[k]), h[k], dtub * bb);
+                acc = k == 0 ? cc * h[k] : __builtin_fmaf(cc, h[k], acc);
+            }
+            pv[i] = acc;
+        });
+        *reinterpret_cast<float4*>(sp + 4 * Q) = float4{pv[0], pv[1], pv[2], pv[3]};
     };
 
     // the same software pipeline as the 16-state kernel, per 16-step chunk
@@ -537,26 +553,19 @@ void scan_ls_wide_kernel(ScanParams p) {
         stage_load(kn, next_tail, sv);
         Raw nx;
         fetch(kn, next_tail, nx);
-        read_bc(buf);
-        const float hk = r.h;  // the state before step t0 (segment k), stored with y
-        lw_steps<N, 0>(r);
+        float hk[S];  // the states before step t0 (segment k), stored with y
+#pragma unroll
+        for (int s = 0; s < S; ++s) hk[s] = h[s];
+        bl_for_ls<0, 4>([&](auto qc) __attribute__((always_inline)) { steps4(buf, qc); });
         stage_store(buf ^ 1, sv);
         const float u0 = uv, g0 = gz;
         prologue(nx);
         __builtin_amdgcn_wave_barrier();
-        // step j: this row's 16 states in order, then the channel's rows: pairs, then halves
-        float y = blk[j];
+        // step j: the row's 16 lanes in order
+        float y = chan[j];
 #pragma unroll
-        for (int m = 1; m < 16; ++m) y += blk[m * kLwRowP + j];
+        for (int m = 1; m < 16; ++m) y += chan[m * kLwRowP + j];
         __builtin_amdgcn_wave_barrier();
-        if constexpr (RPC >= 2) {
-            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-            y = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
-        if constexpr (RPC == 4) {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-            y = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
         const float o = __builtin_fmaf(Dv, u0, y) * g0;
         if (!(ragged && k == nch - 1)) {
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), yr, (int)oy_l, (int)(t0 * 4u), 0);
@@ -564,10 +573,17 @@ void scan_ls_wide_kernel(ScanParams p) {
             const uint32_t a = t0 + j < (uint32_t)L ? oy_l : kLsDropBase;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), yr, (int)a, (int)(t0 * 4u), 0);
         }
-        if constexpr (CK)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hk), ckr, (int)ock, (int)(t0 * (N / 4)), 0);
+        if constexpr (CK) {
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hk[s]), ckr, (int)(ock + 64u * s),
+                                                      (int)(t0 * (N / 4)), 0);
+        }
     }
-    if (p.last_state && valid) p.last_state[b * p.sls_b + d * p.sls_d + n] = r.h;
+    if (p.last_state && valid) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) p.last_state[b * p.sls_b + d * p.sls_d + j + 16 * s] = h[s];
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -585,7 +601,7 @@ inline bool ls_eligible(const ScanParams& q, int64_t es) {
     if (!rows_ok(q.y, q.sy_d, 4)) return false;
     if (((q.dstate - 1) * q.sB_n + q.len) * es >= lim || ((q.dstate - 1) * q.sC_n + q.len) * es >= lim) return false;
     if (q.batch * q.dim > 0x7fffffff) return false;
-    if (q.ck && q.ck_nseg * 256 >= lim) return false;  // a wave's saved states: 64 lanes x nseg floats
+    if (q.ck && q.ck_nseg * 16 * q.dstate >= lim) return false;  // a wave's saved states: 4 rows x nseg x N floats
     return true;
 }
 
@@ -595,8 +611,8 @@ int launch_ls_cfg(const ScanParams& q, hipStream_t stream) {
     int64_t per_group;
     switch (q.dstate) {
         case 16: fn = reinterpret_cast<const void*>(&scan_ls_kernel<T, SP, HZ, VEC, CK>); per_group = 16; break;
-        case 32: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 32, SP, HZ, VEC, CK>); per_group = 8; break;
-        default: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 64, SP, HZ, VEC, CK>); per_group = 4; break;
+        case 32: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 32, SP, HZ, VEC, CK>); per_group = 16; break;
+        default: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 64, SP, HZ, VEC, CK>); per_group = 16; break;
     }
     void* args[] = {const_cast<ScanParams*>(&q)};
     const int64_t groups = q.batch * ((q.dim + per_group - 1) / per_group);
