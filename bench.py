@@ -506,8 +506,10 @@ def backward_sampled_parity(w, out, dy_np, dl_np, n_random=5, seed=11):
 
 def backward_bench(args):
     """The backward pass at the workload's shape: gradients of sum(dy * y) + sum(dl * last_state)
-    for seeded dy, dl. One step = one mamba_scan_bwd call (B/C widening, the two-phase scan,
-    the fixed-order reduction), timed with HIP events on the launch stream."""
+    for seeded dy, dl. One step = one mamba_scan_bwd call (the default kernel at 16 states: the
+    forward writing the segment states unless given, the lane-per-state backward scan, the
+    fixed-order reduction), timed with HIP events on the launch stream after WARM_MS of sustained
+    calls."""
     import numpy as np
     import torch
 
@@ -560,9 +562,15 @@ def backward_bench(args):
                                        delta_softplus=w.softplus, dlast_state=dl, want_dh0=False,
                                        checkpoints=ck, kernel=bwd_kernel)
 
+    # warm-up: the given calls, then sustained calls for WARM_MS, as for the forward's timed
+    # replays (the clocks settle under the backward's own load)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while (time.perf_counter() - t_warm) * 1e3 < WARM_MS:
+        step()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     out = None
