@@ -76,8 +76,9 @@ typedef enum mamba_scan_dtype {
  * FORCE_LANES too (ABI 8; see mamba_scan_bwd). */
 #define MAMBA_SCAN_FORCE_GENERIC (1u << 8) /* one lane per row, any shape and alignment */
 #define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
-#define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one lane per (channel, state): dstate 16, 32 or
-                                              64, no ZOH_B; error if it cannot run (ABI 5) */
+#define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one 16-lane row per channel, one lane per state
+                                              at dstate 16 and dstate/16 states per lane at 32
+                                              or 64; no ZOH_B; error if it cannot run (ABI 5) */
 /* Chunked along the sequence (ABI 7): one wave per channel, its four 16-lane rows scan four
  * consecutive 16-step runs of each 64-step chunk and are combined with the associative (a, b)
  * operator of the parallel scan ("手把手用PyTorch实现Mamba的SSM层…" §3.2), the state carried

@@ -235,10 +235,10 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
 
     u, delta, z: (batch, dim, L); B, C: (batch, N, L); one storage dtype for all five
     (torch.float32 or torch.bfloat16). A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N);
-    these are taken in fp32. ``kernel``: None (library picks), "generic", "tiled", "lanes"
-    (one lane per (channel, state); 16, 32 or 64 states), "chunked" (parallel along the
-    sequence: a wave per channel scanning 4 runs of each 64-step chunk; 16 states) or "step"
-    (short calls such as decode, at most 64 steps; 16 states).
+    these are taken in fp32. ``kernel``: None (library picks), "generic", "tiled", "lanes" (a
+    16-lane row per channel: one state per lane at 16 states, 2 or 4 at 32 or 64), "chunked"
+    (parallel along the sequence: a wave per channel scanning 4 runs of each 64-step chunk; 16
+    states) or "step" (short calls such as decode, at most 64 steps; 16 states).
     ``checkpoints_out``: a contiguous fp32 (batch, dim, ceil(L/16), N) tensor that receives the
     state before every 16-step segment, for ``selective_scan_bwd(checkpoints=...)``
     (lane-per-state kernels only).
