@@ -534,8 +534,9 @@ def backward_bench(args):
     dy, dl = torch.from_numpy(dy_np).to(dev), torch.from_numpy(dl_np).to(dev)
 
     bwd_kernel = None if args.bwd_kernel == "auto" else args.bwd_kernel
-    # the kernel that runs: the library's default is the lane-per-state one at 16 states
-    bwd_kname = bwd_kernel or ("lanes" if w.dstate == 16 else "tiled")
+    # the kernel that runs: the library's default is the lane-per-state one at 16, 32 and 64
+    # states (every workload here is within its offset limits)
+    bwd_kname = bwd_kernel or ("lanes" if w.dstate in (16, 32, 64) else "tiled")
     ck, fwd_ck = None, None
     if args.checkpoints:
         # the forward that saves the segment states, graph-timed like the forward bench, then

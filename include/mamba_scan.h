@@ -202,22 +202,22 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *      MAMBA_SCAN_FORCE_LANES: the lane-per-state backward, one lane per (channel, state) as in
  *        the forward lane-per-state kernel, 16-step segments walked in reverse from the states
  *        saved every 16 steps (given, or written first by a forward lane-per-state launch whose
- *        y goes to du); dstate 16 and row byte offsets within 31 bits (MAMBA_SCAN_ERR_UNSUPPORTED
- *        otherwise). The default wherever it can run.
+ *        y goes to du); dstate 16, 32 or 64 and row byte offsets within 31 bits
+ *        (MAMBA_SCAN_ERR_UNSUPPORTED otherwise). The default wherever it can run.
  *      MAMBA_SCAN_FORCE_TILED: the segment-tiled backward (64 channels per workgroup, at most 2
  *        states per wave), any dstate.
  *    The two give the same gradients to rounding, not bit for bit; each is deterministic.
  *  - Any dstate up to MAMBA_SCAN_MAX_DSTATE. Above 16 the states are processed in blocks of at
- *    most 16 by the segment-tiled kernel, one launch each: du, ddelta and dz are accumulated in
- *    place across the blocks, in block order, so their values can differ in the last bits from a
- *    one-block sum.
+ *    most 16, one launch each (either kernel): du, ddelta and dz are accumulated in place across
+ *    the blocks, in block order, so their values can differ in the last bits from a one-block
+ *    sum.
  *  - checkpoints (ABI 6): NULL, or the states that a forward call with
  *    MAMBA_SCAN_SAVE_CHECKPOINTS saved for the same inputs (same h0 included), 4-byte aligned;
  *    the scan then starts from them instead of recomputing them. The caller guarantees that they
  *    belong to these inputs: nothing checks it.
  *  - Outputs may not overlap each other, any input or the workspace (MAMBA_SCAN_ERR_ARGS).
  *  - Enqueued on `stream`: lane-per-state, the forward that writes the states (unless given),
- *    the backward scan, a fixed-order reduction; segment-tiled, B/C widening, the scan (one
+ *    the backward scan (one launch per block of 16 states), a fixed-order reduction; segment-tiled, B/C widening, the scan (one
  *    launch per block of states), the same reduction. Results are bitwise deterministic.
  */
 typedef struct mamba_scan_bwd_ptrs {

@@ -60,19 +60,21 @@ struct BwdReduceParams {
     int64_t batch, dim, len, dstate, lp, groups;
 };
 
-// Lane-per-state backward (16 states): workgroups of kBlsW waves, 4 channels per wave. Four waves:
+// Lane-per-state backward (16, 32, 64 states): workgroups of kBlsW waves, 4 channels per wave. Four waves:
 // a SIMD's 3 waves then belong to 3 workgroups, whose barriers do not wait together (measured at
 // the Mamba-130m shape: 518 us per launch against 637 us with 6-wave workgroups, whose smaller
 // dB / dC partials did not make up for it).
 constexpr int kBlsW = 4;
 
-// Its byte offsets fit 31 bits: a wave's 4 fp32 rows, a batch's B / C, a wave's saved states
+// 16, 32 or 64 states (the state counts the forward lane-per-state kernels save states for), and
+// byte offsets that fit 31 bits: a wave's 4 fp32 rows, a batch's B / C, a wave's saved states
 // (the forward lane-per-state kernel that writes them has the same limits).
 inline bool bwd_ls_fits(const mamba_scan_shape& s, int64_t es) {
-    if (s.dstate != 16) return false;
+    const int64_t N = s.dstate;
+    if (N != 16 && N != 32 && N != 64) return false;
     const int64_t lim = (int64_t)1 << 31;
     const int64_t nseg = (s.len + kBwdSeg - 1) / kBwdSeg;
-    if (4 * s.len * 4 >= lim || 16 * s.len * es >= lim || 4 * nseg * 16 * 4 >= lim) return false;
+    if (4 * s.len * 4 >= lim || N * s.len * es >= lim || 4 * nseg * N * 4 >= lim) return false;
     return s.batch * s.dim <= 0x7fffffff;
 }
 
@@ -97,11 +99,11 @@ inline BwdLayout bwd_ls_layout(const mamba_scan_shape& s, bool given_ck = false)
     int64_t o = 0;
     l.off_bc = 0;  // no widened copy of B / C
     l.off_ck = o;
-    if (!given_ck) o = bwd_align(o + s.batch * s.dim * l.nseg * 16 * 4);
+    if (!given_ck) o = bwd_align(o + s.batch * s.dim * l.nseg * s.dstate * 4);
     l.off_bcpart = o;
-    o = bwd_align(o + l.groups * s.batch * 2 * 16 * l.lp * 4);
+    o = bwd_align(o + l.groups * s.batch * 2 * s.dstate * l.lp * 4);
     l.off_apart = o;
-    o = bwd_align(o + s.batch * s.dim * 16 * 4);
+    o = bwd_align(o + s.batch * s.dim * s.dstate * 4);
     l.off_dpart = o;
     o = bwd_align(o + s.batch * s.dim * 4);
     l.off_bpart = o;

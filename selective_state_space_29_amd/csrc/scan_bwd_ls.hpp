@@ -1,4 +1,4 @@
-// Lane-per-state backward pass for 16 states (gfx950).
+// Lane-per-state backward pass for 16, 32 and 64 states (gfx950).
 //
 // The same gradients as the segment-tiled backward (scan_bwd.hpp: the derivative of the forward
 // recurrence of "Mamba代码实战…" §3.1-§3.3 and §6, with the output contraction of "Mamba-minimal项目
@@ -28,6 +28,9 @@
 //     deterministic.
 // Per element 14 VALU operations (forward 4, reverse 10), about 2.8 for the sums over states and
 // 3 for the channel sums; per (channel, step) about 35 for the factors and the finish.
+// 32 and 64 states run one launch per block of 16 states, in order: each block's states are
+// independent of the others' for dB, dC, dA and dh0; du, ddelta and (with a gate) the sum over
+// states of C h are carried from block to block through the outputs, the last block finishing dz.
 #pragma once
 
 #include "../../include/mamba_scan.h"
@@ -58,11 +61,13 @@ struct BlsParams {
     float* ddelta;
     float* dz;
     float* dh0;
-    float* bcpart;  // (groups, batch, 2, 16, lp) dB / dC partials of each channel group
-    float* apart;   // (batch, dim, 16)
+    float* bcpart;  // (groups, batch, 2, N, lp) dB / dC partials of each channel group
+    float* apart;   // (batch, dim, N)
     float* dpart;   // (batch, dim)
     float* bpart;   // (batch, dim)
     int64_t batch, dim, len, lp, nseg, groups;
+    int64_t N, n0;    // dstate; this launch's states n0 .. n0 + 15
+    int first, last;  // first / last block of 16 states: initialises / finishes the sums
 };
 
 template <int V>
@@ -79,7 +84,10 @@ __device__ __forceinline__ void bl_for(F&& f) {
     }
 }
 
-template <typename T, int W, bool SOFTPLUS, bool HAS_Z>
+// MULTI: one of several blocks of 16 states (32 or 64 states): du, ddelta and, with a gate, the
+// sum over states of C h are read back from the earlier blocks' launches and added to, in block
+// order; the first block adds the skip term, the last one finishes dz. Otherwise the only block.
+template <typename T, int W, bool SOFTPLUS, bool HAS_Z, bool MULTI>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_bwd_ls_kernel(BlsParams p) {
     __shared__ __align__(16) float s_w[W][2][kBlArea];    // per wave: two quantity areas
@@ -96,12 +104,14 @@ void scan_bwd_ls_kernel(BlsParams p) {
     const int64_t d = valid ? d0 + c : p.dim - 1;  // rows past dim: row dim-1's decay, no gradient
     const int64_t L = p.len;
     const int64_t nseg = p.nseg;
+    const int64_t NS = MULTI ? p.N : 16, n0 = MULTI ? p.n0 : 0;  // state count, this block's first
+    const bool first = !MULTI || p.first, last = !MULTI || p.last;
 
-    const float Av = p.A[d * 16 + n];
+    const float Av = p.A[d * NS + n0 + n];
     const float a2 = Av * kLog2e;
     const float bias = p.bias ? p.bias[d] : 0.0f;
     const float Dv = p.D ? p.D[d] : 0.0f;
-    float lam = (p.dlast && valid) ? p.dlast[(b * p.dim + d) * 16 + n] : 0.0f;
+    float lam = (p.dlast && valid) ? p.dlast[(b * p.dim + d) * NS + n0 + n] : 0.0f;
     float gA = 0.0f, accD = 0.0f, accX = 0.0f;
 
     // Buffer descriptors with 32-bit byte offsets (the host checks that they fit): the wave's 4
@@ -124,10 +134,10 @@ void scan_bwd_ls_kernel(BlsParams p) {
     const __amdgpu_buffer_rsrc_t our = rows_rsrc(p.du, 4), oxr = rows_rsrc(p.ddelta, 4);
     const __amdgpu_buffer_rsrc_t ozr = HAS_Z ? rows_rsrc(p.dz, 4) : our;
     const __amdgpu_buffer_rsrc_t ckr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(p.ck) + row0 * nseg * 16, 0, (int)(nrows * nseg * 64), kLsWord3);
+        const_cast<float*>(p.ck) + row0 * nseg * NS, 0, (int)(nrows * nseg * NS * 4), kLsWord3);
     const uint32_t oi = (dr * (uint32_t)L + n) * es;  // this lane's step n of a segment, inputs
     const uint32_t of = (dr * (uint32_t)L + n) * 4u;  // and fp32 rows
-    const uint32_t ock = (dr * (uint32_t)nseg * 16u + n) * 4u;
+    const uint32_t ock = (dr * (uint32_t)(nseg * NS) + (uint32_t)(n0 + n)) * 4u;
 
     auto load_el = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff) __attribute__((always_inline)) {
         if constexpr (sizeof(T) == 2)
@@ -143,7 +153,7 @@ void scan_bwd_ls_kernel(BlsParams p) {
     const bool stager = tid < 256;
     const int sq = (wave >> 1) & 1, sn = (tid >> 3) & 15, st = (tid & 7) * 2;  // sq wave-uniform
     const __amdgpu_buffer_rsrc_t bcr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(static_cast<const char*>(sq ? p.C : p.B)) + b * 16 * L * es, 0, (int)(16 * L * es),
+        const_cast<char*>(static_cast<const char*>(sq ? p.C : p.B)) + (b * NS + n0) * L * es, 0, (int)(16 * L * es),
         kLsWord3);
     const uint32_t obc = (uint32_t)(sn * L + st) * es;
     float* const sdst = &s_bc[sq][sn * kBlRowP + st];
@@ -157,8 +167,10 @@ void scan_bwd_ls_kernel(BlsParams p) {
     };
 
     // raw inputs of this lane's step of a segment, and its state's saved value, one segment ahead
+    // (MULTI: also the earlier blocks' du, ddelta and sum of C h of this step, read whether or
+    // not this is the first block, which does not use them: no branch around the loads)
     struct Raw {
-        uint32_t x, u, z, g, h;
+        uint32_t x, u, z, g, h, pu, px, pz;
     };
     auto fetch = [&](int64_t k, Raw& w) __attribute__((always_inline)) {
         const uint32_t so = (uint32_t)(k * 16) * es, s4 = (uint32_t)(k * 64);
@@ -166,7 +178,14 @@ void scan_bwd_ls_kernel(BlsParams p) {
         w.u = load_el(ur, oi, so);
         w.z = HAS_Z ? load_el(zr, oi, so) : 0u;
         w.g = __builtin_amdgcn_raw_buffer_load_b32(gr, (int)of, (int)s4, 0);
-        w.h = __builtin_amdgcn_raw_buffer_load_b32(ckr, (int)ock, (int)s4, 0);
+        w.h = __builtin_amdgcn_raw_buffer_load_b32(ckr, (int)ock, (int)(k * NS * 4), 0);
+        if constexpr (MULTI) {
+            w.pu = __builtin_amdgcn_raw_buffer_load_b32(our, (int)of, (int)s4, 0);
+            w.px = __builtin_amdgcn_raw_buffer_load_b32(oxr, (int)of, (int)s4, 0);
+            w.pz = HAS_Z ? __builtin_amdgcn_raw_buffer_load_b32(ozr, (int)of, (int)s4, 0) : 0u;
+        } else {
+            w.pu = w.px = w.pz = 0u;
+        }
     };
 
     float* const area0 = &s_w[wave][0][0];
@@ -185,7 +204,7 @@ void scan_bwd_ls_kernel(BlsParams p) {
     // per-(channel, step) factors of this lane's step of segment k (the forward kernel's dt and
     // dt u, bit for bit)
     struct Fac {
-        float dt, dtu, gp, uu, sg, gz, h;
+        float dt, dtu, gp, uu, sg, gz, h, pu, px, pz;
     };
     auto factors = [&](const Raw& w, int64_t k) __attribute__((always_inline)) {
         Fac f;
@@ -212,6 +231,9 @@ void scan_bwd_ls_kernel(BlsParams p) {
             f.gz = 0.0f;
         }
         f.h = __uint_as_float(w.h);
+        f.pu = __uint_as_float(w.pu);
+        f.px = __uint_as_float(w.px);
+        f.pz = __uint_as_float(w.pz);
         return f;
     };
 
@@ -322,17 +344,25 @@ void scan_bwd_ls_kernel(BlsParams p) {
         {
             const float uu = cur.uu;
             const float gdt = __builtin_fmaf(uu, P1, P2);
-            const float gx = SOFTPLUS ? gdt * cur.sg : gdt * dt;
-            const float gu = __builtin_fmaf(gp, Dv, dt * P1);
+            float gx = SOFTPLUS ? gdt * cur.sg : gdt * dt;
+            float gu = first ? __builtin_fmaf(gp, Dv, dt * P1) : dt * P1 + cur.pu;
+            float ys = Ys;
+            if constexpr (MULTI) {
+                if (!first) {
+                    gx += cur.px;
+                    ys += cur.pz;
+                }
+            }
             if (live) {
-                accD = __builtin_fmaf(gp, uu, accD);
-                accX += gx;
+                if (first) accD = __builtin_fmaf(gp, uu, accD);
+                if (last) accX += gx;  // dbias sums the finished ddelta
             }
             const bool st_ok = live && valid;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gu), our, (int)(st_ok ? of : kLsDropBase), (int)s4, 0);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gx), oxr, (int)(st_ok ? of : kLsDropBase), (int)s4, 0);
             if constexpr (HAS_Z) {
-                const float gzo = cur.gz * __builtin_fmaf(Dv, uu, Ys);
+                // the sum over states of C h until the last block, then the gate's gradient
+                const float gzo = last ? cur.gz * __builtin_fmaf(Dv, uu, ys) : ys;
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gzo), ozr, (int)(st_ok ? of : kLsDropBase), (int)s4, 0);
             }
         }
@@ -347,14 +377,14 @@ void scan_bwd_ls_kernel(BlsParams p) {
                 acc.x += v.x;
                 acc.y += v.y;
             }
-            *reinterpret_cast<float2*>(p.bcpart + (((grp * p.batch + b) * 2 + sq) * 16 + sn) * p.lp + k * 16 + st) = acc;
+            *reinterpret_cast<float2*>(p.bcpart + (((grp * p.batch + b) * 2 + sq) * NS + n0 + sn) * p.lp + k * 16 + st) = acc;
             *reinterpret_cast<float2*>(sdst) = bcn;  // the next segment's B / C
         }
         cur = nxt;
     }
 
     if (valid) {
-        const int64_t i = (b * p.dim + d) * 16 + n;
+        const int64_t i = (b * p.dim + d) * NS + n0 + n;
         if (p.dh0) p.dh0[i] = lam;
         p.apart[i] = gA;
     }
@@ -365,8 +395,8 @@ void scan_bwd_ls_kernel(BlsParams p) {
         accX += __shfl_xor(accX, off, 64);
     }
     if (n == 0 && valid) {
-        p.dpart[b * p.dim + d] = accD;
-        p.bpart[b * p.dim + d] = accX;
+        if (first) p.dpart[b * p.dim + d] = accD;
+        if (last) p.bpart[b * p.dim + d] = accX;
     }
 }
 
@@ -376,8 +406,9 @@ void scan_bwd_ls_kernel(BlsParams p) {
 template <typename T, bool SP, bool HZ>
 int launch_bwd_ls_cfg(const BlsParams& q, hipStream_t stream) {
     void* args[] = {const_cast<BlsParams*>(&q)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ>),
-                           dim3((unsigned)(q.batch * q.groups)), dim3(64 * kBlsW), args, 0, stream) == hipSuccess
+    const void* fn = q.N > 16 ? reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ, true>)
+                              : reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)(q.batch * q.groups)), dim3(64 * kBlsW), args, 0, stream) == hipSuccess
                ? MAMBA_SCAN_OK
                : MAMBA_SCAN_ERR_LAUNCH;
 }
@@ -389,7 +420,7 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
     const BwdLayout l = bwd_ls_layout(s, given);
     char* ws = static_cast<char*>(p->workspace);
     float* ck = given ? const_cast<float*>(p->checkpoints) : reinterpret_cast<float*>(ws + l.off_ck);
-    const int64_t L = s.len, DL = s.dim * L;
+    const int64_t L = s.len, DL = s.dim * L, N = s.dstate;
     if (!given) {
         // the state before every segment, written by the forward lane-per-state kernel (the states
         // a forward call saves, bit for bit); its y goes to du, which the backward overwrites
@@ -408,14 +439,14 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
         f.batch = s.batch;
         f.dim = s.dim;
         f.len = L;
-        f.dstate = 16;
+        f.dstate = N;
         f.su_b = f.sdt_b = f.sz_b = f.sy_b = DL;
         f.su_d = f.sdt_d = f.sz_d = f.sy_d = L;
-        f.sB_b = f.sC_b = 16 * L;
+        f.sB_b = f.sC_b = N * L;
         f.sB_n = f.sC_n = L;
-        f.sh0_b = s.dim * 16;
-        f.sh0_d = 16;
-        f.sA_d = 16;
+        f.sh0_b = s.dim * N;
+        f.sh0_d = N;
+        f.sA_d = N;
         f.sD = f.sbias = 1;
         f.softplus = softplus ? 1 : 0;
         f.zoh_b = 0;
@@ -450,10 +481,17 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
     q.lp = l.lp;
     q.nseg = l.nseg;
     q.groups = l.groups;
+    q.N = N;
     const bool hz = p->z != nullptr;
-    const int rc = softplus ? (hz ? launch_bwd_ls_cfg<T, true, true>(q, stream) : launch_bwd_ls_cfg<T, true, false>(q, stream))
-                            : (hz ? launch_bwd_ls_cfg<T, false, true>(q, stream) : launch_bwd_ls_cfg<T, false, false>(q, stream));
-    if (rc != MAMBA_SCAN_OK) return rc;
+    // one launch per block of 16 states, in order (the sums over states carried in du, ddelta, dz)
+    for (int64_t n0 = 0; n0 < N; n0 += 16) {
+        q.n0 = n0;
+        q.first = n0 == 0;
+        q.last = n0 + 16 == N;
+        const int rc = softplus ? (hz ? launch_bwd_ls_cfg<T, true, true>(q, stream) : launch_bwd_ls_cfg<T, true, false>(q, stream))
+                                : (hz ? launch_bwd_ls_cfg<T, false, true>(q, stream) : launch_bwd_ls_cfg<T, false, false>(q, stream));
+        if (rc != MAMBA_SCAN_OK) return rc;
+    }
     BwdReduceParams r;
     r.bcpart = q.bcpart;
     r.apart = q.apart;
@@ -467,7 +505,7 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
     r.batch = s.batch;
     r.dim = s.dim;
     r.len = L;
-    r.dstate = 16;
+    r.dstate = N;
     r.lp = l.lp;
     r.groups = l.groups;
     return launch_bwd_reduce_any(r, stream);

@@ -305,8 +305,8 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     saved for the same inputs; the backward then does not recompute them. ``static_scratch``: call
     ``mamba_scan_bwd_static``, whose workspace is the library's own static per-device buffer (no
     workspace is allocated here; calls overlapping in time on one GPU must not be made).
-    ``kernel``: None (the library's choice: the lane-per-state kernel at 16 states, else the
-    segment-tiled one), "lanes" or "tiled" (forced; an error where it cannot run).
+    ``kernel``: None (the library's choice: the lane-per-state kernel at 16, 32 and 64 states,
+    else the segment-tiled one), "lanes" or "tiled" (forced; an error where it cannot run).
     """
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):

@@ -287,15 +287,23 @@ def test_static_backward_refusals():
 
 
 def test_backward_workspace_for_wide_states():
-    """Above 16 states the workspace holds the segment states of one block of 16 only, but B, C
-    and their per-group partials for all of them."""
+    """Above 16 states the segment-tiled kernel's workspace holds the segment states of one block
+    of 16 only, but B, C and their per-group partials for all of them; the lane-per-state kernel's
+    (32 and 64 states) holds every state's segment states and dB / dC partials per 16 channels."""
     lib = scan.load_library()
     for N, ckn in ((64, 16), (24, 16), (11, 8), (256, 16)):
         shp = scan.Shape(2, 200, 100, N)
-        n = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(shp), scan.F32, 0)
+        n = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(shp), scan.F32, scan.FORCE_TILED)
         lp, groups = 112, 4
         need = 2 * 2 * N * lp * 4 + 2 * 200 * (lp // 16) * ckn * 4 + groups * 2 * 2 * N * lp * 4
         assert need <= n < need + 2 * 200 * N * 4 + 4 * 2 * 200 * 4 + 6 * 256, (N, n, need)
+    for N in (32, 64):
+        shp = scan.Shape(2, 200, 100, N)
+        n = lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(shp), scan.F32, 0)
+        assert n == lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(shp), scan.F32, scan.FORCE_LANES)
+        lp, groups = 112, 13
+        need = 2 * 200 * (lp // 16) * N * 4 + groups * 2 * 2 * N * lp * 4 + 2 * 200 * (N + 2) * 4
+        assert need <= n < need + 6 * 256, (N, n, need)
 
 
 def test_backward_workspace_query():

@@ -68,10 +68,10 @@ def _check(x, softplus=True, with_h0=False, with_dlast=True, seed=0, tol=None, k
     return gg
 
 
-@pytest.mark.parametrize("wid,kernel", [(1, None), (2, None), (2, "tiled"), (3, None), (3, "tiled")])
+@pytest.mark.parametrize("wid,kernel", [(1, None), (1, "tiled"), (2, None), (2, "tiled"), (3, None), (3, "tiled")])
 def test_workload_backward_parity(wid, kernel):
-    """Default: the lane-per-state kernel at 16 states (workloads 2, 3), the segment-tiled one at
-    32 (workload 1); the segment-tiled kernel forced at 16 states as well."""
+    """Default: the lane-per-state kernel (16 states in workloads 2, 3; 32 in workload 1, two
+    blocks of 16); the segment-tiled kernel forced as well."""
     w = workloads.WORKLOADS[wid]
     x = workloads.make_inputs(w)
     print(f"backward parity, workload {wid}: {w.name}, kernel {kernel or 'default'}", flush=True)
@@ -112,49 +112,55 @@ def test_backward_edge_cases(idx):
            with_dlast=fl.get("dlast", True), seed=idx)
 
 
-# 16 states with the lane-per-state kernel forced: ragged lengths (segments of 16 steps), channel
-# counts that leave workgroups (16 channels) and waves (4) partly empty, every optional input on
-# and off
-EDGE16 = [
-    # (batch, dim, L, dtype, flags)
-    (1, 1, 1, "f32", {}),
-    (1, 3, 2, "bf16", {"h0": True}),
-    (2, 16, 15, "f32", {}),
-    (1, 17, 16, "bf16", {"dlast": False}),
-    (3, 20, 17, "f32", {"h0": True}),
-    (2, 33, 31, "bf16", {"softplus": False}),
-    (1, 64, 33, "f32", {"z": False, "D": False, "bias": False}),
-    (2, 48, 100, "bf16", {"a_kind": "rand", "h0": True}),
-    (1, 130, 257, "f32", {"z": False}),
-    (2, 96, 64, "bf16", {"D": False, "dlast": False}),
-    (1, 40, 1000, "f32", {"softplus": False, "h0": True}),
+# The lane-per-state kernel forced: ragged lengths (segments of 16 steps), channel counts that
+# leave workgroups (16 channels) and waves (4) partly empty, every optional input on and off; 32
+# and 64 states (blocks of 16 carried through du, ddelta, dz) with and without the gate
+EDGE_LANES = [
+    # (batch, dim, N, L, dtype, flags)
+    (1, 1, 16, 1, "f32", {}),
+    (1, 3, 16, 2, "bf16", {"h0": True}),
+    (2, 16, 16, 15, "f32", {}),
+    (1, 17, 16, 16, "bf16", {"dlast": False}),
+    (3, 20, 16, 17, "f32", {"h0": True}),
+    (2, 33, 16, 31, "bf16", {"softplus": False}),
+    (1, 64, 16, 33, "f32", {"z": False, "D": False, "bias": False}),
+    (2, 48, 16, 100, "bf16", {"a_kind": "rand", "h0": True}),
+    (1, 130, 16, 257, "f32", {"z": False}),
+    (2, 96, 16, 64, "bf16", {"D": False, "dlast": False}),
+    (1, 40, 16, 1000, "f32", {"softplus": False, "h0": True}),
+    (2, 70, 32, 40, "f32", {"h0": True}),
+    (1, 33, 32, 17, "bf16", {"z": False}),
+    (1, 130, 64, 70, "bf16", {"h0": True}),
+    (2, 20, 64, 33, "f32", {"softplus": False, "dlast": False}),
+    (1, 50, 64, 300, "bf16", {"D": False, "bias": False, "a_kind": "rand"}),
 ]
 
 
-@pytest.mark.parametrize("idx", range(len(EDGE16)))
+@pytest.mark.parametrize("idx", range(len(EDGE_LANES)))
 def test_lane_backward_edge_cases(idx):
-    batch, dim, L, dtype, fl = EDGE16[idx]
-    print(f"lane-per-state backward edge case {EDGE16[idx]}", flush=True)
-    x = gu.case(700 + idx, batch, dim, 16, L, dtype=dtype, z=fl.get("z", True), D=fl.get("D", True),
+    batch, dim, N, L, dtype, fl = EDGE_LANES[idx]
+    print(f"lane-per-state backward edge case {EDGE_LANES[idx]}", flush=True)
+    x = gu.case(700 + idx, batch, dim, N, L, dtype=dtype, z=fl.get("z", True), D=fl.get("D", True),
                 bias=fl.get("bias", True), a_kind=fl.get("a_kind", "mamba"))
     _check(x, softplus=fl.get("softplus", True), with_h0=fl.get("h0", False),
            with_dlast=fl.get("dlast", True), seed=idx, kernel="lanes")
 
 
-def test_state_blocks_are_independent():
+@pytest.mark.parametrize("kernel", ["tiled", "lanes"])
+def test_state_blocks_are_independent(kernel):
     """dB, dC, dA and dh0 of a state depend on no other state, so with 32 states the first 16
-    states' gradients are the bits of a 16-state run on those states alone (the same block of the
-    segment-tiled kernel, which 32 states run on; forced for the 16-state run)."""
+    states' gradients are the bits of a 16-state run on those states alone (the same first block
+    of 16 states, with either kernel)."""
     x = gu.case(73, 2, 96, 32, 90, dtype="bf16")
     rng = np.random.default_rng(4)
     dy = rng.standard_normal((2, 96, 90)).astype(np.float32)
     dlast = rng.standard_normal((2, 96, 32)).astype(np.float32)
     h0 = rng.standard_normal((2, 96, 32)).astype(np.float32)
-    full = _grads_gpu(x, dy, dlast, True, h0)
+    full = _grads_gpu(x, dy, dlast, True, h0, kernel=kernel)
     half = dict(x, A=np.ascontiguousarray(x["A"][:, :16]), B=np.ascontiguousarray(x["B"][:, :16]),
                 C=np.ascontiguousarray(x["C"][:, :16]))
     part = _grads_gpu(half, dy, np.ascontiguousarray(dlast[..., :16]), True, np.ascontiguousarray(h0[..., :16]),
-                      kernel="tiled")
+                      kernel=kernel)
     for k in ("B", "C"):
         assert np.array_equal(full[k][:, :16], part[k]), k
     assert np.array_equal(full["A"][:, :16], part["A"])
