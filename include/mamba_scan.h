@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 8
+#define MAMBA_SCAN_ABI_VERSION 9
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -59,7 +59,8 @@ typedef enum mamba_scan_dtype {
 #define MAMBA_SCAN_RETURN_LAST_STATE (1u << 1) /* write last_state */
 /* B discretised by zero-order hold: the input term becomes (exp(dt*A[d,n]) - 1) / A[d,n] * B * u
  * (dt * B * u where A[d,n] = 0) instead of dt * B * u. "手把手用PyTorch实现Mamba的SSM层…" §2.1:
- * B_d = A^-1 (e^{A dt} - I) B, for a diagonal A. Forward only (mamba_scan_bwd rejects it). */
+ * B_d = A^-1 (e^{A dt} - I) B, for a diagonal A. Forward only (mamba_scan_bwd rejects it). Run by
+ * the lane-per-state kernels at dstate 16, 32 and 64 (ABI 9), else by the tiled or generic one. */
 #define MAMBA_SCAN_ZOH_B (1u << 2)
 /* Save the state before every 16-step segment, for the backward pass: the forward writes
  * h before steps 0, 16, 32, ... of every (b, d) row to the workspace, laid out (batch, dim,
@@ -78,7 +79,8 @@ typedef enum mamba_scan_dtype {
 #define MAMBA_SCAN_FORCE_TILED (1u << 9)   /* the LDS-tiled kernel; error if it cannot run */
 #define MAMBA_SCAN_FORCE_LANES (1u << 10)  /* one 16-lane row per channel, one lane per state
                                               at dstate 16 and dstate/16 states per lane at 32
-                                              or 64; no ZOH_B; error if it cannot run (ABI 5) */
+                                              or 64; ZOH_B from ABI 9; error if it cannot run
+                                              (ABI 5) */
 /* Chunked along the sequence (ABI 7): one wave per channel, its four 16-lane rows scan four
  * consecutive 16-step runs of each 64-step chunk and are combined with the associative (a, b)
  * operator of the parallel scan ("手把手用PyTorch实现Mamba的SSM层…" §3.2), the state carried

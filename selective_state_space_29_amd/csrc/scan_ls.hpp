@@ -57,24 +57,33 @@ __device__ __forceinline__ void bl_for_ls(F&& f) {
 }
 
 struct LsRegs {
-    float h, a2;
-    float dt[2], dtu[2];
+    float h, a2, ia;  // ia = 1 / A (zero-order hold only)
+    float dt[2], dtu[2];  // dtu: dt u, or u with the zero-order hold
     float Bv[2][kLsH], Cv[2][kLsH];  // [half][step] of this lane's state rows of B and C
     float pv[4];
     float* sp;  // this lane's state row in LDS
 };
 
-// Steps S .. kLsH-1 of half-chunk HALF (buffer BUF) of the recurrence.
-template <int HALF, int BUF, int S>
+// Steps S .. kLsH-1 of half-chunk HALF (buffer BUF) of the recurrence. The input term: dt u B
+// (Euler), or with the zero-order hold (ZOH) its coefficient of B times u, times B.
+template <int HALF, int BUF, int S, bool ZOH>
 __device__ __forceinline__ void ls_steps(LsRegs& r) {
     if constexpr (S < kLsH) {
         constexpr int s = HALF * kLsH + S;  // step within the chunk
-        const float dA = hw_exp2(row_bcast<s / 2>(r.dt[s % 2]) * r.a2);
-        r.h = __builtin_fmaf(dA, r.h, row_bcast<s / 2>(r.dtu[s % 2]) * r.Bv[BUF][S]);
+        if constexpr (ZOH) {
+            const float dtb = row_bcast<s / 2>(r.dt[s % 2]);
+            const float x2 = dtb * r.a2;
+            const float dA = hw_exp2(x2);
+            const float inc = zoh_coef2_f(dtb, x2, dA, r.ia) * row_bcast<s / 2>(r.dtu[s % 2]) * r.Bv[BUF][S];
+            r.h = __builtin_fmaf(dA, r.h, inc);
+        } else {
+            const float dA = hw_exp2(row_bcast<s / 2>(r.dt[s % 2]) * r.a2);
+            r.h = __builtin_fmaf(dA, r.h, row_bcast<s / 2>(r.dtu[s % 2]) * r.Bv[BUF][S]);
+        }
         r.pv[s % 4] = r.Cv[BUF][S] * r.h;
         if constexpr (s % 4 == 3)
             *reinterpret_cast<float4*>(r.sp + (s - 3)) = float4{r.pv[0], r.pv[1], r.pv[2], r.pv[3]};
-        ls_steps<HALF, BUF, S + 1>(r);
+        ls_steps<HALF, BUF, S + 1, ZOH>(r);
     }
 }
 
@@ -111,8 +120,9 @@ __device__ __forceinline__ void pack4_bf16(uint32_t (&v)[4]) {
     v[0] = v[0] | (v[1] << 16), v[1] = v[2] | (v[3] << 16), v[2] = 0u, v[3] = 0u;
 }
 
-// VEC: B and C rows 4-element aligned, staged with one vector load per 4 steps
-template <typename T, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK>
+// VEC: B and C rows 4-element aligned, staged with one vector load per 4 steps; ZOH: B
+// discretised by zero-order hold
+template <typename T, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK, bool ZOH>
 __global__ __launch_bounds__(64 * kLsWaves) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_ls_kernel(ScanParams p) {
     __shared__ __align__(16) float s_p[kLsWaves * 4 * kLsChanP];
@@ -130,7 +140,11 @@ void scan_ls_kernel(ScanParams p) {
     const int64_t L = p.len;
 
     LsRegs r;
-    r.a2 = p.A[d * p.sA_d + n] * kLog2e;
+    {
+        const float an = p.A[d * p.sA_d + n];
+        r.a2 = an * kLog2e;
+        r.ia = an != 0.0f ? 1.0f / an : 0.0f;
+    }
     r.h = p.h0 ? p.h0[b * p.sh0_b + d * p.sh0_d + n] : 0.0f;
     const float bias = p.bias ? p.bias[d * p.sbias] : 0.0f;
     const float Dv = p.D ? p.D[d * p.sD] : 0.0f;  // no skip term: D = 0
@@ -251,8 +265,9 @@ void scan_ls_kernel(ScanParams p) {
         }
     };
 
-    // Per-(channel, step) factors of this lane's two steps of chunk k: dt and dt*u (read by the
-    // whole row through the broadcast), and u and the gate for the epilogue.
+    // Per-(channel, step) factors of this lane's two steps of chunk k: dt and dt*u (u with the
+    // zero-order hold; read by the whole row through the broadcast), and u and the gate for the
+    // epilogue.
     float uv[2], gz[2];
     auto prologue = [&](const Raw& w) __attribute__((always_inline)) {
 #pragma unroll
@@ -260,7 +275,7 @@ void scan_ls_kernel(ScanParams p) {
             const float xb = widen(w.x[j]) + bias;
             r.dt[j] = SOFTPLUS ? softplus_f(xb) : hw_exp2(xb * kLog2e);
             uv[j] = widen(w.u[j]);
-            r.dtu[j] = r.dt[j] * uv[j];
+            r.dtu[j] = ZOH ? uv[j] : r.dt[j] * uv[j];
             gz[j] = HAS_Z ? silu_f(widen(w.z[j])) : 1.0f;
         }
     };
@@ -293,9 +308,9 @@ void scan_ls_kernel(ScanParams p) {
         read_bc(buf, 1);
         // the states before steps t0 and t0 + 16 (segments 2k and 2k + 1), stored with y
         const float hk0 = r.h;
-        ls_steps<0, 0, 0>(r);
+        ls_steps<0, 0, 0, ZOH>(r);
         const float hk1 = r.h;
-        ls_steps<1, 1, 0>(r);
+        ls_steps<1, 1, 0, ZOH>(r);
         // the next chunk's B / C into the other buffer (its last readers passed the barrier above)
         *reinterpret_cast<float4*>(sdst + (buf ^ 1) * kBufStride) =
             widen4<T, VEC>(sv);
@@ -358,7 +373,7 @@ constexpr int kLwChanP = 16 * kLwRowP + 16;   // one channel's 16 lane rows, ske
 // state rows, and a staging thread's 16-byte write, touch distinct banks across 16 lanes.
 __device__ __forceinline__ int lw_bc_at(int m, int g) { return m * kLwT + (((g ^ (m >> 2)) & 3) << 2); }
 
-template <typename T, int N, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK>
+template <typename T, int N, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK, bool ZOH>
 __global__ __launch_bounds__(64 * kLsWaves) __attribute__((amdgpu_waves_per_eu(4)))
 void scan_ls_wide_kernel(ScanParams p) {
     static_assert(N == 32 || N == 64, "wide lane-per-state kernel: 32 or 64 states");
@@ -378,10 +393,12 @@ void scan_ls_wide_kernel(ScanParams p) {
     const int64_t d = valid ? d0 + c : p.dim - 1;
     const int64_t L = p.len;
 
-    float h[S], a2[S];
+    float h[S], a2[S], ia[S];  // ia = 1 / A (zero-order hold only)
 #pragma unroll
     for (int k = 0; k < S; ++k) {
-        a2[k] = p.A[d * p.sA_d + j + 16 * k] * kLog2e;
+        const float an = p.A[d * p.sA_d + j + 16 * k];
+        a2[k] = an * kLog2e;
+        ia[k] = an != 0.0f ? 1.0f / an : 0.0f;
         h[k] = p.h0 ? p.h0[b * p.sh0_b + d * p.sh0_d + j + 16 * k] : 0.0f;
     }
     const float bias = p.bias ? p.bias[d * p.sbias] : 0.0f;
@@ -501,7 +518,7 @@ void scan_ls_wide_kernel(ScanParams p) {
         const float xb = widen(w.x) + bias;
         dt = SOFTPLUS ? softplus_f(xb) : hw_exp2(xb * kLog2e);
         uv = widen(w.u);
-        dtu = dt * uv;
+        dtu = ZOH ? uv : dt * uv;  // u with the zero-order hold, whose coefficient replaces dt
         gz = HAS_Z ? silu_f(widen(w.z)) : 1.0f;
     };
 
@@ -524,7 +541,13 @@ void scan_ls_wide_kernel(ScanParams p) {
             for (int k = 0; k < S; ++k) {
                 const float bb = i == 0 ? bv[k].x : i == 1 ? bv[k].y : i == 2 ? bv[k].z : bv[k].w;
                 const float cc = i == 0 ? cv[k].x : i == 1 ? cv[k].y : i == 2 ? cv[k].z : cv[k].w;
-                h[k] = __builtin_fmaf(hw_exp2(dtb * a2[k]), h[k], dtub * bb);
+                if constexpr (ZOH) {
+                    const float x2 = dtb * a2[k];
+                    const float dA = hw_exp2(x2);
+                    h[k] = __builtin_fmaf(dA, h[k], zoh_coef2_f(dtb, x2, dA, ia[k]) * dtub * bb);
+                } else {
+                    h[k] = __builtin_fmaf(hw_exp2(dtb * a2[k]), h[k], dtub * bb);
+                }
                 acc = k == 0 ? cc * h[k] : __builtin_fmaf(cc, h[k], acc);
             }
             pv[i] = acc;
@@ -589,10 +612,11 @@ void scan_ls_wide_kernel(ScanParams p) {
 // ---------------------------------------------------------------------------------------------
 // host side
 
-// The lane-per-state kernels take dstate 16, 32 or 64 with the Euler input term, and shapes whose
-// byte offsets within a wave's rows (u, delta, z, y) and within a batch's B / C fit 31 bits.
+// The lane-per-state kernels take dstate 16, 32 or 64 (the zero-order hold without saved states,
+// which only the Euler backward reads), and shapes whose byte offsets within a wave's rows (u,
+// delta, z, y) and within a batch's B / C fit 31 bits.
 inline bool ls_eligible(const ScanParams& q, int64_t es) {
-    if ((q.dstate != 16 && q.dstate != 32 && q.dstate != 64) || q.zoh_b) return false;
+    if ((q.dstate != 16 && q.dstate != 32 && q.dstate != 64) || (q.zoh_b && q.ck)) return false;
     const int64_t lim = (int64_t)1 << 31;
     const auto rows_ok = [&](const void* ptr, int64_t sd, int64_t e) {
         return ptr == nullptr || (3 * sd + q.len) * e < lim;
@@ -605,14 +629,14 @@ inline bool ls_eligible(const ScanParams& q, int64_t es) {
     return true;
 }
 
-template <typename T, bool SP, bool HZ, bool VEC, bool CK>
+template <typename T, bool SP, bool HZ, bool VEC, bool CK, bool ZOH>
 int launch_ls_cfg(const ScanParams& q, hipStream_t stream) {
     const void* fn;
     int64_t per_group;
     switch (q.dstate) {
-        case 16: fn = reinterpret_cast<const void*>(&scan_ls_kernel<T, SP, HZ, VEC, CK>); per_group = 16; break;
-        case 32: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 32, SP, HZ, VEC, CK>); per_group = 16; break;
-        default: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 64, SP, HZ, VEC, CK>); per_group = 16; break;
+        case 16: fn = reinterpret_cast<const void*>(&scan_ls_kernel<T, SP, HZ, VEC, CK, ZOH>); per_group = 16; break;
+        case 32: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 32, SP, HZ, VEC, CK, ZOH>); per_group = 16; break;
+        default: fn = reinterpret_cast<const void*>(&scan_ls_wide_kernel<T, 64, SP, HZ, VEC, CK, ZOH>); per_group = 16; break;
     }
     void* args[] = {const_cast<ScanParams*>(&q)};
     const int64_t groups = q.batch * ((q.dim + per_group - 1) / per_group);
@@ -623,8 +647,11 @@ int launch_ls_cfg(const ScanParams& q, hipStream_t stream) {
 
 template <typename T, bool SP, bool HZ, bool VEC>
 int launch_ls_ck(const ScanParams& q, hipStream_t stream) {
-    // saving the segment states is a separate instantiation: the plain forward issues no stores for it
-    return q.ck ? launch_ls_cfg<T, SP, HZ, VEC, true>(q, stream) : launch_ls_cfg<T, SP, HZ, VEC, false>(q, stream);
+    // saving the segment states is a separate instantiation: the plain forward issues no stores
+    // for it; so is the zero-order hold (never with saved states)
+    if (q.zoh_b) return launch_ls_cfg<T, SP, HZ, VEC, false, true>(q, stream);
+    return q.ck ? launch_ls_cfg<T, SP, HZ, VEC, true, false>(q, stream)
+                : launch_ls_cfg<T, SP, HZ, VEC, false, false>(q, stream);
 }
 
 template <typename T, bool SP, bool HZ>

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 8
+    assert scan.load_library().mamba_scan_abi_version() == 9
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -124,12 +124,11 @@ CASES = [
     ("step_and_chunked_forced", _flags(scan.FORCE_STEP | scan.FORCE_CHUNKED), -6),
     ("checkpoints_with_step", lambda c: _ck_ws(c, 1 << 20, extra=scan.FORCE_STEP), -8),
     ("lanes_and_tiled_forced", _flags(scan.FORCE_LANES | scan.FORCE_TILED), -6),
-    # the lane-per-state kernels take 16, 32 or 64 states, the Euler input term, 31-bit row offsets
+    # the lane-per-state kernels take 16, 32 or 64 states and 31-bit row offsets
     ("lanes_forced_8_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
                                          setattr(c["shape"], "dstate", 8)), -8),
     ("lanes_forced_48_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
                                           setattr(c["shape"], "dstate", 48)), -8),
-    ("lanes_forced_zoh", _flags(scan.DELTA_SOFTPLUS | scan.FORCE_LANES | scan.ZOH_B), -8),
     ("lanes_forced_wide_rows", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_LANES),
                                           setattr(c["st"], "u", (ctypes.c_int64 * 3)(1 << 31, 1 << 29, 1))), -8),
     ("y_aliases_u", _set("ptrs", "y", (1 << 40) + (1 << 32) + 64), -6),
@@ -160,7 +159,8 @@ def test_invalid_arguments_are_rejected(name, mutate, code):
 
 @pytest.mark.parametrize("extra,dstate,expect", [
     (scan.FORCE_GENERIC, 16, 1), (scan.FORCE_TILED, 16, 2), (scan.FORCE_LANES, 16, 3),
-    (scan.FORCE_CHUNKED, 16, 4), (0, 24, 2), (0, 100, 1), (scan.ZOH_B, 16, 2),
+    (scan.FORCE_CHUNKED, 16, 4), (0, 24, 2), (0, 100, 1), (scan.ZOH_B, 16, 3), (scan.ZOH_B, 64, 3),
+    (scan.ZOH_B, 24, 2), (scan.ZOH_B | scan.FORCE_TILED, 16, 2), (scan.ZOH_B | scan.FORCE_LANES, 32, 3),
     (scan.FORCE_LANES, 64, 3), (scan.FORCE_STEP, 16, 5)])
 def test_kernel_query(extra, dstate, expect):
     """mamba_scan_fwd_kernel names the kernel a call would run (the forced one, or the default

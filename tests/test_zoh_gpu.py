@@ -1,7 +1,8 @@
 """GPU parity of the zero-order-hold B discretisation (MAMBA_SCAN_ZOH_B) against the fp64 oracle
-with ``zoh_b=True``, for both kernels. Bars as for the Euler scan: max|g - r| / (1 + |r|) <= 1e-4
-for fp32 inputs, <= 2e-3 for bf16 inputs (the GPU's coefficient (e^{dt A} - 1) / A is within
-2^-20 relative of the exact one, see zoh_coef_f)."""
+with ``zoh_b=True``, for the lane-per-state (16, 32, 64 states), tiled and generic kernels. Bars as
+for the Euler scan: max|g - r| / (1 + |r|) <= 1e-4 for fp32 inputs, <= 2e-3 for bf16 inputs (the
+GPU's coefficient (e^{dt A} - 1) / A is within 2^-20 relative of the exact one, see zoh_coef_f
+and zoh_coef2_f)."""
 
 import numpy as np
 import pytest
@@ -35,11 +36,12 @@ def _check(x, tol, kernel=None, softplus=True, h0=None):
     assert ey <= tol and el <= tol, (ey, el)
 
 
-@pytest.mark.parametrize("wid", [2, 3])
-def test_zoh_workload_parity(wid):
+@pytest.mark.parametrize("wid,kernel", [(1, None), (2, None), (3, None), (3, "tiled")])
+def test_zoh_workload_parity(wid, kernel):
+    """Default: the lane-per-state kernels (32 states in workload 1, 16 in 2 and 3)."""
     w = workloads.WORKLOADS[wid]
-    print(f"zoh parity, workload {wid}: {w.name}", flush=True)
-    _check(workloads.make_inputs(w), 1e-4 if w.dtype == "f32" else 2e-3)
+    print(f"zoh parity, workload {wid}: {w.name}, kernel {kernel}", flush=True)
+    _check(workloads.make_inputs(w), 1e-4 if w.dtype == "f32" else 2e-3, kernel=kernel)
 
 
 EDGE = [
@@ -52,6 +54,16 @@ EDGE = [
     (1, 64, 64, 32, "f32", "rand", "tiled", True),
     (2, 33, 16, 17, "f32", "zeros_mixed", "generic", True),
     (1, 40, 100, 23, "f32", "rand", "generic", False),
+    # the lane-per-state kernels: ragged chunks (32 steps at 16 states, 16 at 32 and 64), partly
+    # filled waves and workgroups, both sides of the series threshold in one chunk
+    (2, 64, 16, 64, "f32", "mamba", "lanes", False),
+    (2, 37, 16, 45, "bf16", "rand", "lanes", True),
+    (1, 70, 16, 40, "f32", "zeros_mixed", "lanes", False),
+    (2, 64, 16, 100, "f32", "tiny", "lanes", True),
+    (1, 50, 32, 33, "bf16", "mamba", "lanes", False),
+    (2, 19, 32, 70, "f32", "zeros_mixed", "lanes", True),
+    (1, 64, 64, 31, "f32", "rand", "lanes", True),
+    (1, 33, 64, 50, "bf16", "tiny", "lanes", False),
 ]
 
 
@@ -78,10 +90,10 @@ def test_zoh_edge_cases(idx):
     _check(x, 1e-4 if dtype == "f32" else 2e-3, kernel=kernel, h0=h0)
 
 
-@pytest.mark.parametrize("kernel", ["tiled", "generic"])
-def test_zoh_with_zero_A_is_euler_bit_for_bit(kernel):
+@pytest.mark.parametrize("kernel,N", [("tiled", 16), ("generic", 16), ("lanes", 16), ("lanes", 64)])
+def test_zoh_with_zero_A_is_euler_bit_for_bit(kernel, N):
     """At A = 0 the zero-order-hold coefficient is dt exactly: the same bits as the Euler scan."""
-    x = gu.case(720, 2, 64, 16, 64, dtype="bf16")
+    x = gu.case(720, 2, 64, N, 64, dtype="bf16")
     x["A"] = np.zeros_like(x["A"])
     ye, le = _run(x, kernel, zoh=False)
     yz, lz = _run(x, kernel, zoh=True)
