@@ -198,7 +198,9 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *    plus MAMBA_SCAN_SAVE_CHECKPOINTS when `checkpoints` is given), 256-byte aligned, device
  *    memory owned by the caller (states every 16 steps unless given; partial sums of dB and dC
  *    per group of channels, 16 channels for the lane-per-state kernel, 64 for the segment-tiled
- *    one, which also keeps fp32 copies of B and C).
+ *    one, which also keeps fp32 copies of B and C; for few long rows the lane-per-state kernel
+ *    splits the sequence into parts run side by side and keeps per-part partial sums of dA, dD,
+ *    dbias and the adjoint handed from part to part).
  *  - Flags: MAMBA_SCAN_DELTA_SOFTPLUS, and at most one of the kernel choices (ABI 8;
  *    MAMBA_SCAN_ERR_ARGS for both or any other flag):
  *      MAMBA_SCAN_FORCE_LANES: the lane-per-state backward, one lane per (channel, state) as in

@@ -468,17 +468,20 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdReduceParams p) {
         for (int k = 0; k < 4; ++k)
             if (t + k < p.len) dst[k] = a[k];
     } else if (i < 2 * nbc4 + na) {
+        // over the batch, and within a batch over the sequence parts in order
         const int64_t j = i - 2 * nbc4;
         float acc = 0.0f;
-        for (int64_t b = 0; b < p.batch; ++b) acc += p.apart[b * na + j];
+        for (int64_t b = 0; b < p.batch; ++b)
+            for (int64_t q = 0; q < p.parts; ++q) acc += p.apart[(q * p.batch + b) * na + j];
         p.dA[j] = acc;
     } else if (i < 2 * nbc4 + na + p.dim) {
         const int64_t d = i - 2 * nbc4 - na;
         float accd = 0.0f, accb = 0.0f;
-        for (int64_t b = 0; b < p.batch; ++b) {
-            accd += p.dpart[b * p.dim + d];
-            accb += p.bpart[b * p.dim + d];
-        }
+        for (int64_t b = 0; b < p.batch; ++b)
+            for (int64_t q = 0; q < p.parts; ++q) {
+                accd += p.dpart[(q * p.batch + b) * p.dim + d];
+                accb += p.bpart[(q * p.batch + b) * p.dim + d];
+            }
         if (p.dD) p.dD[d] = accd;
         if (p.dbias) p.dbias[d] = accb;
     }

@@ -62,10 +62,14 @@ struct BlsParams {
     float* dz;
     float* dh0;
     float* bcpart;  // (groups, batch, 2, N, lp) dB / dC partials of each channel group
-    float* apart;   // (batch, dim, N)
-    float* dpart;   // (batch, dim)
-    float* bpart;   // (batch, dim)
+    float* apart;   // (parts, batch, dim, N)
+    float* dpart;   // (parts, batch, dim)
+    float* bpart;   // (parts, batch, dim)
+    float* carry;   // sub-parts 1 .. subs-1: (subs - 1, batch, dim, N) adjoint contributions,
+                    // then as many decay products
     int64_t batch, dim, len, lp, nseg, groups;
+    int64_t parts, spp;  // sequence parts; segments per part (the last part may have fewer)
+    int64_t subs, sspp;  // the pre-pass's sub-parts (subs / parts to a part); segments per sub-part
     int64_t N, n0;    // dstate; this launch's states n0 .. n0 + 15
     int first, last;  // first / last block of 16 states: initialises / finishes the sums
 };
@@ -84,6 +88,15 @@ __device__ __forceinline__ void bl_for(F&& f) {
     }
 }
 
+// Sequence parts: with p.parts > 1 workgroup (part, b, group) walks only the part's segments,
+// part * spp .. (part + 1) * spp - 1. The reverse recurrence is linear in the adjoint it starts
+// from, lam -> (lam + gp C) a per step, so a part's run over its steps from a zero adjoint gives
+// a contribution R and its decays a product D such that the adjoint leaving the part is R + D lam
+// for any entering lam. scan_bwd_ls_carry_kernel computes R and D for every sub-part of parts
+// 1 .. P-1 (subs / P sub-parts tile a part), and part p starts from dlast folded through those of
+// the sub-parts after it, last first. dh0 comes from part 0; the dA, dD and dbias partials are
+// kept per part and added in part order by the reduction.
+//
 // MULTI: one of several blocks of 16 states (32 or 64 states): du, ddelta and, with a gate, the
 // sum over states of C h are read back from the earlier blocks' launches and added to, in block
 // order; the first block adds the skip term, the last one finishes dz. Otherwise the only block.
@@ -96,14 +109,17 @@ void scan_bwd_ls_kernel(BlsParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t b = blockIdx.x / p.groups;
-    const int64_t grp = blockIdx.x - b * p.groups;
+    const int64_t bg = p.batch * p.groups;
+    const int64_t part = blockIdx.x / bg;
+    const int64_t b = (blockIdx.x - part * bg) / p.groups;
+    const int64_t grp = blockIdx.x - part * bg - b * p.groups;
     const int64_t d0 = grp * (4 * W) + wave * 4;
     const int c = lane >> 4, n = lane & 15;
     const bool valid = d0 + c < p.dim;
     const int64_t d = valid ? d0 + c : p.dim - 1;  // rows past dim: row dim-1's decay, no gradient
     const int64_t L = p.len;
     const int64_t nseg = p.nseg;
+    const int64_t kbeg = part * p.spp, kend = kbeg + p.spp < nseg ? kbeg + p.spp : nseg;  // this part
     const int64_t NS = MULTI ? p.N : 16, n0 = MULTI ? p.n0 : 0;  // state count, this block's first
     const bool first = !MULTI || p.first, last = !MULTI || p.last;
 
@@ -111,7 +127,17 @@ void scan_bwd_ls_kernel(BlsParams p) {
     const float a2 = Av * kLog2e;
     const float bias = p.bias ? p.bias[d] : 0.0f;
     const float Dv = p.D ? p.D[d] : 0.0f;
-    float lam = (p.dlast && valid) ? p.dlast[(b * p.dim + d) * NS + n0 + n] : 0.0f;
+    const int64_t si = (b * p.dim + d) * NS + n0 + n;  // this lane's (b, d, state)
+    float lam = (p.dlast && valid) ? p.dlast[si] : 0.0f;
+    if (valid) {
+        // the adjoint entering this part: dlast carried through the later sub-parts, last first
+        // (rows past dim keep a zero adjoint: their dB / dC terms must vanish)
+        const int64_t pstride = p.batch * p.dim * NS;
+        const float* const dprod = p.carry + (p.subs - 1) * pstride;
+        const int64_t gend = (part + 1) * (p.subs / p.parts);  // the first sub-part after this part
+        for (int64_t g = p.subs - 1; g >= gend; --g)
+            lam = __builtin_fmaf(dprod[(g - 1) * pstride + si], lam, p.carry[(g - 1) * pstride + si]);
+    }
     float gA = 0.0f, accD = 0.0f, accX = 0.0f;
 
     // Buffer descriptors with 32-bit byte offsets (the host checks that they fit): the wave's 4
@@ -240,18 +266,18 @@ void scan_bwd_ls_kernel(BlsParams p) {
     // Software pipeline: segment k-1's raw inputs and B / C are loaded at the top of segment k
     // and turned into values before segment k's stores, so no wait for them covers a store.
     Raw raw;
-    fetch(nseg - 1, raw);
+    fetch(kend - 1, raw);
     uint32_t sv[2];
     if (stager) {
-        stage_fetch(nseg - 1, sv);
+        stage_fetch(kend - 1, sv);
         stage_store(sv);
     }
-    Fac cur = factors(raw, nseg - 1);
-    for (int64_t k = nseg - 1; k >= 0; --k) {
+    Fac cur = factors(raw, kend - 1);
+    for (int64_t k = kend - 1; k >= kbeg; --k) {
         __syncthreads();  // the segment's B / C staged; the previous segment's LDS reads done
         const uint32_t s4 = (uint32_t)(k * 64);
         const bool live = k * 16 + n < L;
-        const int64_t kp = k > 0 ? k - 1 : 0;
+        const int64_t kp = k > kbeg ? k - 1 : kbeg;
         fetch(kp, raw);
         if (stager) stage_fetch(kp, sv);
         const float dt = cur.dt, dtu = cur.dtu, gp = cur.gp;
@@ -384,9 +410,8 @@ void scan_bwd_ls_kernel(BlsParams p) {
     }
 
     if (valid) {
-        const int64_t i = (b * p.dim + d) * NS + n0 + n;
-        if (p.dh0) p.dh0[i] = lam;
-        p.apart[i] = gA;
+        if (p.dh0 && part == 0) p.dh0[si] = lam;
+        p.apart[part * p.batch * p.dim * NS + si] = gA;
     }
     // the channel's dD and dbias shares: its 16 lanes (one step of every segment each)
 #pragma unroll
@@ -395,8 +420,138 @@ void scan_bwd_ls_kernel(BlsParams p) {
         accX += __shfl_xor(accX, off, 64);
     }
     if (n == 0 && valid) {
-        if (first) p.dpart[b * p.dim + d] = accD;
-        if (last) p.bpart[b * p.dim + d] = accX;
+        if (first) p.dpart[(part * p.batch + b) * p.dim + d] = accD;
+        if (last) p.bpart[(part * p.batch + b) * p.dim + d] = accX;
+    }
+}
+
+// Sub-parts of parts 1 .. parts-1 of the sequence (above): each lane (channel, state) runs the
+// reverse adjoint recurrence over its sub-part's steps from zero, lam -> a lam + a gp C (dt, gp and a computed
+// as in the main kernel; one FMA per step on the dependent chain), and writes the contribution lam
+// and the sub-part's decay product exp(A * sum of its dt), capped at FLT_MAX (an overflowing product
+// times a zero adjoint must stay zero, as in the sequential recurrence). A workgroup is one wave
+// (4 channels of one batch) that stages the segment's C in its own LDS, one segment ahead: no
+// workgroup barrier (a wave's LDS accesses are performed in order).
+template <typename T, bool SOFTPLUS, bool HAS_Z>
+__global__ __launch_bounds__(64) void scan_bwd_ls_carry_kernel(BlsParams p) {
+    __shared__ __align__(16) float s_c[2][16 * kBlRowP];  // [buffer][state][step]
+
+    const int lane = threadIdx.x & 63;
+    const int64_t cg = (p.dim + 3) / 4;  // 4-channel groups
+    const int64_t bg = p.batch * cg;
+    const int64_t g0 = p.subs / p.parts;  // sub-parts to a part; part 0's need none
+    const int64_t sub = g0 + blockIdx.x / bg;
+    const int64_t b = (blockIdx.x - (sub - g0) * bg) / cg;
+    const int64_t d0 = (blockIdx.x - (sub - g0) * bg - b * cg) * 4;
+    const int c = lane >> 4, n = lane & 15;
+    const bool valid = d0 + c < p.dim;
+    const int64_t d = valid ? d0 + c : p.dim - 1;
+    const int64_t L = p.len;
+    const int64_t NS = p.N, n0 = p.n0;
+    // segments kbeg .. kend-1 within the part (an empty sub-part: contribution 0, product 1)
+    const int64_t pbeg = (sub / g0) * p.spp;
+    const int64_t pend = pbeg + p.spp < p.nseg ? pbeg + p.spp : p.nseg;
+    const int64_t kbeg = pbeg + (sub % g0) * p.sspp;
+    const int64_t kend = kbeg + p.sspp < pend ? kbeg + p.sspp : pend;
+
+    const float a2 = p.A[d * NS + n0 + n] * kLog2e;
+    const float bias = p.bias ? p.bias[d] : 0.0f;
+
+    constexpr uint32_t es = sizeof(T);
+    const int64_t dl = d0 + 3 < p.dim ? d0 + 3 : p.dim - 1;
+    const uint32_t dr = (uint32_t)(d - d0);
+    const int64_t row0 = b * p.dim + d0, nrows = dl - d0 + 1;
+    auto rows_rsrc = [&](const void* base, int64_t e) __attribute__((always_inline)) {
+        char* p0 = const_cast<char*>(static_cast<const char*>(base)) + row0 * L * e;
+        return __builtin_amdgcn_make_buffer_rsrc(p0, 0, (int)(nrows * L * e), kLsWord3);
+    };
+    const __amdgpu_buffer_rsrc_t xr = rows_rsrc(p.delta, es);
+    const __amdgpu_buffer_rsrc_t zr = HAS_Z ? rows_rsrc(p.z, es) : xr;
+    const __amdgpu_buffer_rsrc_t gr = rows_rsrc(p.dy, 4);
+    const uint32_t oi = (dr * (uint32_t)L + n) * es, of = (dr * (uint32_t)L + n) * 4u;
+    // C staging: lane l stages steps 4 (l % 4) .. + 3 of state row l / 4 (past len: the next
+    // row's values or 0, at steps whose dt and gp are zero)
+    const int sn = lane >> 2, st = (lane & 3) * 4;
+    const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(p.C)) + (b * NS + n0) * L * es, 0, (int)(16 * L * es), kLsWord3);
+    const uint32_t oc = (uint32_t)(sn * L + st) * es;
+    auto load_el = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff) __attribute__((always_inline)) {
+        if constexpr (sizeof(T) == 2)
+            return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, (int)soff, 0);
+        else
+            return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, (int)soff, 0);
+    };
+    auto widen = [](uint32_t v) __attribute__((always_inline)) {
+        return __uint_as_float(sizeof(T) == 2 ? v << 16 : v);
+    };
+
+    struct Raw {
+        uint32_t x, z, g, c[4];
+    };
+    auto fetch = [&](int64_t k, Raw& w) __attribute__((always_inline)) {
+        const uint32_t so = (uint32_t)(k * 16) * es, s4 = (uint32_t)(k * 64);
+        w.x = load_el(xr, oi, so);
+        w.z = HAS_Z ? load_el(zr, oi, so) : 0u;
+        w.g = __builtin_amdgcn_raw_buffer_load_b32(gr, (int)of, (int)s4, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w.c[j] = load_el(cr, oc + j * es, so);
+    };
+    auto stage = [&](const Raw& w, int buf) __attribute__((always_inline)) {
+        *reinterpret_cast<float4*>(&s_c[buf][sn * kBlRowP + st]) =
+            float4{widen(w.c[0]), widen(w.c[1]), widen(w.c[2]), widen(w.c[3])};
+    };
+    // dt and gp of this lane's step of segment k, as the main kernel computes them
+    auto factors = [&](const Raw& w, int64_t k, float& dt, float& gp) __attribute__((always_inline)) {
+        const bool live = k * 16 + n < L;
+        const float xb = widen(w.x) + bias;
+        const float x = live ? xb : -__builtin_inff();
+        dt = SOFTPLUS ? softplus_f(x) : hw_exp2(x * kLog2e);
+        const float gy = (live && valid) ? __uint_as_float(w.g) : 0.0f;
+        if constexpr (HAS_Z) {
+            const float zz = widen(w.z);
+            gp = gy * zz * hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
+        } else {
+            gp = gy;
+        }
+    };
+
+    Raw raw;
+    fetch(kend - 1, raw);
+    stage(raw, 0);
+    float dt, gp;
+    factors(raw, kend - 1, dt, gp);
+    float lam = 0.0f, sdt = 0.0f;  // sdt: this lane's steps' dt summed (its row sums the channel's)
+    int buf = 0;
+    for (int64_t k = kend - 1; k >= kbeg; --k) {
+        const int64_t kp = k > kbeg ? k - 1 : kbeg;
+        fetch(kp, raw);
+        __builtin_amdgcn_wave_barrier();
+        float Cv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 vc = *reinterpret_cast<const float4*>(&s_c[buf][n * kBlRowP + 4 * q]);
+            Cv[4 * q] = vc.x, Cv[4 * q + 1] = vc.y, Cv[4 * q + 2] = vc.z, Cv[4 * q + 3] = vc.w;
+        }
+        sdt += dt;
+        bl_for<0, 16>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int j = 15 - decltype(ic)::value;
+            const float a = hw_exp2(row_bcast<j>(dt) * a2);
+            lam = __builtin_fmaf(a, lam, a * (row_bcast<j>(gp) * Cv[j]));
+        });
+        // the next segment's C into the other buffer (this wave's reads of it are done: in order)
+        __builtin_amdgcn_wave_barrier();
+        stage(raw, buf ^ 1);
+        factors(raw, kp, dt, gp);
+        buf ^= 1;
+    }
+    // the channel's sum of dt over the part: the row's 16 lanes
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) sdt += __shfl_xor(sdt, off, 64);
+    if (valid) {
+        const int64_t pstride = p.batch * p.dim * NS;
+        const int64_t i = (sub - 1) * pstride + (b * p.dim + d) * NS + n0 + n;
+        p.carry[i] = lam;
+        p.carry[(p.subs - 1) * pstride + i] = __builtin_fminf(hw_exp2(a2 * sdt), 3.4028234663852886e38f);
     }
 }
 
@@ -406,9 +561,19 @@ void scan_bwd_ls_kernel(BlsParams p) {
 template <typename T, bool SP, bool HZ>
 int launch_bwd_ls_cfg(const BlsParams& q, hipStream_t stream) {
     void* args[] = {const_cast<BlsParams*>(&q)};
+    if (q.parts > 1) {
+        // the adjoint contribution and decay product of every sub-part after part 0, before the
+        // parts run
+        const void* cf = reinterpret_cast<const void*>(&scan_bwd_ls_carry_kernel<T, SP, HZ>);
+        const int64_t nsub = q.subs - q.subs / q.parts;
+        if (hipLaunchKernel(cf, dim3((unsigned)(nsub * q.batch * ((q.dim + 3) / 4))), dim3(64), args, 0, stream) !=
+            hipSuccess)
+            return MAMBA_SCAN_ERR_LAUNCH;
+    }
     const void* fn = q.N > 16 ? reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ, true>)
                               : reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ, false>);
-    return hipLaunchKernel(fn, dim3((unsigned)(q.batch * q.groups)), dim3(64 * kBlsW), args, 0, stream) == hipSuccess
+    return hipLaunchKernel(fn, dim3((unsigned)(q.parts * q.batch * q.groups)), dim3(64 * kBlsW), args, 0, stream) ==
+                   hipSuccess
                ? MAMBA_SCAN_OK
                : MAMBA_SCAN_ERR_LAUNCH;
 }
@@ -475,6 +640,11 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
     q.apart = reinterpret_cast<float*>(ws + l.off_apart);
     q.dpart = reinterpret_cast<float*>(ws + l.off_dpart);
     q.bpart = reinterpret_cast<float*>(ws + l.off_bpart);
+    q.carry = reinterpret_cast<float*>(ws + l.off_carry);
+    q.parts = l.parts;
+    q.spp = l.spp;
+    q.subs = l.subs;
+    q.sspp = l.sspp;
     q.batch = s.batch;
     q.dim = s.dim;
     q.len = L;
@@ -508,6 +678,7 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
     r.dstate = N;
     r.lp = l.lp;
     r.groups = l.groups;
+    r.parts = l.parts;
     return launch_bwd_reduce_any(r, stream);
 }
 

@@ -114,7 +114,11 @@ def test_backward_edge_cases(idx):
 
 # The lane-per-state kernel forced: ragged lengths (segments of 16 steps), channel counts that
 # leave workgroups (16 channels) and waves (4) partly empty, every optional input on and off; 32
-# and 64 states (blocks of 16 carried through du, ddelta, dz) with and without the gate
+# and 64 states (blocks of 16 carried through du, ddelta, dz) with and without the gate; few
+# channels over long sequences, which split the segments into parts of at least 32 segments and
+# 4 pre-pass sub-parts each (63 at (1, 4, 16, 32770), whose last part is 3 segments: one short and
+# three empty sub-parts; 5 at (1, 8, 16, 3000), 4 at (2, 20, 32, 2047), 2 at (1, 3, 64, 1500)),
+# with and without dlast
 EDGE_LANES = [
     # (batch, dim, N, L, dtype, flags)
     (1, 1, 16, 1, "f32", {}),
@@ -133,6 +137,10 @@ EDGE_LANES = [
     (1, 130, 64, 70, "bf16", {"h0": True}),
     (2, 20, 64, 33, "f32", {"softplus": False, "dlast": False}),
     (1, 50, 64, 300, "bf16", {"D": False, "bias": False, "a_kind": "rand"}),
+    (1, 8, 16, 3000, "f32", {"h0": True}),
+    (2, 20, 32, 2047, "bf16", {"a_kind": "rand", "dlast": False}),
+    (1, 3, 64, 1500, "f32", {"softplus": False}),
+    (1, 4, 16, 32770, "f32", {"dlast": False}),
 ]
 
 
@@ -146,16 +154,18 @@ def test_lane_backward_edge_cases(idx):
            with_dlast=fl.get("dlast", True), seed=idx, kernel="lanes")
 
 
-@pytest.mark.parametrize("kernel", ["tiled", "lanes"])
-def test_state_blocks_are_independent(kernel):
+@pytest.mark.parametrize("kernel,shape", [("tiled", (2, 96, 90)), ("lanes", (2, 96, 90)), ("lanes", (1, 20, 3000))])
+def test_state_blocks_are_independent(kernel, shape):
     """dB, dC, dA and dh0 of a state depend on no other state, so with 32 states the first 16
     states' gradients are the bits of a 16-state run on those states alone (the same first block
-    of 16 states, with either kernel)."""
-    x = gu.case(73, 2, 96, 32, 90, dtype="bf16")
+    of 16 states, with either kernel; (1, 20, 3000) splits the sequence into 5 parts, by a rule
+    that does not depend on the state count)."""
+    batch, dim, L = shape
+    x = gu.case(73, batch, dim, 32, L, dtype="bf16")
     rng = np.random.default_rng(4)
-    dy = rng.standard_normal((2, 96, 90)).astype(np.float32)
-    dlast = rng.standard_normal((2, 96, 32)).astype(np.float32)
-    h0 = rng.standard_normal((2, 96, 32)).astype(np.float32)
+    dy = rng.standard_normal((batch, dim, L)).astype(np.float32)
+    dlast = rng.standard_normal((batch, dim, 32)).astype(np.float32)
+    h0 = rng.standard_normal((batch, dim, 32)).astype(np.float32)
     full = _grads_gpu(x, dy, dlast, True, h0, kernel=kernel)
     half = dict(x, A=np.ascontiguousarray(x["A"][:, :16]), B=np.ascontiguousarray(x["B"][:, :16]),
                 C=np.ascontiguousarray(x["C"][:, :16]))
@@ -225,11 +235,13 @@ def test_large_workload_sampled_channels(wid):
         assert err <= TOL, k
 
 
-@pytest.mark.parametrize("kernel", ["lanes", "tiled"])
-def test_backward_is_deterministic(kernel):
-    x = gu.case(71, 2, 150, 16, 200, dtype="bf16")
+@pytest.mark.parametrize("kernel,shape", [("lanes", (2, 150, 200)), ("tiled", (2, 150, 200)), ("lanes", (1, 30, 2500))])
+def test_backward_is_deterministic(kernel, shape):
+    """Two calls, the same bits ((1, 30, 2500): 4 sequence parts)."""
+    batch, dim, L = shape
+    x = gu.case(71, batch, dim, 16, L, dtype="bf16")
     rng = np.random.default_rng(1)
-    dy = rng.standard_normal((2, 150, 200)).astype(np.float32)
+    dy = rng.standard_normal((batch, dim, L)).astype(np.float32)
     a = _grads_gpu(x, dy, None, True, kernel=kernel)
     b = _grads_gpu(x, dy, None, True, kernel=kernel)
     for k in a:
