@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 9
+#define MAMBA_SCAN_ABI_VERSION 10
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -66,7 +66,9 @@ typedef enum mamba_scan_dtype {
  * h before steps 0, 16, 32, ... of every (b, d) row to the workspace, laid out (batch, dim,
  * ceil(len/16), dstate) fp32 contiguous (mamba_scan_workspace_bytes gives its size with this
  * flag), and mamba_scan_bwd, given them as `checkpoints`, skips recomputing them. The
- * lane-per-state kernels only (dstate 16, 32 or 64, no ZOH_B): MAMBA_SCAN_ERR_UNSUPPORTED
+ * lane-per-state kernels (dstate 16, 32 or 64) and, from ABI 10, the chunked kernel (dstate 16:
+ * the default where it is the default without the flag; its states come from its combine, so they
+ * agree with the sequential recurrence's to rounding); no ZOH_B: MAMBA_SCAN_ERR_UNSUPPORTED
  * otherwise. ABI version 6. */
 #define MAMBA_SCAN_SAVE_CHECKPOINTS (1u << 3)
 /* Kernel selection, for testing and tuning; at most one of these bits (MAMBA_SCAN_ERR_ARGS
@@ -84,8 +86,8 @@ typedef enum mamba_scan_dtype {
 /* Chunked along the sequence (ABI 7): one wave per channel, its four 16-lane rows scan four
  * consecutive 16-step runs of each 64-step chunk and are combined with the associative (a, b)
  * operator of the parallel scan ("手把手用PyTorch实现Mamba的SSM层…" §3.2), the state carried
- * from chunk to chunk in registers. dstate 16, no ZOH_B, no SAVE_CHECKPOINTS; error if it cannot
- * run. Results agree with the sequential kernels to rounding (not bit for bit); a sequence split
+ * from chunk to chunk in registers. dstate 16, no ZOH_B (SAVE_CHECKPOINTS from ABI 10); error if
+ * it cannot run. Results agree with the sequential kernels to rounding (not bit for bit); a sequence split
  * at a multiple of 64 steps and resumed from last_state gives the same bits as one call. */
 #define MAMBA_SCAN_FORCE_CHUNKED (1u << 11)
 /* Short calls (ABI 7): one lane per (channel, state), each step in registers with no LDS staging
@@ -205,8 +207,9 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *    MAMBA_SCAN_ERR_ARGS for both or any other flag):
  *      MAMBA_SCAN_FORCE_LANES: the lane-per-state backward, one lane per (channel, state) as in
  *        the forward lane-per-state kernel, 16-step segments walked in reverse from the states
- *        saved every 16 steps (given, or written first by a forward lane-per-state launch whose
- *        y goes to du); dstate 16, 32 or 64 and row byte offsets within 31 bits
+ *        saved every 16 steps (given, or written first by the forward launch that a call with
+ *        MAMBA_SCAN_SAVE_CHECKPOINTS would make, its y going to du); dstate 16, 32 or 64 and
+ *        row byte offsets within 31 bits
  *        (MAMBA_SCAN_ERR_UNSUPPORTED otherwise). The default wherever it can run.
  *      MAMBA_SCAN_FORCE_TILED: the segment-tiled backward (64 channels per workgroup, at most 2
  *        states per wave), any dstate.

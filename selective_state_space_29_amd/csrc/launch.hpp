@@ -30,6 +30,8 @@ inline bool tiled_can_run_any(const ScanParams& q, bool bf16) {
 inline int launch_ls_any(const ScanParams& q, bool bf16, hipStream_t stream) {
     return bf16 ? launch_ls_bf16(q, stream) : launch_ls_f32(q, stream);
 }
+// the forward that saves the segment states (q.ck), on the kernel a forward call would choose
+int launch_fwd_checkpoints(const ScanParams& q, bool bf16, hipStream_t stream);
 struct BwdReduceParams;
 // the backward: the segment-tiled kernel (any dstate) or the lane-per-state one (16 states), each
 // finished by the fixed-order reduction

@@ -181,7 +181,7 @@ int device_cus() {
 // kernel, whose results do not depend on where a sequence is split.)
 constexpr int64_t kChunkedMinLen = 1024;
 bool prefer_chunked(const ScanParams& q) {
-    if (q.dstate != 16 || q.zoh_b || q.ck || q.len < kChunkedMinLen) return false;
+    if (q.dstate != 16 || q.zoh_b || q.len < kChunkedMinLen) return false;
     const int cus = device_cus();
     if (cus <= 0) return false;
     const int64_t ls_waves = q.batch * ((q.dim + 3) / 4);
@@ -201,10 +201,11 @@ int check_checkpoint_workspace(const mamba_scan_ptrs* p, const mamba_scan_shape*
 // Shared by mamba_scan_fwd and mamba_scan_fwd_kernel so that the query and the launch agree.
 int choose_kernel(const ScanParams& q, uint32_t flags, bool bf16) {
     const int64_t es = bf16 ? 2 : 4;
-    if (q.ck) {  // the saved states come from the lane-per-state kernels only
-        if (flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_CHUNKED |
-                     MAMBA_SCAN_FORCE_STEP))
+    if (q.ck) {  // the saved states come from the lane-per-state and chunked kernels only
+        if (flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_STEP))
             return MAMBA_SCAN_ERR_UNSUPPORTED;
+        if (flags & MAMBA_SCAN_FORCE_CHUNKED) return lp_eligible(q, es) ? MAMBA_SCAN_KERNEL_CHUNKED : MAMBA_SCAN_ERR_UNSUPPORTED;
+        if (!(flags & MAMBA_SCAN_FORCE_LANES) && prefer_chunked(q) && lp_eligible(q, es)) return MAMBA_SCAN_KERNEL_CHUNKED;
         return ls_eligible(q, es) ? MAMBA_SCAN_KERNEL_LANES : MAMBA_SCAN_ERR_UNSUPPORTED;
     }
     if (flags & MAMBA_SCAN_FORCE_STEP) return step_eligible(q) ? MAMBA_SCAN_KERNEL_STEP : MAMBA_SCAN_ERR_UNSUPPORTED;
@@ -223,6 +224,21 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
                    uint32_t flags, void* stream);
 
 }  // namespace
+
+namespace mscan {
+
+// The forward launch that writes the saved states when the backward recomputes them: the kernel
+// that a forward call with SAVE_CHECKPOINTS runs by default (chunked or lane-per-state), so that
+// the backward's states are those bits either way.
+int launch_fwd_checkpoints(const ScanParams& q, bool bf16, hipStream_t stream) {
+    const int k = choose_kernel(q, 0, bf16);
+    if (k == MAMBA_SCAN_KERNEL_CHUNKED) return launch_lp_any(q, bf16, stream);
+    if (k == MAMBA_SCAN_KERNEL_LANES) return launch_ls_any(q, bf16, stream);
+    return k < 0 ? k : MAMBA_SCAN_ERR_UNSUPPORTED;
+}
+
+}  // namespace mscan
+
 
 // The static workspace of mamba_scan_bwd_static: every GPU the library runs on holds its own copy
 // until the process ends. In host code this name is only a handle for hipGetSymbolAddress; the

@@ -587,8 +587,9 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
     float* ck = given ? const_cast<float*>(p->checkpoints) : reinterpret_cast<float*>(ws + l.off_ck);
     const int64_t L = s.len, DL = s.dim * L, N = s.dstate;
     if (!given) {
-        // the state before every segment, written by the forward lane-per-state kernel (the states
-        // a forward call saves, bit for bit); its y goes to du, which the backward overwrites
+        // the state before every segment, written by the forward kernel that a forward call saving
+        // them runs (lane-per-state or chunked: the same bits); its y goes to du, which the
+        // backward overwrites
         ScanParams f{};
         f.u = p->u;
         f.delta = p->delta;
@@ -617,7 +618,7 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
         f.zoh_b = 0;
         f.ck = ck;
         f.ck_nseg = l.nseg;
-        const int rc = launch_ls_any(f, sizeof(T) == 2, stream);
+        const int rc = launch_fwd_checkpoints(f, sizeof(T) == 2, stream);
         if (rc != MAMBA_SCAN_OK) return rc;
     }
     BlsParams q;

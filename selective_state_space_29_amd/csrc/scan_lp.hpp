@@ -21,6 +21,8 @@
 //     broadcast folded into the multiply (as in the sequential lane-per-state kernel); B and C are
 //     staged per chunk in LDS by the workgroup (W channels of one batch) and read with 16-byte
 //     LDS reads; the sum over states goes through the wave's own LDS area, in state order.
+// With CK the state entering every run, which the combine produces anyway, is the state before a
+// 16-step segment: it is stored as the segment's checkpoint (the states saved for the backward).
 // Per element: the sequential kernel's 5 operations (2 broadcast multiplies, exp, FMA, C h) plus
 // the fix pass's FMA; per chunk and lane the row sum of dt, one exp and about 15 operations of
 // combine. It exists for shapes with too few (batch, channel, state) chains to fill the GPU
@@ -43,7 +45,7 @@ constexpr int kLpPRow = 16 * (kLpK + 4) + 16;  // LDS floats per run of the C h 
 // recurrence keeps it zero).
 __device__ __forceinline__ float lp_cap(float a) { return __builtin_fminf(a, 3.4028234663852886e38f); }
 
-template <typename T, int W, bool SOFTPLUS, bool HAS_Z, bool VEC>
+template <typename T, int W, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK>
 __global__ __launch_bounds__(64 * W) void scan_lp_kernel(ScanParams p) {
     __shared__ __align__(16) float s_p[W * 4 * kLpPRow];
     __shared__ __align__(16) float s_bc[2][2][16 * kLpRowP];  // [chunk parity][B|C][state][step]
@@ -78,6 +80,11 @@ __global__ __launch_bounds__(64 * W) void scan_lp_kernel(ScanParams p) {
     const __amdgpu_buffer_rsrc_t yr =
         __builtin_amdgcn_make_buffer_rsrc(p.y + b * p.sy_b + d * p.sy_d, 0, (int)(L * 4), kLsWord3);
     const uint32_t st_l = (uint32_t)(r * kLpK + n);  // this lane's step within a chunk
+    // saved states (CK): (segment, state) of this channel, segment 4 k + r entered by run r of
+    // chunk k; past the last segment the store gets an offset past the range and is dropped
+    const __amdgpu_buffer_rsrc_t ckr = __builtin_amdgcn_make_buffer_rsrc(
+        CK ? p.ck + (b * p.dim + d) * p.ck_nseg * 16 : p.y, 0, CK ? (int)(p.ck_nseg * 16 * 4) : 0, kLsWord3);
+    const uint32_t ock = valid ? (uint32_t)(r * 16 + n) * 4u : kLsDropBase;
 
     auto load_el = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff) __attribute__((always_inline)) {
         if constexpr (sizeof(T) == 2)
@@ -243,6 +250,8 @@ __global__ __launch_bounds__(64 * W) void scan_lp_kernel(ScanParams p) {
             // the state entering run r: runs 0 .. r-1 applied to the carry
             const float h1 = row2 ? __builtin_fmaf(LA, carry, Lb) : carry;
             const float hin = row1 ? __builtin_fmaf(loA, h1, lob) : h1;
+            if constexpr (CK)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hin), ckr, (int)ock, (int)(t0 * 4u), 0);
             // the carry into the next chunk: all 4 runs applied to it
             const float tA = lp_cap(LA * HA), tb = __builtin_fmaf(HA, Lb, Hb);
             carry = __builtin_fmaf(tA, carry, tb);
@@ -289,12 +298,13 @@ __global__ __launch_bounds__(64 * W) void scan_lp_kernel(ScanParams p) {
 
 constexpr int kLpW = 4;  // channels (waves) per workgroup
 
-// 16 states, Euler input term, and byte offsets within a row (u, delta, z, y) and within a
-// batch's B / C that fit 31 bits.
+// 16 states, Euler input term, and byte offsets within a row (u, delta, z, y), within a batch's
+// B / C and within a channel's saved states that fit 31 bits.
 inline bool lp_eligible(const ScanParams& q, int64_t es) {
-    if (q.dstate != 16 || q.zoh_b || q.ck) return false;
+    if (q.dstate != 16 || q.zoh_b) return false;
     const int64_t lim = (int64_t)1 << 31;
     if (q.len * 4 >= lim) return false;
+    if (q.ck && q.ck_nseg * 16 * 4 >= lim) return false;
     if ((15 * q.sB_n + q.len) * es >= lim || (15 * q.sC_n + q.len) * es >= lim) return false;
     if (q.batch * ((q.dim + kLpW - 1) / kLpW) > 0x7fffffff) return false;
     return true;
@@ -304,8 +314,10 @@ template <typename T, bool SP, bool HZ, bool VEC>
 int launch_lp_cfg(const ScanParams& q, hipStream_t stream) {
     void* args[] = {const_cast<ScanParams*>(&q)};
     const int64_t groups = q.batch * ((q.dim + kLpW - 1) / kLpW);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&scan_lp_kernel<T, kLpW, SP, HZ, VEC>),
-                           dim3((unsigned)groups), dim3(64 * kLpW), args, 0, stream) == hipSuccess
+    // saving the segment states is a separate instantiation: the plain forward issues no stores for it
+    const void* fn = q.ck ? reinterpret_cast<const void*>(&scan_lp_kernel<T, kLpW, SP, HZ, VEC, true>)
+                          : reinterpret_cast<const void*>(&scan_lp_kernel<T, kLpW, SP, HZ, VEC, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * kLpW), args, 0, stream) == hipSuccess
                ? MAMBA_SCAN_OK
                : MAMBA_SCAN_ERR_LAUNCH;
 }

@@ -241,7 +241,7 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     states) or "step" (short calls such as decode, at most 64 steps; 16 states).
     ``checkpoints_out``: a contiguous fp32 (batch, dim, ceil(L/16), N) tensor that receives the
     state before every 16-step segment, for ``selective_scan_bwd(checkpoints=...)``
-    (lane-per-state kernels only).
+    (lane-per-state and chunked kernels only).
     """
     lib = load_library()
     ptrs, shape, st, dtype, flags, y, ls, ws, keep = _fwd_args(
@@ -385,8 +385,8 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
 class SelectiveScan(torch.autograd.Function):
     """y (and last_state) = selective_scan(...) with a backward pass through ``mamba_scan_bwd``.
 
-    The inputs are saved, and, where the lane-per-state forward runs (16, 32 or 64 states), the
-    state before every 16-step segment; the backward recomputes the states inside each segment
+    The inputs are saved, and, where the lane-per-state or chunked forward runs (16, 32 or 64
+    states), the state before every 16-step segment; the backward recomputes the states inside each segment
     from there ("手把手用PyTorch实现Mamba的SSM层…" §4.2), or from the start without them.
     Gradients come back in each input's dtype.
     """

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 9
+    assert scan.load_library().mamba_scan_abi_version() == 10
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -115,7 +115,6 @@ CASES = [
     ("chunked_forced_32_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_CHUNKED),
                                             setattr(c["shape"], "dstate", 32)), -8),
     ("chunked_forced_zoh", _flags(scan.DELTA_SOFTPLUS | scan.FORCE_CHUNKED | scan.ZOH_B), -8),
-    ("checkpoints_with_chunked", lambda c: _ck_ws(c, 1 << 20, extra=scan.FORCE_CHUNKED), -8),
     # the short-call kernel: 16 states, Euler, at most 64 steps, no saved states
     ("step_forced_32_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_STEP),
                                          setattr(c["shape"], "dstate", 32)), -8),
@@ -167,6 +166,24 @@ def test_kernel_query(extra, dstate, expect):
     order); it launches nothing, so it answers without a GPU too."""
     def m(c):
         c["flags"] = scan.DELTA_SOFTPLUS | extra
+        c["shape"].dstate = dstate
+        for k in ("B", "C"):
+            setattr(c["st"], k, (ctypes.c_int64 * 3)(dstate * 40, 40, 1))
+        for k in ("h0",):
+            setattr(c["st"], k, (ctypes.c_int64 * 3)(3 * dstate, dstate, 1))
+        c["st"].A = (ctypes.c_int64 * 2)(dstate, 1)
+    assert fake_call(m, query=True) == expect
+
+
+@pytest.mark.parametrize("extra,dstate,expect", [
+    (scan.FORCE_CHUNKED, 16, 4), (scan.FORCE_LANES, 16, 3), (0, 32, 3), (scan.FORCE_CHUNKED, 32, -8),
+    (scan.FORCE_STEP, 16, -8), (scan.ZOH_B | scan.FORCE_CHUNKED, 16, -8)])
+def test_kernel_query_with_checkpoints(extra, dstate, expect):
+    """Saving the segment states: the chunked kernel (16 states) or the lane-per-state one (ABI 10);
+    the default between them depends on the device's size, so only forced choices and 32 states
+    are fixed here."""
+    def m(c):
+        _ck_ws(c, 1 << 24, extra=extra)
         c["shape"].dstate = dstate
         for k in ("B", "C"):
             setattr(c["st"], k, (ctypes.c_int64 * 3)(dstate * 40, 40, 1))

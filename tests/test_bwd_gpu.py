@@ -154,12 +154,14 @@ def test_lane_backward_edge_cases(idx):
            with_dlast=fl.get("dlast", True), seed=idx, kernel="lanes")
 
 
-@pytest.mark.parametrize("kernel,shape", [("tiled", (2, 96, 90)), ("lanes", (2, 96, 90)), ("lanes", (1, 20, 3000))])
+@pytest.mark.parametrize("kernel,shape", [("tiled", (2, 96, 90)), ("lanes", (2, 96, 90)), ("lanes", (4, 2048, 1024))])
 def test_state_blocks_are_independent(kernel, shape):
     """dB, dC, dA and dh0 of a state depend on no other state, so with 32 states the first 16
     states' gradients are the bits of a 16-state run on those states alone (the same first block
-    of 16 states, with either kernel; (1, 20, 3000) splits the sequence into 5 parts, by a rule
-    that does not depend on the state count)."""
+    of 16 states, with either kernel; (4, 2048, 1024) splits the sequence into 2 parts, by a rule
+    that does not depend on the state count, and recomputes the states with the lane-per-state
+    forward at both state counts: a shape whose 16-state forward is the chunked kernel would not
+    give the 32-state run's bits)."""
     batch, dim, L = shape
     x = gu.case(73, batch, dim, 32, L, dtype="bf16")
     rng = np.random.default_rng(4)

@@ -3,7 +3,8 @@ starts from them instead of recomputing them ("手把手用PyTorch实现Mamba的
 ways: store the states, or recompute them).
 
   * checkpoint k is the state before step 16 k: the oracle's last state of the first 16 k steps
-    (h0 for k = 0), to the forward bar, and the GPU's own last state of that prefix, bit for bit;
+    (h0 for k = 0), to the forward bar, and the GPU's own last state of that prefix, bit for bit
+    (the chunked kernel, whose states come from its combine: at every 64-step chunk boundary);
   * the backward given them matches the fp64 backward oracle to the backward bars (1e-4 for fp32
     inputs, 2e-3 for bf16 inputs), and the backward that recomputes them to 1e-5;
   * the autograd function saves them where the lane-per-state forward runs and falls back to
@@ -21,42 +22,62 @@ from selective_state_space_29_amd import scan
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (batch, dim, N, L, dtype, h0)
-    (2, 12, 16, 70, "bf16", False),   # ragged: last segment of 6 steps, last 32-step chunk of 6
-    (1, 5, 16, 64, "f32", True),      # exact chunks, initial state
-    (2, 9, 32, 47, "bf16", True),
-    (1, 4, 64, 33, "f32", False),
-    (1, 3, 16, 1, "bf16", False),     # one step: one checkpoint, the initial state
+    # (batch, dim, N, L, dtype, h0, kernel)
+    (2, 12, 16, 70, "bf16", False, None),   # ragged: last segment of 6 steps, last 32-step chunk of 6
+    (1, 5, 16, 64, "f32", True, None),      # exact chunks, initial state
+    (2, 9, 32, 47, "bf16", True, None),
+    (1, 4, 64, 33, "f32", False, None),
+    (1, 3, 16, 1, "bf16", False, None),     # one step: one checkpoint, the initial state
+    # the chunked kernel: the default for few rows of >= 1024 steps, forced below that; ragged
+    # last chunks (runs past len, segments past the last one), an exact chunk, h0
+    (1, 8, 16, 1100, "bf16", False, None),
+    (2, 5, 16, 200, "f32", True, "chunked"),
+    (1, 3, 16, 64, "bf16", False, "chunked"),
+    (1, 6, 16, 77, "f32", False, "chunked"),
 ]
-IDS = [f"b{c[0]}d{c[1]}n{c[2]}l{c[3]}{c[4]}{'h0' if c[5] else ''}" for c in CASES]
+IDS = [f"b{c[0]}d{c[1]}n{c[2]}l{c[3]}{c[4]}{'h0' if c[5] else ''}{c[6] or ''}" for c in CASES]
 
 
 def _dev(x):
     return {k: gu.to_dev(v) if isinstance(v, np.ndarray) else v for k, v in x.items()}
 
 
-def _forward_with_checkpoints(x, h0):
+def _forward_with_checkpoints(x, h0, kernel=None):
     g = _dev(x)
     batch, dim, L = x["u"].shape
     N = x["A"].shape[1]
     ck = torch.full(scan.checkpoint_shape(batch, dim, L, N), float("nan"), dtype=torch.float32, device="cuda:0")
     y, ls = scan.selective_scan_fn(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
                                    delta_bias=g["delta_bias"], delta_softplus=True, return_last_state=True,
-                                   h0=None if h0 is None else gu.to_dev(h0), checkpoints_out=ck)
+                                   h0=None if h0 is None else gu.to_dev(h0), checkpoints_out=ck, kernel=kernel)
     torch.cuda.synchronize()
     return y.cpu().numpy(), ls.cpu().numpy(), ck
 
 
+def _kernel_that_ran(x, h0, kernel):
+    """The forward kernel of a call with saved states (the library's own answer)."""
+    g = _dev(x)
+    batch, dim, L = x["u"].shape
+    N = x["A"].shape[1]
+    ck = torch.empty(scan.checkpoint_shape(batch, dim, L, N), dtype=torch.float32, device="cuda:0")
+    return scan.forward_kernel(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                               delta_bias=g["delta_bias"], delta_softplus=True, return_last_state=True,
+                               h0=None if h0 is None else gu.to_dev(h0), kernel=kernel, checkpoints_out=ck)
+
+
 @pytest.mark.parametrize("idx", range(len(CASES)), ids=IDS)
 def test_checkpoints_are_the_prefix_states(idx):
-    batch, dim, N, L, dtype, with_h0 = CASES[idx]
+    batch, dim, N, L, dtype, with_h0, kernel = CASES[idx]
     print(f"checkpoint case {CASES[idx]}", flush=True)
     x = gu.case(8000 + idx, batch, dim, N, L, dtype=dtype)
     h0 = np.random.default_rng(idx).standard_normal((batch, dim, N)).astype(np.float32) if with_h0 else None
-    y, ls, ck = _forward_with_checkpoints(x, h0)
+    ran = _kernel_that_ran(x, h0, kernel)
+    print(f"   kernel: {ran}", flush=True)
+    assert ran in ("lanes", "chunked")
+    y, ls, ck = _forward_with_checkpoints(x, h0, kernel)
     ck = ck.cpu().numpy()
-    # the outputs are those of the same (lane-per-state) kernel without checkpoints, bit for bit
-    y2, ls2 = gu.gpu_scan(x, h0=h0, kernel="lanes")
+    # the outputs are those of the same kernel without checkpoints, bit for bit
+    y2, ls2 = gu.gpu_scan(x, h0=h0, kernel=ran)
     assert np.array_equal(y, y2) and np.array_equal(ls, ls2)
     tol = gu.FP32_TOL if dtype == "f32" else gu.BF16_TOL
     start = np.zeros((batch, dim, N)) if h0 is None else h0
@@ -67,20 +88,21 @@ def test_checkpoints_are_the_prefix_states(idx):
         _, lr = gu.oracle_scan(pre, h0=h0)
         err = gu.rel_err(ck[:, :, k, :], lr)
         assert err <= tol, f"checkpoint {k}: {err:.3g}"
-        _, lg = gu.gpu_scan(pre, h0=h0, kernel="lanes")
-        assert np.array_equal(ck[:, :, k, :], lg), f"checkpoint {k} differs from the prefix scan"
+        if ran == "lanes" or k % 4 == 0:
+            _, lg = gu.gpu_scan(pre, h0=h0, kernel=ran)
+            assert np.array_equal(ck[:, :, k, :], lg), f"checkpoint {k} differs from the prefix scan"
 
 
 @pytest.mark.parametrize("idx", range(len(CASES)), ids=IDS)
 def test_backward_from_checkpoints(idx):
-    batch, dim, N, L, dtype, with_h0 = CASES[idx]
+    batch, dim, N, L, dtype, with_h0, kernel = CASES[idx]
     print(f"checkpoint backward case {CASES[idx]}", flush=True)
     x = gu.case(8100 + idx, batch, dim, N, L, dtype=dtype)
     rng = np.random.default_rng(100 + idx)
     h0 = rng.standard_normal((batch, dim, N)).astype(np.float32) if with_h0 else None
     dy = rng.standard_normal((batch, dim, L)).astype(np.float32)
     dlast = rng.standard_normal((batch, dim, N)).astype(np.float32)
-    _, _, ck = _forward_with_checkpoints(x, h0)
+    _, _, ck = _forward_with_checkpoints(x, h0, kernel)
     g = _dev(x)
     kw = dict(D=g["D"], z=g["z"], delta_bias=g["delta_bias"], delta_softplus=True,
               h0=None if h0 is None else gu.to_dev(h0), dlast_state=gu.to_dev(dlast), want_dh0=True)
