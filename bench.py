@@ -140,11 +140,11 @@ def copy_calibration(mb, steps, warmup):
 def resolved_kernel(w, kernel, zoh=False, cus=256):
     """The forward kernel the library's default picks for this workload on a GPU with `cus`
     compute units (the bench itself asks the library, scan.forward_kernel): the chunked kernel
-    for 16 states, Euler B, >= 1024 steps and fewer than 2 lane-per-state waves per SIMD; else
-    the lane-per-state kernels for 16, 32 or 64 states; else the tiled one."""
+    for 16 states, >= 1024 steps and fewer than 2 lane-per-state waves per SIMD; else the
+    lane-per-state kernels for 16, 32 or 64 states; else the tiled one."""
     if kernel not in ("auto", None):
         return kernel
-    if w.dstate == 16 and not zoh and w.seqlen >= 1024 and w.batch * ((w.dim + 3) // 4) < 8 * cus:
+    if w.dstate == 16 and w.seqlen >= 1024 and w.batch * ((w.dim + 3) // 4) < 8 * cus:
         return "chunked"
     return "lanes" if w.dstate in (16, 32, 64) else "tiled"
 

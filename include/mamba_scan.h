@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 10
+#define MAMBA_SCAN_ABI_VERSION 11
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -60,7 +60,8 @@ typedef enum mamba_scan_dtype {
 /* B discretised by zero-order hold: the input term becomes (exp(dt*A[d,n]) - 1) / A[d,n] * B * u
  * (dt * B * u where A[d,n] = 0) instead of dt * B * u. "手把手用PyTorch实现Mamba的SSM层…" §2.1:
  * B_d = A^-1 (e^{A dt} - I) B, for a diagonal A. Forward only (mamba_scan_bwd rejects it). Run by
- * the lane-per-state kernels at dstate 16, 32 and 64 (ABI 9), else by the tiled or generic one. */
+ * the lane-per-state kernels at dstate 16, 32 and 64 (ABI 9) and the chunked kernel (ABI 11), else
+ * by the tiled or generic one. */
 #define MAMBA_SCAN_ZOH_B (1u << 2)
 /* Save the state before every 16-step segment, for the backward pass: the forward writes
  * h before steps 0, 16, 32, ... of every (b, d) row to the workspace, laid out (batch, dim,
@@ -86,8 +87,8 @@ typedef enum mamba_scan_dtype {
 /* Chunked along the sequence (ABI 7): one wave per channel, its four 16-lane rows scan four
  * consecutive 16-step runs of each 64-step chunk and are combined with the associative (a, b)
  * operator of the parallel scan ("手把手用PyTorch实现Mamba的SSM层…" §3.2), the state carried
- * from chunk to chunk in registers. dstate 16, no ZOH_B (SAVE_CHECKPOINTS from ABI 10); error if
- * it cannot run. Results agree with the sequential kernels to rounding (not bit for bit); a sequence split
+ * from chunk to chunk in registers. dstate 16; SAVE_CHECKPOINTS from ABI 10, ZOH_B from ABI 11,
+ * not both; error if it cannot run. Results agree with the sequential kernels to rounding (not bit for bit); a sequence split
  * at a multiple of 64 steps and resumed from last_state gives the same bits as one call. */
 #define MAMBA_SCAN_FORCE_CHUNKED (1u << 11)
 /* Short calls (ABI 7): one lane per (channel, state), each step in registers with no LDS staging

@@ -181,7 +181,7 @@ int device_cus() {
 // kernel, whose results do not depend on where a sequence is split.)
 constexpr int64_t kChunkedMinLen = 1024;
 bool prefer_chunked(const ScanParams& q) {
-    if (q.dstate != 16 || q.zoh_b || q.len < kChunkedMinLen) return false;
+    if (q.dstate != 16 || q.len < kChunkedMinLen) return false;
     const int cus = device_cus();
     if (cus <= 0) return false;
     const int64_t ls_waves = q.batch * ((q.dim + 3) / 4);

@@ -45,7 +45,9 @@ constexpr int kLpPRow = 16 * (kLpK + 4) + 16;  // LDS floats per run of the C h 
 // recurrence keeps it zero).
 __device__ __forceinline__ float lp_cap(float a) { return __builtin_fminf(a, 3.4028234663852886e38f); }
 
-template <typename T, int W, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK>
+// ZOH: B discretised by zero-order hold (the input term's coefficient of B from zoh_coef2_f, times
+// u, times B), in the local pass where the decays are formed.
+template <typename T, int W, bool SOFTPLUS, bool HAS_Z, bool VEC, bool CK, bool ZOH>
 __global__ __launch_bounds__(64 * W) void scan_lp_kernel(ScanParams p) {
     __shared__ __align__(16) float s_p[W * 4 * kLpPRow];
     __shared__ __align__(16) float s_bc[2][2][16 * kLpRowP];  // [chunk parity][B|C][state][step]
@@ -61,7 +63,9 @@ __global__ __launch_bounds__(64 * W) void scan_lp_kernel(ScanParams p) {
     const int64_t d = valid ? d0 + wave : p.dim - 1;
     const int64_t L = p.len;
 
-    const float a2 = p.A[d * p.sA_d + n] * kLog2e;
+    const float an = p.A[d * p.sA_d + n];
+    const float a2 = an * kLog2e;
+    const float ia = an != 0.0f ? 1.0f / an : 0.0f;  // zero-order hold only
     float carry = p.h0 ? p.h0[b * p.sh0_b + d * p.sh0_d + n] : 0.0f;
     const float bias = p.bias ? p.bias[d * p.sbias] : 0.0f;
     const float Dv = p.D ? p.D[d * p.sD] : 0.0f;  // no skip term: D = 0
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(64 * W) void scan_lp_kernel(ScanParams p) {
         const float xb = widen(w.x) + bias;
         dt = SOFTPLUS ? softplus_f(xb) : hw_exp2(xb * kLog2e);
         uv = widen(w.u);
-        dtu = dt * uv;
+        dtu = ZOH ? uv : dt * uv;  // u with the zero-order hold, whose coefficient replaces dt
         gz = HAS_Z ? silu_f(widen(w.z)) : 1.0f;
     };
 
@@ -218,9 +222,15 @@ __global__ __launch_bounds__(64 * W) void scan_lp_kernel(ScanParams p) {
                 Bv[4 * q] = v.x, Bv[4 * q + 1] = v.y, Bv[4 * q + 2] = v.z, Bv[4 * q + 3] = v.w;
             }
             float hl = 0.0f;
-#define MSCAN_LP_LOCAL(S)                                          \
-    dA[S] = hw_exp2(row_bcast<S>(dt) * a2);                        \
-    bu[S] = row_bcast<S>(dtu) * Bv[S];                             \
+#define MSCAN_LP_LOCAL(S)                                                                   \
+    if constexpr (ZOH) {                                                                    \
+        const float dtb = row_bcast<S>(dt), x2 = dtb * a2;                                  \
+        dA[S] = hw_exp2(x2);                                                                \
+        bu[S] = zoh_coef2_f(dtb, x2, dA[S], ia) * row_bcast<S>(dtu) * Bv[S];                \
+    } else {                                                                                \
+        dA[S] = hw_exp2(row_bcast<S>(dt) * a2);                                             \
+        bu[S] = row_bcast<S>(dtu) * Bv[S];                                                  \
+    }                                                                                       \
     hl = (S) == 0 ? bu[S] : __builtin_fmaf(dA[S], hl, bu[S]);
             MSCAN_LP_LOCAL(0) MSCAN_LP_LOCAL(1) MSCAN_LP_LOCAL(2) MSCAN_LP_LOCAL(3)
             MSCAN_LP_LOCAL(4) MSCAN_LP_LOCAL(5) MSCAN_LP_LOCAL(6) MSCAN_LP_LOCAL(7)
@@ -298,10 +308,11 @@ __global__ __launch_bounds__(64 * W) void scan_lp_kernel(ScanParams p) {
 
 constexpr int kLpW = 4;  // channels (waves) per workgroup
 
-// 16 states, Euler input term, and byte offsets within a row (u, delta, z, y), within a batch's
-// B / C and within a channel's saved states that fit 31 bits.
+// 16 states (either input term; the zero-order hold without saved states, which only the Euler
+// backward reads), and byte offsets within a row (u, delta, z, y), within a batch's B / C and
+// within a channel's saved states that fit 31 bits.
 inline bool lp_eligible(const ScanParams& q, int64_t es) {
-    if (q.dstate != 16 || q.zoh_b) return false;
+    if (q.dstate != 16 || (q.zoh_b && q.ck)) return false;
     const int64_t lim = (int64_t)1 << 31;
     if (q.len * 4 >= lim) return false;
     if (q.ck && q.ck_nseg * 16 * 4 >= lim) return false;
@@ -314,9 +325,11 @@ template <typename T, bool SP, bool HZ, bool VEC>
 int launch_lp_cfg(const ScanParams& q, hipStream_t stream) {
     void* args[] = {const_cast<ScanParams*>(&q)};
     const int64_t groups = q.batch * ((q.dim + kLpW - 1) / kLpW);
-    // saving the segment states is a separate instantiation: the plain forward issues no stores for it
-    const void* fn = q.ck ? reinterpret_cast<const void*>(&scan_lp_kernel<T, kLpW, SP, HZ, VEC, true>)
-                          : reinterpret_cast<const void*>(&scan_lp_kernel<T, kLpW, SP, HZ, VEC, false>);
+    // saving the segment states is a separate instantiation: the plain forward issues no stores
+    // for it; so is the zero-order hold (never with saved states)
+    const void* fn = q.zoh_b ? reinterpret_cast<const void*>(&scan_lp_kernel<T, kLpW, SP, HZ, VEC, false, true>)
+                     : q.ck  ? reinterpret_cast<const void*>(&scan_lp_kernel<T, kLpW, SP, HZ, VEC, true, false>)
+                             : reinterpret_cast<const void*>(&scan_lp_kernel<T, kLpW, SP, HZ, VEC, false, false>);
     return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * kLpW), args, 0, stream) == hipSuccess
                ? MAMBA_SCAN_OK
                : MAMBA_SCAN_ERR_LAUNCH;

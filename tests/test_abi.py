@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 10
+    assert scan.load_library().mamba_scan_abi_version() == 11
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -111,10 +111,9 @@ CASES = [
     ("zoh_flag_is_known", lambda c: (c.__setitem__("flags", scan.ZOH_B), setattr(c["ptrs"], "u", None)), -1),
     ("both_forced", _flags(scan.FORCE_GENERIC | scan.FORCE_TILED), -6),
     ("chunked_and_lanes_forced", _flags(scan.FORCE_CHUNKED | scan.FORCE_LANES), -6),
-    # the chunked kernel: 16 states, the Euler input term, no saved states
+    # the chunked kernel: 16 states
     ("chunked_forced_32_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_CHUNKED),
                                             setattr(c["shape"], "dstate", 32)), -8),
-    ("chunked_forced_zoh", _flags(scan.DELTA_SOFTPLUS | scan.FORCE_CHUNKED | scan.ZOH_B), -8),
     # the short-call kernel: 16 states, Euler, at most 64 steps, no saved states
     ("step_forced_32_states", lambda c: (c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.FORCE_STEP),
                                          setattr(c["shape"], "dstate", 32)), -8),
@@ -160,6 +159,7 @@ def test_invalid_arguments_are_rejected(name, mutate, code):
     (scan.FORCE_GENERIC, 16, 1), (scan.FORCE_TILED, 16, 2), (scan.FORCE_LANES, 16, 3),
     (scan.FORCE_CHUNKED, 16, 4), (0, 24, 2), (0, 100, 1), (scan.ZOH_B, 16, 3), (scan.ZOH_B, 64, 3),
     (scan.ZOH_B, 24, 2), (scan.ZOH_B | scan.FORCE_TILED, 16, 2), (scan.ZOH_B | scan.FORCE_LANES, 32, 3),
+    (scan.ZOH_B | scan.FORCE_CHUNKED, 16, 4),
     (scan.FORCE_LANES, 64, 3), (scan.FORCE_STEP, 16, 5)])
 def test_kernel_query(extra, dstate, expect):
     """mamba_scan_fwd_kernel names the kernel a call would run (the forced one, or the default

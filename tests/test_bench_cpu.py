@@ -33,7 +33,7 @@ def test_traffic_is_reported_only_for_the_profiled_sources():
     assert bench.measured_traffic(w3, "auto") == bench.measured_traffic(w3, "lanes")
     assert bench.resolved_kernel(w3, "auto") == "lanes"
     assert bench.resolved_kernel(w3, "auto", zoh=True) == "lanes"
-    assert bench.resolved_kernel(workloads.WORKLOADS[4], "auto", zoh=True) == "lanes"
+    assert bench.resolved_kernel(workloads.WORKLOADS[4], "auto", zoh=True) == "chunked"
     assert bench.resolved_kernel(workloads.WORKLOADS[1], "auto", zoh=True) == "lanes"
     assert bench.resolved_kernel(workloads.WORKLOADS[5], "auto") == "lanes"
     # few long rows: the chunked kernel (4 x 1024 channels of 100 000 steps)

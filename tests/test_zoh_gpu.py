@@ -1,5 +1,6 @@
 """GPU parity of the zero-order-hold B discretisation (MAMBA_SCAN_ZOH_B) against the fp64 oracle
-with ``zoh_b=True``, for the lane-per-state (16, 32, 64 states), tiled and generic kernels. Bars as
+with ``zoh_b=True``, for the lane-per-state (16, 32, 64 states), chunked, tiled and generic
+kernels. Bars as
 for the Euler scan: max|g - r| / (1 + |r|) <= 1e-4 for fp32 inputs, <= 2e-3 for bf16 inputs (the
 GPU's coefficient (e^{dt A} - 1) / A is within 2^-20 relative of the exact one, see zoh_coef_f
 and zoh_coef2_f)."""
@@ -64,6 +65,12 @@ EDGE = [
     (2, 19, 32, 70, "f32", "zeros_mixed", "lanes", True),
     (1, 64, 64, 31, "f32", "rand", "lanes", True),
     (1, 33, 64, 50, "bf16", "tiny", "lanes", False),
+    # the chunked kernel: the default for few rows of >= 1024 steps, forced below that; ragged
+    # last chunks, both sides of the series threshold within a run
+    (1, 8, 16, 1100, "f32", "zeros_mixed", None, True),
+    (2, 5, 16, 200, "bf16", "tiny", "chunked", False),
+    (1, 6, 16, 77, "f32", "rand", "chunked", True),
+    (2, 64, 16, 130, "f32", "mamba", "chunked", False),
 ]
 
 
@@ -90,7 +97,7 @@ def test_zoh_edge_cases(idx):
     _check(x, 1e-4 if dtype == "f32" else 2e-3, kernel=kernel, h0=h0)
 
 
-@pytest.mark.parametrize("kernel,N", [("tiled", 16), ("generic", 16), ("lanes", 16), ("lanes", 64)])
+@pytest.mark.parametrize("kernel,N", [("tiled", 16), ("generic", 16), ("lanes", 16), ("lanes", 64), ("chunked", 16)])
 def test_zoh_with_zero_A_is_euler_bit_for_bit(kernel, N):
     """At A = 0 the zero-order-hold coefficient is dt exactly: the same bits as the Euler scan."""
     x = gu.case(720, 2, 64, N, 64, dtype="bf16")
