@@ -349,7 +349,7 @@ def decode_bench(args):
         scan.selective_scan_fn(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
                                delta_bias=p["delta_bias"], delta_softplus=w.softplus,
                                return_last_state=True, h0=h0, out=ys[i],
-                               last_state_out=hs[(i + 1) % 2])
+                               last_state_out=hs[(i + 1) % 2], zoh_b=args.zoh)
 
     def run_all():
         for i in range(calls):
@@ -358,7 +358,8 @@ def decode_bench(args):
     p0 = pieces[0]
     kname = scan.forward_kernel(p0["u"], p0["delta"], p0["A"], p0["B"], p0["C"], D=p0["D"], z=p0["z"],
                                 delta_bias=p0["delta_bias"], delta_softplus=w.softplus,
-                                return_last_state=True, h0=hs[0], out=ys[0], last_state_out=hs[1])
+                                return_last_state=True, h0=hs[0], out=ys[0], last_state_out=hs[1],
+                                zoh_b=args.zoh)
     for i in range(min(args.warmup, calls)):
         call(i, hs[i % 2])
     torch.cuda.synchronize()
@@ -406,7 +407,7 @@ def decode_bench(args):
                for k in xr}
         _, l1 = oracle.selective_scan(cut["u"], cut["delta"], cut["A"], cut["B"], cut["C"],
                                       D=cut["D"], z=cut["z"], delta_bias=cut["delta_bias"],
-                                      delta_softplus=w.softplus)
+                                      delta_softplus=w.softplus, zoh_b=args.zoh)
         lr.append(l1.reshape(-1))
     lg = hs[calls % 2].reshape(w.rows, w.dstate)[torch.tensor(rows, device=dev)].cpu().numpy()
     lr = np.stack(lr)
@@ -426,7 +427,7 @@ def decode_bench(args):
         "dtype": "f32",
         "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name + "-decode", "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
-                   "steps_per_call": C, "storage": w.dtype, "kernel": kname},
+                   "steps_per_call": C, "storage": w.dtype, "kernel": kname, "zoh_b": bool(args.zoh)},
         "kernel_sources_sha256": kernel_source_hash(kname, KERNEL_SOURCES),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 11
+#define MAMBA_SCAN_ABI_VERSION 12
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -60,8 +60,8 @@ typedef enum mamba_scan_dtype {
 /* B discretised by zero-order hold: the input term becomes (exp(dt*A[d,n]) - 1) / A[d,n] * B * u
  * (dt * B * u where A[d,n] = 0) instead of dt * B * u. "手把手用PyTorch实现Mamba的SSM层…" §2.1:
  * B_d = A^-1 (e^{A dt} - I) B, for a diagonal A. Forward only (mamba_scan_bwd rejects it). Run by
- * the lane-per-state kernels at dstate 16, 32 and 64 (ABI 9) and the chunked kernel (ABI 11), else
- * by the tiled or generic one. */
+ * the lane-per-state kernels at dstate 16, 32 and 64 (ABI 9), the chunked kernel (ABI 11) and the
+ * short-call kernel (ABI 12), else by the tiled or generic one. */
 #define MAMBA_SCAN_ZOH_B (1u << 2)
 /* Save the state before every 16-step segment, for the backward pass: the forward writes
  * h before steps 0, 16, 32, ... of every (b, d) row to the workspace, laid out (batch, dim,
@@ -93,9 +93,9 @@ typedef enum mamba_scan_dtype {
 #define MAMBA_SCAN_FORCE_CHUNKED (1u << 11)
 /* Short calls (ABI 7): one lane per (channel, state), each step in registers with no LDS staging
  * and no barrier; for recurrent decode (one or a few steps per call from the previous call's
- * last_state, "告别'炼丹'…" §2.1 times single-step inference). dstate 16, no ZOH_B, no
+ * last_state, "告别'炼丹'…" §2.1 times single-step inference). dstate 16 (ZOH_B from ABI 12), no
  * SAVE_CHECKPOINTS, at most 64 steps; the default for calls of at most 4 steps. Its states are the
- * same bits as the lane-per-state kernel's; y may differ in the last bits (the 16 states' terms
+ * same bits as the lane-per-state kernel's, with either input term; y may differ in the last bits (the 16 states' terms
  * are added in another order). */
 #define MAMBA_SCAN_FORCE_STEP (1u << 12)
 #define MAMBA_SCAN_KNOWN_FLAGS 0x1F0Fu

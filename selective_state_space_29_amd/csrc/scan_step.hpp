@@ -27,7 +27,9 @@ constexpr int kStepGroup = 4;   // steps whose inputs are loaded together before
 constexpr int kStepWavesOne = 16;
 constexpr int kStepWaves = 4;
 
-template <typename T, int W, bool SOFTPLUS, bool HAS_Z>
+// ZOH: B discretised by zero-order hold, the lane-per-state kernels' term (zoh_coef2_f times u,
+// times B), so that the states are their bits in either mode.
+template <typename T, int W, bool SOFTPLUS, bool HAS_Z, bool ZOH>
 __global__ __launch_bounds__(64 * W) void scan_step_kernel(ScanParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -39,7 +41,9 @@ __global__ __launch_bounds__(64 * W) void scan_step_kernel(ScanParams p) {
     const bool valid = d0 + c < p.dim;
     const int64_t d = valid ? d0 + c : p.dim - 1;
 
-    const float a2 = p.A[d * p.sA_d + n] * kLog2e;
+    const float an = p.A[d * p.sA_d + n];
+    const float a2 = an * kLog2e;
+    const float ia = an != 0.0f ? 1.0f / an : 0.0f;  // zero-order hold only
     float h = p.h0 ? p.h0[b * p.sh0_b + d * p.sh0_d + n] : 0.0f;
     const float bias = p.bias ? p.bias[d * p.sbias] : 0.0f;
     const float Dv = p.D ? p.D[d * p.sD] : 0.0f;  // no skip term: D = 0
@@ -56,8 +60,9 @@ __global__ __launch_bounds__(64 * W) void scan_step_kernel(ScanParams p) {
         const float xb = to_f32(xr[0]) + bias;
         const float dt = SOFTPLUS ? softplus_f(xb) : hw_exp2(xb * kLog2e);
         const float u0 = to_f32(ur[0]);
-        const float dA = hw_exp2(dt * a2);
-        h = __builtin_fmaf(dA, h, dt * u0 * to_f32(Br[0]));
+        const float x2 = dt * a2;
+        const float dA = hw_exp2(x2);
+        h = __builtin_fmaf(dA, h, (ZOH ? zoh_coef2_f(dt, x2, dA, ia) : dt) * u0 * to_f32(Br[0]));
         float s = to_f32(Cr[0]) * h;
         s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x111, 0xF, 0xF, false));
         s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x112, 0xF, 0xF, false));
@@ -89,8 +94,9 @@ __global__ __launch_bounds__(64 * W) void scan_step_kernel(ScanParams p) {
             if (t0 + i >= L) break;  // uniform across the grid
             const float xb = xv[i] + bias;
             const float dt = SOFTPLUS ? softplus_f(xb) : hw_exp2(xb * kLog2e);
-            const float dtu = dt * uv[i];
-            const float dA = hw_exp2(dt * a2);
+            const float x2 = dt * a2;
+            const float dA = hw_exp2(x2);
+            const float dtu = (ZOH ? zoh_coef2_f(dt, x2, dA, ia) : dt) * uv[i];
             h = __builtin_fmaf(dA, h, dtu * bv[i]);
             // sum over the row's 16 states: inclusive prefix sum, lane 15 ends with the total
             float s = cv[i] * h;
@@ -113,21 +119,21 @@ __global__ __launch_bounds__(64 * W) void scan_step_kernel(ScanParams p) {
 
 constexpr int64_t kStepLimitLen = 64;  // the longest call it takes when forced
 
-// 16 states, the Euler input term, no saved states, at most kStepLimitLen steps (the default
-// picks it for calls of at most kStepMaxLen steps).
+// 16 states, either input term, no saved states, at most kStepLimitLen steps (the default picks
+// it for calls of at most kStepMaxLen steps).
 inline bool step_eligible(const ScanParams& q) {
-    return q.dstate == 16 && !q.zoh_b && !q.ck && q.len <= kStepLimitLen &&
+    return q.dstate == 16 && !q.ck && q.len <= kStepLimitLen &&
            q.batch * ((q.dim + 4 * kStepWaves - 1) / (4 * kStepWaves)) <= 0x7fffffff;  // the most workgroups
 }
 
-template <typename T, bool SP, bool HZ>
+template <typename T, bool SP, bool HZ, bool ZOH>
 int launch_step_cfg(const ScanParams& q, hipStream_t stream) {
     void* args[] = {const_cast<ScanParams*>(&q)};
     const bool one = q.len == 1;
     const int W = one ? kStepWavesOne : kStepWaves;
     const int64_t groups = q.batch * ((q.dim + 4 * W - 1) / (4 * W));
-    const void* fn = one ? reinterpret_cast<const void*>(&scan_step_kernel<T, kStepWavesOne, SP, HZ>)
-                         : reinterpret_cast<const void*>(&scan_step_kernel<T, kStepWaves, SP, HZ>);
+    const void* fn = one ? reinterpret_cast<const void*>(&scan_step_kernel<T, kStepWavesOne, SP, HZ, ZOH>)
+                         : reinterpret_cast<const void*>(&scan_step_kernel<T, kStepWaves, SP, HZ, ZOH>);
     return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * W), args, 0, stream) == hipSuccess
                ? MAMBA_SCAN_OK
                : MAMBA_SCAN_ERR_LAUNCH;
@@ -137,10 +143,16 @@ template <typename T>
 int launch_step(const ScanParams& q, hipStream_t stream) {
     if (!step_eligible(q)) return MAMBA_SCAN_ERR_UNSUPPORTED;
     const bool sp = q.softplus != 0, hz = q.z != nullptr;
-    if (sp && hz) return launch_step_cfg<T, true, true>(q, stream);
-    if (sp) return launch_step_cfg<T, true, false>(q, stream);
-    if (hz) return launch_step_cfg<T, false, true>(q, stream);
-    return launch_step_cfg<T, false, false>(q, stream);
+    if (q.zoh_b) {
+        if (sp && hz) return launch_step_cfg<T, true, true, true>(q, stream);
+        if (sp) return launch_step_cfg<T, true, false, true>(q, stream);
+        if (hz) return launch_step_cfg<T, false, true, true>(q, stream);
+        return launch_step_cfg<T, false, false, true>(q, stream);
+    }
+    if (sp && hz) return launch_step_cfg<T, true, true, false>(q, stream);
+    if (sp) return launch_step_cfg<T, true, false, false>(q, stream);
+    if (hz) return launch_step_cfg<T, false, true, false>(q, stream);
+    return launch_step_cfg<T, false, false, false>(q, stream);
 }
 
 }  // namespace mscan

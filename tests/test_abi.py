@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 11
+    assert scan.load_library().mamba_scan_abi_version() == 12
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -160,7 +160,7 @@ def test_invalid_arguments_are_rejected(name, mutate, code):
     (scan.FORCE_CHUNKED, 16, 4), (0, 24, 2), (0, 100, 1), (scan.ZOH_B, 16, 3), (scan.ZOH_B, 64, 3),
     (scan.ZOH_B, 24, 2), (scan.ZOH_B | scan.FORCE_TILED, 16, 2), (scan.ZOH_B | scan.FORCE_LANES, 32, 3),
     (scan.ZOH_B | scan.FORCE_CHUNKED, 16, 4),
-    (scan.FORCE_LANES, 64, 3), (scan.FORCE_STEP, 16, 5)])
+    (scan.FORCE_LANES, 64, 3), (scan.FORCE_STEP, 16, 5), (scan.FORCE_STEP | scan.ZOH_B, 16, 5)])
 def test_kernel_query(extra, dstate, expect):
     """mamba_scan_fwd_kernel names the kernel a call would run (the forced one, or the default
     order); it launches nothing, so it answers without a GPU too."""

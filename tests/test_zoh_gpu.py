@@ -106,3 +106,18 @@ def test_zoh_with_zero_A_is_euler_bit_for_bit(kernel, N):
     yz, lz = _run(x, kernel, zoh=True)
     assert np.array_equal(ye, yz) and np.array_equal(le, lz)
 
+
+
+@pytest.mark.parametrize("L", [1, 3, 64])
+def test_zoh_short_calls_keep_the_lane_kernel_states(L):
+    """The short-call kernel with the zero-order hold (the default for calls of at most 4 steps):
+    its states are the lane-per-state kernel's bits, y agrees to rounding (the 16 states' terms
+    are added in another order), and both match the oracle."""
+    x = gu.case(740 + L, 2, 96, 16, L, dtype="bf16", a_kind="rand")
+    rng = np.random.default_rng(L)
+    h0 = rng.standard_normal((2, 96, 16)).astype(np.float32)
+    ys, ls = _run(x, "step", h0=h0)
+    yl, ll = _run(x, "lanes", h0=h0)
+    assert np.array_equal(ls, ll)
+    assert gu.rel_err(ys, yl) <= 1e-6
+    _check(x, 2e-3, kernel="step", h0=h0)
