@@ -294,20 +294,27 @@ def cpu_baseline_one_thread(w, inputs, zoh=False):
                       f"states), fp64, {dt:.2f} s on one thread"}
 
 
-def cpu_baseline(w, inputs, zoh=False):
-    """fp64 oracle over the whole workload on every core this process may use."""
+def cpu_baseline(w, inputs, zoh=False, min_wall_s=0.75):
+    """fp64 oracle over the whole workload on every core this process may use, repeated until
+    at least ``min_wall_s`` of wall time has passed (about 10 s of CPU work on 16 threads at the
+    Mamba-130m shape); the rate is over all passes."""
     import oracle
 
     cores = oracle.default_threads()
+    passes = 0
     t0 = time.perf_counter()
-    oracle.selective_scan(inputs["u"], inputs["delta"], inputs["A"], inputs["B"], inputs["C"],
-                          D=inputs["D"], z=inputs["z"], delta_bias=inputs["delta_bias"],
-                          delta_softplus=w.softplus, nthreads=cores, zoh_b=zoh)
-    dt = time.perf_counter() - t0
-    return {"value": round(w.elements / dt / 1e9, 4), "unit": "Gelem/s", "cores": cores,
+    while True:
+        oracle.selective_scan(inputs["u"], inputs["delta"], inputs["A"], inputs["B"], inputs["C"],
+                              D=inputs["D"], z=inputs["z"], delta_bias=inputs["delta_bias"],
+                              delta_softplus=w.softplus, nthreads=cores, zoh_b=zoh)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_wall_s or passes >= 64:
+            break
+    return {"value": round(passes * w.elements / dt / 1e9, 4), "unit": "Gelem/s", "cores": cores,
             "kind": "oracle",
             "sample": f"the whole workload ({w.rows} rows x {w.seqlen} steps x {w.dstate} states), "
-                      f"fp64, {dt:.2f} s wall on {cores} threads"}
+                      f"{passes} pass{'es' if passes > 1 else ''}, fp64, {dt:.2f} s wall on {cores} threads"}
 
 
 def decode_bench(args):

@@ -105,3 +105,18 @@ def test_sampled_indices_exist_for_every_workload():
         assert rows and all(0 <= r < w.rows for r in rows), w.name
         chans = bench.sampled_channels(w)
         assert chans and all(0 <= c < w.dim for c in chans), w.name
+
+
+def test_cpu_baseline_repeats_the_whole_workload_until_the_wall_time():
+    import bench
+    from selective_state_space_29_amd import workloads
+
+    w = workloads.WORKLOADS[1]
+    x = workloads.make_inputs(w)
+    r = bench.cpu_baseline(w, x, min_wall_s=0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "Gelem/s" and r["value"] > 0 and r["cores"] >= 1
+    passes = int(r["sample"].split(", ")[1].split()[0])
+    assert 1 <= passes <= 64
+    # the rate is over every pass: passes x elements / wall time
+    wall = float(r["sample"].split(" s wall")[0].split()[-1])
+    assert abs(r["value"] - passes * w.elements / max(wall, 1e-9) / 1e9) <= 0.5 * r["value"]
