@@ -68,9 +68,10 @@ class UpShape(ctypes.Structure):
 
 
 class MambaScanError(RuntimeError):
-    def __init__(self, code: int, msg: str):
-        super().__init__(f"mamba_scan_fwd failed ({code}): {msg}")
+    def __init__(self, code: int, msg: str, entry: str = "mamba_scan_fwd"):
+        super().__init__(f"{entry} failed ({code}): {msg}")
         self.code = code
+        self.entry = entry
 
 
 _lib = None
@@ -202,7 +203,7 @@ def _fwd_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_s
     else:
         ws_bytes = lib.mamba_scan_workspace_bytes(ctypes.byref(shape), dtype, flags)
         if ws_bytes < 0:
-            raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
+            _raise(int(ws_bytes), "mamba_scan_workspace_bytes")
         ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev) if (ws_bytes > 0 and allocate) else None
 
     st = Strides()
@@ -219,9 +220,11 @@ def _fwd_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_s
     return ptrs, shape, st, dtype, flags, y, ls, ws, keep
 
 
-def _raise(rc):
-    err = MambaScanError(rc, strerror(rc))
-    if rc in (-1, -2, -3, -4, -5, -6, -8, -9):
+def _raise(rc, entry="mamba_scan_fwd"):
+    """A library error code as an exception: ValueError (with the MambaScanError as its cause)
+    for the codes that reject the arguments, MambaScanError itself for a refused launch."""
+    err = MambaScanError(rc, strerror(rc), entry)
+    if rc in (-1, -2, -3, -4, -5, -6, -8, -9, -10):
         raise ValueError(str(err)) from err
     raise err
 
@@ -278,7 +281,7 @@ def forward_kernel(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
         rc = lib.mamba_scan_fwd_kernel(ctypes.byref(ptrs), ctypes.byref(shape), ctypes.byref(st), dtype, flags)
     del keep
     if rc < 0:
-        _raise(rc)
+        _raise(rc, "mamba_scan_fwd_kernel")
     return KERNEL_NAMES[rc]
 
 
@@ -359,7 +362,7 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
         ws_bytes = lib.mamba_scan_bwd_workspace_bytes(
             ctypes.byref(shape), dtype, flags | (SAVE_CHECKPOINTS if checkpoints is not None else 0))
         if ws_bytes < 0:
-            raise MambaScanError(int(ws_bytes), strerror(int(ws_bytes)))
+            _raise(int(ws_bytes), "mamba_scan_bwd_workspace_bytes")
         ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev)
     ptrs = BwdPtrs(_ptr(u), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(delta_bias),
                    _ptr(h0), _ptr(dy), _ptr(dlast_state), _ptr(g["u"]), _ptr(g["delta"]), _ptr(g.get("z")),
@@ -373,10 +376,7 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
         entry = lib.mamba_scan_bwd_static if static_scratch else lib.mamba_scan_bwd
         rc = entry(ctypes.byref(ptrs), ctypes.byref(shape), dtype, flags, stream)
     if rc != 0:
-        err = MambaScanError(rc, strerror(rc))
-        if rc in (-1, -2, -3, -4, -5, -6, -8, -9, -10):
-            raise ValueError(str(err)) from err
-        raise err
+        _raise(rc, "mamba_scan_bwd_static" if static_scratch else "mamba_scan_bwd")
     if ws is not None:
         ws.record_stream(torch.cuda.current_stream(dev))
     return g
@@ -473,10 +473,7 @@ def block_upstream(x, conv_w, conv_b, w_x, w_dt, dstate, dt_rank, out=None):
         rc = lib.mamba_block_upstream(ctypes.byref(ptrs), ctypes.byref(shape), BF16,
                                       torch.cuda.current_stream(x.device).cuda_stream)
     if rc != 0:
-        err = MambaScanError(rc, strerror(rc))
-        if rc in (-1, -2, -3, -4, -5, -6, -8):
-            raise ValueError(str(err)) from err
-        raise err
+        _raise(rc, "mamba_block_upstream")
     return u, xdbl, delta
 
 
