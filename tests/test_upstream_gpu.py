@@ -139,3 +139,22 @@ def test_block_ssm_is_upstream_then_scan():
     torch.cuda.synchronize()
     assert torch.equal(y, y2) and torch.equal(ls, ls2)
     assert torch.isfinite(y).all()
+
+
+def sweep_case(i):
+    """Upstream sweep case i, drawn from a generator seeded by i alone, within what the kernel
+    takes (dim a multiple of 8, dt_rank a multiple of 8 up to 64, at most 128 projection rows,
+    L a multiple of 4, d_conv 1-4)."""
+    rng = np.random.default_rng(29_700 + i)
+    dt_rank = 8 * int(rng.integers(1, 9))
+    dstate = int(rng.integers(1, (128 - dt_rank) // 2 + 1))
+    return (int(rng.integers(1, 4)), 8 * int(rng.integers(1, 129)), dstate, dt_rank,
+            4 * int(rng.integers(1, 131)), int(rng.integers(1, 5)), bool(rng.random() < 0.75))
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_upstream_sweep(i):
+    batch, dim, dstate, dt_rank, L, d_conv, bias = sweep_case(i)
+    print(f"upstream sweep case {i}: {sweep_case(i)}", flush=True)
+    x = workloads.make_upstream_case(29_800 + i, batch, dim, dstate, dt_rank, L, d_conv, bias)
+    check(x, dstate, dt_rank)
