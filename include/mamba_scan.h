@@ -29,7 +29,13 @@
  *    A/h0/last_state) must be 1; the other strides are free (slices are fine) but must be >= 0.
  *    A NULL strides argument means every tensor is contiguous.
  *  - z, D, delta_bias, h0 may be NULL (absent: no gate, no skip, no bias, zero initial state).
- *    last_state must be non-NULL exactly when MAMBA_SCAN_RETURN_LAST_STATE is set.
+ *    last_state must be non-NULL exactly when MAMBA_SCAN_RETURN_LAST_STATE is set (it may be
+ *    NULL in an empty call, below).
+ *  - Empty calls (ABI 13): batch, dim and len may be 0 (dstate must be at least 1). A tensor with
+ *    no elements is never read or written and its pointer may be NULL. With batch * dim = 0 the
+ *    call enqueues nothing. With len = 0, y has no elements and last_state, when requested,
+ *    receives h0, or zeros without h0: a scan of no steps leaves its initial state (one launch
+ *    of the generic kernel). A forced kernel is not used in an empty call.
  *  - Outputs must not overlap any input or each other.
  *  - The work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *    returns without waiting. Calls on different streams may run concurrently.
@@ -46,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 12
+#define MAMBA_SCAN_ABI_VERSION 13
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -103,7 +109,7 @@ typedef enum mamba_scan_dtype {
 /* error codes */
 #define MAMBA_SCAN_OK 0
 #define MAMBA_SCAN_ERR_NULL (-1)      /* a required pointer is NULL */
-#define MAMBA_SCAN_ERR_SHAPE (-2)     /* a dimension <= 0, or a stride < 0 */
+#define MAMBA_SCAN_ERR_SHAPE (-2)     /* a dimension < 0, dstate < 1, or a stride < 0 */
 #define MAMBA_SCAN_ERR_STRIDE (-3)    /* an innermost stride is not 1 */
 #define MAMBA_SCAN_ERR_DTYPE (-4)     /* unknown dtype */
 #define MAMBA_SCAN_ERR_DSTATE (-5)    /* dstate above MAMBA_SCAN_MAX_DSTATE */
@@ -157,7 +163,10 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s,
 /* The kernel mamba_scan_fwd would run for these arguments (ABI 7): one of the values below, or
  * the error code mamba_scan_fwd would return before launching. Enqueues nothing; the pointers are
  * only compared (overlaps, alignment), never dereferenced. The choice between the chunked and
- * the lane-per-state kernel depends on the current device's compute-unit count. */
+ * the lane-per-state kernel depends on the current device's compute-unit count. An empty call
+ * gives MAMBA_SCAN_KERNEL_NONE when it enqueues nothing and MAMBA_SCAN_KERNEL_GENERIC when it
+ * writes last_state (ABI 13). */
+#define MAMBA_SCAN_KERNEL_NONE 0
 #define MAMBA_SCAN_KERNEL_GENERIC 1
 #define MAMBA_SCAN_KERNEL_TILED 2
 #define MAMBA_SCAN_KERNEL_LANES 3
@@ -215,6 +224,12 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *      MAMBA_SCAN_FORCE_TILED: the segment-tiled backward (64 channels per workgroup, at most 2
  *        states per wave), any dstate.
  *    The two give the same gradients to rounding, not bit for bit; each is deterministic.
+ *  - Empty calls (ABI 13): batch, dim and len may be 0, as in the forward (tensors with no
+ *    elements are never touched and may be NULL). No scan runs and the workspace may be empty
+ *    (mamba_scan_bwd_workspace_bytes gives 0); the gradients that have elements are sums over
+ *    nothing and are written as zeros (dA, dD, ddelta_bias; dB and dC when dim = 0), except dh0,
+ *    which with len = 0 receives dlast_state (or zeros without it): the initial state of a scan
+ *    of no steps is its final state.
  *  - Any dstate up to MAMBA_SCAN_MAX_DSTATE. Above 16 the states are processed in blocks of at
  *    most 16, one launch each (either kernel): du, ddelta and dz are accumulated in place across
  *    the blocks, in block order, so their values can differ in the last bits from a one-block

@@ -35,7 +35,10 @@ Span span_of(const void* ptr, int64_t esize, const int64_t* sizes, const int64_t
     Span s{0, 0, false};
     if (!ptr) return s;
     int64_t maxoff = 0;
-    for (int i = 0; i < nd; ++i) maxoff += (sizes[i] - 1) * strides[i];
+    for (int i = 0; i < nd; ++i) {
+        if (sizes[i] <= 0) return s;  // no elements: nothing is read or written
+        maxoff += (sizes[i] - 1) * strides[i];
+    }
     s.lo = reinterpret_cast<uintptr_t>(ptr);
     s.hi = s.lo + (uintptr_t)((maxoff + 1) * esize);
     s.valid = true;
@@ -65,6 +68,18 @@ void contiguous_strides(const mamba_scan_shape& s, mamba_scan_strides* st) {
     st->delta_bias = 1;
 }
 
+// batch, dim and len may be 0 (an empty call); dstate must be at least 1.
+bool bad_shape(const mamba_scan_shape& s) { return s.batch < 0 || s.dim < 0 || s.len < 0 || s.dstate <= 0; }
+
+// What an empty call does: 0 = not empty; 1 = nothing (no (batch, channel) row, or no step and no
+// last_state); 2 = no step, last_state written with h0 or zeros (the generic kernel, whose step
+// loop then runs no iteration).
+int empty_plan(const mamba_scan_shape& s, uint32_t flags) {
+    if (s.batch * s.dim == 0) return 1;
+    if (s.len == 0) return (flags & MAMBA_SCAN_RETURN_LAST_STATE) ? 2 : 1;
+    return 0;
+}
+
 int validate(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_scan_strides* st,
              mamba_scan_dtype dtype, uint32_t flags) {
     if (!p || !s || !st) return MAMBA_SCAN_ERR_NULL;
@@ -73,11 +88,15 @@ int validate(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const mamba_sc
     const uint32_t forced = flags & (MAMBA_SCAN_FORCE_GENERIC | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_LANES |
                                      MAMBA_SCAN_FORCE_CHUNKED | MAMBA_SCAN_FORCE_STEP);
     if (forced & (forced - 1)) return MAMBA_SCAN_ERR_ARGS;  // at most one kernel may be forced
-    if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+    if (bad_shape(*s)) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
-    if (!p->u || !p->delta || !p->B || !p->C || !p->A || !p->y) return MAMBA_SCAN_ERR_NULL;
+    // a tensor with no elements is never touched: its pointer may be NULL
+    const bool rows = s->batch * s->dim > 0, steps = s->batch * s->len > 0;
+    if ((rows && s->len > 0 && (!p->u || !p->delta || !p->y)) || (steps && (!p->B || !p->C)) ||
+        (s->dim > 0 && !p->A))
+        return MAMBA_SCAN_ERR_NULL;
     const bool want_ls = (flags & MAMBA_SCAN_RETURN_LAST_STATE) != 0;
-    if (want_ls != (p->last_state != nullptr)) return MAMBA_SCAN_ERR_ARGS;
+    if (want_ls ? (rows && !p->last_state) : p->last_state != nullptr) return MAMBA_SCAN_ERR_ARGS;
     if (p->workspace_bytes < 0 || (p->workspace_bytes > 0 && !p->workspace)) return MAMBA_SCAN_ERR_ARGS;
 
     const int64_t* inner3[] = {st->u, st->delta, st->z, st->B, st->C, st->y, st->h0, st->last_state};
@@ -192,6 +211,7 @@ bool prefer_chunked(const ScanParams& q) {
 int check_checkpoint_workspace(const mamba_scan_ptrs* p, const mamba_scan_shape* s, uint32_t flags) {
     if (!(flags & MAMBA_SCAN_SAVE_CHECKPOINTS)) return MAMBA_SCAN_OK;
     const int64_t need = s->batch * s->dim * ((s->len + 15) / 16) * s->dstate * 4;
+    if (need == 0) return MAMBA_SCAN_OK;  // an empty call saves nothing
     if (!p->workspace || p->workspace_bytes < need) return MAMBA_SCAN_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(p->workspace) % 4) return MAMBA_SCAN_ERR_ARGS;
     return MAMBA_SCAN_OK;
@@ -285,7 +305,7 @@ const char* mamba_scan_strerror(int code) {
     switch (code) {
         case MAMBA_SCAN_OK: return "success";
         case MAMBA_SCAN_ERR_NULL: return "a required pointer is NULL";
-        case MAMBA_SCAN_ERR_SHAPE: return "a dimension is <= 0 or a stride is negative";
+        case MAMBA_SCAN_ERR_SHAPE: return "a dimension is negative, dstate < 1, or a stride is negative";
         case MAMBA_SCAN_ERR_STRIDE: return "an innermost stride (along len, or along dstate) is not 1";
         case MAMBA_SCAN_ERR_DTYPE: return "unknown dtype (expected MAMBA_SCAN_F32 or MAMBA_SCAN_BF16)";
         case MAMBA_SCAN_ERR_DSTATE: return "dstate exceeds MAMBA_SCAN_MAX_DSTATE";
@@ -306,7 +326,7 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
     if (!s) return MAMBA_SCAN_ERR_NULL;
     if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
     if (flags & ~MAMBA_SCAN_KNOWN_FLAGS) return MAMBA_SCAN_ERR_ARGS;
-    if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+    if (bad_shape(*s)) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
     if (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) return s->batch * s->dim * ((s->len + 15) / 16) * s->dstate * 4;
     return 0;
@@ -316,8 +336,10 @@ int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dty
     if (!s) return MAMBA_SCAN_ERR_NULL;
     if (dtype != MAMBA_SCAN_F32 && dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
     if (flags & ~(kBwdFlags | MAMBA_SCAN_SAVE_CHECKPOINTS)) return MAMBA_SCAN_ERR_ARGS;
-    if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+    if (bad_shape(*s)) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
+    if ((flags & MAMBA_SCAN_FORCE_LANES) && (flags & MAMBA_SCAN_FORCE_TILED)) return MAMBA_SCAN_ERR_ARGS;
+    if (s->batch * s->dim * s->len == 0) return 0;  // an empty call runs no scan
     const int pick = bwd_pick(*s, dtype == MAMBA_SCAN_BF16 ? 2 : 4, flags);
     if (pick < 0) return pick;
     const bool given_ck = (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) != 0;
@@ -358,14 +380,17 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     const int64_t need =
         mamba_scan_bwd_workspace_bytes(s, dtype, flags | (p->checkpoints ? MAMBA_SCAN_SAVE_CHECKPOINTS : 0u));
     if (need < 0) return (int)need;
-    if (!p->u || !p->delta || !p->B || !p->C || !p->A || !p->dy || !p->du || !p->ddelta || !p->dB ||
-        !p->dC || !p->dA)
+    // pointers of tensors with elements (batch, dim and len may be 0: an empty call)
+    const bool cells = s->batch * s->dim * s->len > 0, steps = s->batch * s->len > 0;
+    if ((cells && (!p->u || !p->delta || !p->dy || !p->du || !p->ddelta)) ||
+        (steps && (!p->B || !p->C || !p->dB || !p->dC)) || (s->dim > 0 && (!p->A || !p->dA)))
         return MAMBA_SCAN_ERR_NULL;
-    if ((p->z != nullptr) != (p->dz != nullptr) || (p->D != nullptr) != (p->dD != nullptr) ||
-        (p->delta_bias != nullptr) != (p->ddelta_bias != nullptr))
+    if ((cells && (p->z != nullptr) != (p->dz != nullptr)) ||
+        (s->dim > 0 && ((p->D != nullptr) != (p->dD != nullptr) ||
+                        (p->delta_bias != nullptr) != (p->ddelta_bias != nullptr))))
         return MAMBA_SCAN_ERR_ARGS;
     if (p->workspace_bytes < 0 || (p->workspace_bytes > 0 && !p->workspace)) return MAMBA_SCAN_ERR_ARGS;
-    if (!p->workspace || p->workspace_bytes < need) return MAMBA_SCAN_ERR_WORKSPACE;
+    if (need > 0 && (!p->workspace || p->workspace_bytes < need)) return MAMBA_SCAN_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(p->workspace) % 256 != 0) return MAMBA_SCAN_ERR_ARGS;
     if (reinterpret_cast<uintptr_t>(p->checkpoints) % 4 != 0) return MAMBA_SCAN_ERR_ARGS;
     const int64_t es = dtype == MAMBA_SCAN_BF16 ? 2 : 4;
@@ -376,7 +401,7 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     const int64_t DN = s->batch * s->dim * s->dstate;
     auto span = [](const void* ptr, int64_t bytes) {
         Span x{0, 0, false};
-        if (!ptr) return x;
+        if (!ptr || bytes <= 0) return x;  // no elements: nothing is read or written
         x.lo = reinterpret_cast<uintptr_t>(ptr);
         x.hi = x.lo + (uintptr_t)bytes;
         x.valid = true;
@@ -397,6 +422,21 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
             if (&o2 != &o && overlaps(o, o2)) return MAMBA_SCAN_ERR_ARGS;
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (!cells) {
+        // no scan: the gradients that have elements are sums over nothing, except that of the
+        // initial state over no steps, which is the final state's (or zero)
+        int rc = MAMBA_SCAN_OK;
+        auto fill = [&](float* dst, const float* src, int64_t n) {
+            if (rc == MAMBA_SCAN_OK) rc = launch_bwd_fill(dst, src, n, hs);
+        };
+        fill(p->dA, nullptr, s->dim * s->dstate);
+        fill(p->dD, nullptr, s->dim);
+        fill(p->ddelta_bias, nullptr, s->dim);
+        fill(p->dB, nullptr, NL);
+        fill(p->dC, nullptr, NL);
+        fill(p->dh0, s->len == 0 ? p->dlast_state : nullptr, DN);
+        return rc;
+    }
     const bool sp = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) != 0;
     return lanes ? launch_bwd_ls_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs)
                  : launch_bwd_tiled_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
@@ -466,7 +506,7 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const ma
     if (st_in) {
         st = *st_in;
     } else {
-        if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+        if (bad_shape(*s)) return MAMBA_SCAN_ERR_SHAPE;
         contiguous_strides(*s, &st);
     }
     const int rc = validate(p, s, &st, dtype, flags);
@@ -477,6 +517,7 @@ int mamba_scan_fwd(const mamba_scan_ptrs* p, const mamba_scan_shape* s, const ma
 
     const int wrc = check_checkpoint_workspace(p, s, flags);
     if (wrc != MAMBA_SCAN_OK) return wrc;
+    if (const int e = empty_plan(*s, flags)) return e == 1 ? MAMBA_SCAN_OK : launch_generic_any(q, bf16, hs);
     const int kernel = choose_kernel(q, flags, bf16);
     switch (kernel) {
         case MAMBA_SCAN_KERNEL_CHUNKED: return launch_lp_any(q, bf16, hs);
@@ -495,13 +536,14 @@ int mamba_scan_fwd_kernel(const mamba_scan_ptrs* p, const mamba_scan_shape* s, c
     if (st_in) {
         st = *st_in;
     } else {
-        if (s->batch <= 0 || s->dim <= 0 || s->len <= 0 || s->dstate <= 0) return MAMBA_SCAN_ERR_SHAPE;
+        if (bad_shape(*s)) return MAMBA_SCAN_ERR_SHAPE;
         contiguous_strides(*s, &st);
     }
     const int rc = validate(p, s, &st, dtype, flags);
     if (rc != MAMBA_SCAN_OK) return rc;
     const int wrc = check_checkpoint_workspace(p, s, flags);
     if (wrc != MAMBA_SCAN_OK) return wrc;
+    if (const int e = empty_plan(*s, flags)) return e == 1 ? MAMBA_SCAN_KERNEL_NONE : MAMBA_SCAN_KERNEL_GENERIC;
     const ScanParams q = make_params(p, s, &st, flags);
     return choose_kernel(q, flags, dtype == MAMBA_SCAN_BF16);
 }

@@ -139,7 +139,7 @@ def _s3(x, fallback=(0, 0, 1)):
     return (_I64 * 3)(*(_strides(x) if x is not None else fallback))
 
 
-KERNEL_NAMES = {1: "generic", 2: "tiled", 3: "lanes", 4: "chunked", 5: "step"}
+KERNEL_NAMES = {0: "none", 1: "generic", 2: "tiled", 3: "lanes", 4: "chunked", 5: "step"}
 
 
 def _fwd_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, return_last_state, h0, kernel, out,

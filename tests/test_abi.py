@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 12
+    assert scan.load_library().mamba_scan_abi_version() == 13
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -95,7 +95,15 @@ CASES = [
     ("null_B", _set("ptrs", "B", None), -1),
     ("null_A", _set("ptrs", "A", None), -1),
     ("null_y", _set("ptrs", "y", None), -1),
-    ("zero_batch", _set("shape", "batch", 0), -2),
+    # empty calls: no (batch, channel) row, or no step and no last_state, enqueue nothing
+    ("zero_batch_is_empty", _set("shape", "batch", 0), 0),
+    ("zero_dim_is_empty", _set("shape", "dim", 0), 0),
+    ("zero_len_is_empty", _set("shape", "len", 0), 0),
+    ("empty_call_reads_no_sequence", lambda c: (setattr(c["shape"], "batch", 0),
+                                                [setattr(c["ptrs"], k, None) for k in ("u", "delta", "B", "C", "y")]), 0),
+    ("empty_call_still_needs_A", lambda c: (setattr(c["shape"], "batch", 0), setattr(c["ptrs"], "A", None)), -1),
+    ("no_steps_still_need_B", lambda c: (setattr(c["shape"], "dim", 0), setattr(c["ptrs"], "B", None)), -1),
+    ("negative_batch", _set("shape", "batch", -1), -2),
     ("negative_len", _set("shape", "len", -5), -2),
     ("zero_dstate", _set("shape", "dstate", 0), -2),
     ("inner_stride_u", _set("st", "u", (ctypes.c_int64 * 3)(120, 40, 2)), -3),
@@ -200,7 +208,9 @@ def test_null_struct_pointers_are_rejected():
 
 def test_null_strides_means_contiguous_and_still_validates():
     assert fake_call(_set("ptrs", "delta", None), strides=False) == -1
-    assert fake_call(_set("shape", "dim", 0), strides=False) == -2
+    assert fake_call(_set("shape", "dim", -1), strides=False) == -2
+    assert fake_call(_set("shape", "dstate", 0), strides=False) == -2
+    assert fake_call(_set("shape", "dim", 0), strides=False) == 0  # empty: nothing enqueued
 
 
 def test_strerror_and_workspace_query():
@@ -212,7 +222,13 @@ def test_strerror_and_workspace_query():
     # no forward kernel uses scratch memory: only the saved states need a workspace
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok), scan.BF16, 0) == 0
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok), scan.BF16, scan.FORCE_CHUNKED) == 0
-    assert lib.mamba_scan_workspace_bytes(ctypes.byref(scan.Shape(0, 1, 1, 1)), 0, 0) == -2
+    assert lib.mamba_scan_workspace_bytes(ctypes.byref(scan.Shape(-1, 1, 1, 1)), 0, 0) == -2
+    assert lib.mamba_scan_workspace_bytes(ctypes.byref(scan.Shape(1, 1, 1, 0)), 0, 0) == -2
+    # empty calls need nothing, with saved states or without, forward or backward
+    for shp in ((0, 4, 40, 16), (2, 0, 40, 16), (2, 4, 0, 16)):
+        assert lib.mamba_scan_workspace_bytes(ctypes.byref(scan.Shape(*shp)), scan.BF16, scan.SAVE_CHECKPOINTS) == 0
+        for fl in (0, scan.FORCE_LANES, scan.FORCE_TILED, scan.SAVE_CHECKPOINTS):
+            assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(*shp)), scan.BF16, fl) == 0
     assert lib.mamba_scan_workspace_bytes(ctypes.byref(ok), 3, 0) == -4
     # saved segment states: (batch, dim, ceil(len/16), dstate) fp32
     for shp in ((2, 3, 40, 16), (1, 5, 16, 32), (3, 2, 17, 64)):
@@ -260,7 +276,8 @@ BWD_CASES = [
      lambda c: (c.__setitem__("flags", scan.FORCE_LANES), setattr(c["shape"], "dstate", 8)), -8),
     ("zoh_not_in_backward", lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.ZOH_B), -6),
     ("bad_dtype", lambda c: c.__setitem__("dtype", 7), -4),
-    ("zero_len", _set("shape", "len", 0), -2),
+    ("negative_len", _set("shape", "len", -1), -2),
+    ("zero_dstate", _set("shape", "dstate", 0), -2),
     ("dstate_above_max", _set("shape", "dstate", 300), -5),
     ("output_aliases_input", lambda c: setattr(c["ptrs"], "du", c["ptrs"].dy), -6),
     ("outputs_alias", lambda c: setattr(c["ptrs"], "dB", c["ptrs"].dC), -6),
@@ -339,7 +356,9 @@ def test_backward_workspace_query():
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), scan.BF16, scan.FORCE_TILED | scan.FORCE_LANES) == -6
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(2, 8, 40, 24)), scan.BF16,
                                               scan.FORCE_LANES) == -8
-    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(0, 1, 1, 1)), 0, 0) == -2
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(-1, 1, 1, 1)), 0, 0) == -2
+    assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(scan.Shape(0, 1, 1, 1)), 0,
+                                              scan.FORCE_TILED | scan.FORCE_LANES) == -6
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 3, 0) == -4
     assert lib.mamba_scan_bwd_workspace_bytes(ctypes.byref(ok), 0, 1 << 1) == -6
     # given the forward's saved states, the backward needs no room for recomputed ones
