@@ -70,6 +70,10 @@ def _bind_bwd(lib):
     P = ctypes.c_void_p
     f.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int] + [P] * 5 + [P] * 4 + [ctypes.c_int] + [
         P] * 11 + [ctypes.c_int]
+    g = lib.oracle_selective_scan_bwd_ex
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int] + [P] * 5 + [P] * 4 + [ctypes.c_int] * 2 + [
+        P] * 11 + [ctypes.c_int]
     return lib
 
 
@@ -164,9 +168,11 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
 
 
 def selective_scan_bwd(u, delta, A, B, C, gy, D=None, z=None, delta_bias=None,
-                       delta_softplus=False, h0=None, glast=None, nthreads=None, lib_path=None):
+                       delta_softplus=False, h0=None, glast=None, nthreads=None, lib_path=None,
+                       zoh_b=False):
     """Gradients of a loss with dLoss/dy = gy (batch, dim, L) and dLoss/dlast_state = glast
-    (batch, dim, N) or None, in fp64. Inputs as for ``selective_scan``.
+    (batch, dim, N) or None, in fp64. Inputs as for ``selective_scan`` (``zoh_b``: of the scan
+    whose B is discretised by zero-order hold).
 
     Returns a dict: u, delta, z (batch, dim, L; z only when given), B, C (batch, N, L), A (dim, N),
     D, delta_bias (dim,) and h0 (batch, dim, N), all fp64.
@@ -196,9 +202,9 @@ def selective_scan_bwd(u, delta, A, B, C, gy, D=None, z=None, delta_bias=None,
     def ptr(a):
         return None if a is None else a.ctypes.data
 
-    rc = lib.oracle_selective_scan_bwd(
+    rc = lib.oracle_selective_scan_bwd_ex(
         batch, dim, L, N, in_dtype, ptr(u), ptr(delta), ptr(z), ptr(B), ptr(C), ptr(A), ptr(D),
-        ptr(delta_bias), ptr(h0), int(bool(delta_softplus)), ptr(gy), ptr(glast),
+        ptr(delta_bias), ptr(h0), int(bool(delta_softplus)), int(bool(zoh_b)), ptr(gy), ptr(glast),
         ptr(out["u"]), ptr(out["delta"]), ptr(out["z"]), ptr(out["B"]), ptr(out["C"]),
         ptr(out["A"]), ptr(out["D"]), ptr(out["delta_bias"]), ptr(out["h0"]),
         int(nthreads or default_threads()))

@@ -63,6 +63,19 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  * invertible) its limit dt. expm1 keeps it accurate when A dt is small. */
 static double zoh_coef(double dt, double An) { return An == 0.0 ? dt : expm1(dt * An) / An; }
 
+/* Its derivative with respect to A: d/dA [(e^{A dt} - 1) / A] = (dt e^{A dt} - (e^{A dt} - 1)/A) / A,
+ * whose limit at A = 0 is dt^2 / 2. For |A dt| < 1/64 the Taylor series of the same function,
+ * dt^2 (1/2 + x/3 + x^2/8 + x^3/30 + x^4/144) with x = A dt (the first dropped term, x^5 / 840,
+ * is below 3e-12 of the sum there), so that the difference of two nearly equal terms is never
+ * formed; above it the closed form, whose cancellation costs at most a factor 2/|x| < 128 on the
+ * fp64 rounding. Its derivative with respect to dt is e^{A dt}. */
+static double zoh_coef_dA(double dt, double An) {
+    const double x = dt * An;
+    if (fabs(x) < 1.0 / 64.0)
+        return dt * dt * (0.5 + x * (1.0 / 3.0 + x * (1.0 / 8.0 + x * (1.0 / 30.0 + x / 144.0))));
+    return (dt * exp(x) - expm1(x) / An) / An;
+}
+
 /* One row (b, d): writes y[out_row, 0..L) and last_state[out_row, 0..N). */
 static void scan_row(const orc_args* a, int64_t b, int64_t d, int64_t out_row, double* h) {
     const int64_t L = a->len, N = a->dstate, D = a->dim;
@@ -190,6 +203,10 @@ int oracle_selective_scan(int64_t batch, int64_t dim, int64_t len, int64_t dstat
  *   gdt_t = sum_n lam_t (a_t h_{t-1} A + B_t u_t);  gA[d,n] += lam_t a_t h_{t-1} dt_t (summed over b, t)
  *   gx_t = gdt_t sigmoid(x_t) (softplus) or gdt_t dt_t (exp);  gdelta_t = gx_t;  gbias[d] += gx_t
  *   gD[d] += gp_t u_t;  then lam_{t-1} = a_t lam_t;  gh0 = lam before the first step.
+ * With the zero-order hold the input term is c_t B_t u_t with c_t = (a_t - 1) / A (dt_t at A = 0)
+ * in place of dt_t B_t u_t, so dt_t becomes c_t in gB and gu, the input term's derivative in gdt
+ * is dc/ddt = a_t instead of 1 (gdt_t = sum_n lam_t a_t (h_{t-1} A + B_t u_t)), and gA gains
+ * lam_t B_t u_t dc/dA (zoh_coef_dA); the adjoint recurrence is unchanged.
  * Each row keeps its forward states (fp64); the reductions over rows use per-thread fp64
  * partial sums added in thread order.
  * ---------------------------------------------------------------------------------------------- */
@@ -221,7 +238,9 @@ static void bwd_row(const orc_bwd_job* j, int64_t b, int64_t d, double* hist, do
         const double ut = widen(a->u, a->in_dtype, row_off + t);
         for (int64_t n = 0; n < N; ++n) {
             const double Bt = widen(a->B, a->in_dtype, bc_off + n * L + t);
-            hist[(t + 1) * N + n] = exp(dt * (double)a->A[d * N + n]) * hist[t * N + n] + dt * Bt * ut;
+            const double An = (double)a->A[d * N + n];
+            const double cf = a->zoh_b ? zoh_coef(dt, An) : dt;
+            hist[(t + 1) * N + n] = exp(dt * An) * hist[t * N + n] + cf * Bt * ut;
         }
     }
     for (int64_t n = 0; n < N; ++n) lam[n] = j->glast ? j->glast[(b * D + d) * N + n] : 0.0;
@@ -251,12 +270,15 @@ static void bwd_row(const orc_bwd_job* j, int64_t b, int64_t d, double* hist, do
             const double Ct = widen(a->C, a->in_dtype, bc_off + n * L + t);
             const double An = (double)a->A[d * N + n];
             const double an = exp(dt * An);
+            const double cf = a->zoh_b ? zoh_coef(dt, An) : dt;    /* input coefficient */
+            const double cf_dt = a->zoh_b ? an : 1.0;               /* its derivative in dt */
             lam[n] += gp * Ct;
             j->pC[bc_off + n * L + t] += gp * h[n];
-            j->pB[bc_off + n * L + t] += lam[n] * dt * ut;
-            gu += lam[n] * dt * Bt;
-            gdt += lam[n] * (an * hprev[n] * An + Bt * ut);
+            j->pB[bc_off + n * L + t] += lam[n] * cf * ut;
+            gu += lam[n] * cf * Bt;
+            gdt += lam[n] * (an * hprev[n] * An + cf_dt * Bt * ut);
             j->pA[d * N + n] += lam[n] * an * hprev[n] * dt;
+            if (a->zoh_b) j->pA[d * N + n] += lam[n] * Bt * ut * zoh_coef_dA(dt, An);
             lam[n] *= an;
         }
         const double gx = a->delta_softplus ? gdt * sigmoid(x) : gdt * dt;
@@ -293,20 +315,20 @@ static void* orc_bwd_worker(void* p) {
  * NULL. gz/gD/gbias are written even when z/D/delta_bias are absent (then as if they were zero,
  * with gz left untouched). Returns 0, or a negative value on a bad argument or allocation failure.
  */
-int oracle_selective_scan_bwd(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int in_dtype,
-                              const void* u, const void* delta, const void* z, const void* B,
-                              const void* C, const float* A, const float* Dvec,
-                              const float* delta_bias, const double* h0, int delta_softplus,
-                              const double* gy, const double* glast, double* gu, double* gdelta,
-                              double* gz, double* gB, double* gC, double* gA, double* gD,
-                              double* gbias, double* gh0, int nthreads) {
+int oracle_selective_scan_bwd_ex(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int in_dtype,
+                                 const void* u, const void* delta, const void* z, const void* B,
+                                 const void* C, const float* A, const float* Dvec,
+                                 const float* delta_bias, const double* h0, int delta_softplus,
+                                 int zoh_b, const double* gy, const double* glast, double* gu,
+                                 double* gdelta, double* gz, double* gB, double* gC, double* gA,
+                                 double* gD, double* gbias, double* gh0, int nthreads) {
     if (batch <= 0 || dim <= 0 || len <= 0 || dstate <= 0) return -2;
     if (in_dtype != ORC_F32 && in_dtype != ORC_BF16) return -4;
     if (!u || !delta || !B || !C || !A || !gy || !gu || !gdelta || !gB || !gC || !gA || !gD || !gbias)
         return -1;
     if (z && !gz) return -1;
     orc_args f = {batch, dim, len, dstate, in_dtype, u, delta, z, B, C, A, Dvec, delta_bias, h0,
-                  delta_softplus, 0, NULL, batch * dim, NULL, NULL};
+                  delta_softplus, zoh_b ? 1 : 0, NULL, batch * dim, NULL, NULL};
     const int64_t nrows = batch * dim;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > ORC_MAX_THREADS) nthreads = ORC_MAX_THREADS;
@@ -365,4 +387,17 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t dim, int64_t len, int64_t d
     }
     free(part);
     return ok ? 0 : -8;
+}
+
+/* The backward of the scan with Euler B. */
+int oracle_selective_scan_bwd(int64_t batch, int64_t dim, int64_t len, int64_t dstate, int in_dtype,
+                              const void* u, const void* delta, const void* z, const void* B,
+                              const void* C, const float* A, const float* Dvec,
+                              const float* delta_bias, const double* h0, int delta_softplus,
+                              const double* gy, const double* glast, double* gu, double* gdelta,
+                              double* gz, double* gB, double* gC, double* gA, double* gD,
+                              double* gbias, double* gh0, int nthreads) {
+    return oracle_selective_scan_bwd_ex(batch, dim, len, dstate, in_dtype, u, delta, z, B, C, A, Dvec,
+                                        delta_bias, h0, delta_softplus, 0, gy, glast, gu, gdelta, gz,
+                                        gB, gC, gA, gD, gbias, gh0, nthreads);
 }
