@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 13
+#define MAMBA_SCAN_ABI_VERSION 14
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -65,9 +65,9 @@ typedef enum mamba_scan_dtype {
 #define MAMBA_SCAN_RETURN_LAST_STATE (1u << 1) /* write last_state */
 /* B discretised by zero-order hold: the input term becomes (exp(dt*A[d,n]) - 1) / A[d,n] * B * u
  * (dt * B * u where A[d,n] = 0) instead of dt * B * u. "手把手用PyTorch实现Mamba的SSM层…" §2.1:
- * B_d = A^-1 (e^{A dt} - I) B, for a diagonal A. Forward only (mamba_scan_bwd rejects it). Run by
- * the lane-per-state kernels at dstate 16, 32 and 64 (ABI 9), the chunked kernel (ABI 11) and the
- * short-call kernel (ABI 12), else by the tiled or generic one. */
+ * B_d = A^-1 (e^{A dt} - I) B, for a diagonal A. Run by the lane-per-state kernels at dstate 16,
+ * 32 and 64 (ABI 9), the chunked kernel (ABI 11) and the short-call kernel (ABI 12), else by the
+ * tiled or generic one. The backward pass takes it from ABI 14 (see mamba_scan_bwd). */
 #define MAMBA_SCAN_ZOH_B (1u << 2)
 /* Save the state before every 16-step segment, for the backward pass: the forward writes
  * h before steps 0, 16, 32, ... of every (b, d) row to the workspace, laid out (batch, dim,
@@ -213,8 +213,12 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *    one, which also keeps fp32 copies of B and C; for few long rows the lane-per-state kernel
  *    splits the sequence into parts run side by side and keeps per-part partial sums of dA, dD,
  *    dbias and the adjoint handed from part to part).
- *  - Flags: MAMBA_SCAN_DELTA_SOFTPLUS, and at most one of the kernel choices (ABI 8;
- *    MAMBA_SCAN_ERR_ARGS for both or any other flag):
+ *  - Flags: MAMBA_SCAN_DELTA_SOFTPLUS, MAMBA_SCAN_ZOH_B (ABI 14: the gradients of the forward
+ *    with zero-order-hold B, where the input term's coefficient c = (exp(dt*A) - 1) / A replaces
+ *    dt in dB and du, its derivative exp(dt*A) enters ddelta, and dA gains
+ *    sum lam*B*u*dc/dA; run by the segment-tiled kernel, which recomputes the states: with
+ *    `checkpoints` or MAMBA_SCAN_FORCE_LANES, MAMBA_SCAN_ERR_UNSUPPORTED), and at most one of
+ *    the kernel choices (ABI 8; MAMBA_SCAN_ERR_ARGS for both or any other flag):
  *      MAMBA_SCAN_FORCE_LANES: the lane-per-state backward, one lane per (channel, state) as in
  *        the forward lane-per-state kernel, 16-step segments walked in reverse from the states
  *        saved every 16 steps (given, or written first by the forward launch that a call with

@@ -1,0 +1,13 @@
+// Launchers of the segment-tiled backward pass with B discretised by zero-order hold (its own
+// translation unit: the kernel's instantiations compile in parallel with the Euler ones).
+#include "launch.hpp"
+#include "scan_bwd.hpp"
+
+namespace mscan {
+
+int launch_bwd_tiled_zoh_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
+                             hipStream_t stream) {
+    return bf16 ? launch_bwd<bf16_t, true>(p, s, softplus, stream) : launch_bwd<float, true>(p, s, softplus, stream);
+}
+
+}  // namespace mscan

@@ -37,6 +37,8 @@ struct BwdReduceParams;
 // finished by the fixed-order reduction
 int launch_bwd_tiled_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
                          hipStream_t stream);
+int launch_bwd_tiled_zoh_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
+                             hipStream_t stream);
 int launch_bwd_ls_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
                       hipStream_t stream);
 int launch_bwd_reduce_any(const BwdReduceParams& r, hipStream_t stream);

@@ -21,7 +21,8 @@
 using namespace mscan;
 
 // flags the backward entry points take
-constexpr uint32_t kBwdFlags = MAMBA_SCAN_DELTA_SOFTPLUS | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_LANES;
+constexpr uint32_t kBwdFlags =
+    MAMBA_SCAN_DELTA_SOFTPLUS | MAMBA_SCAN_ZOH_B | MAMBA_SCAN_FORCE_TILED | MAMBA_SCAN_FORCE_LANES;
 
 namespace {
 
@@ -339,6 +340,8 @@ int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dty
     if (bad_shape(*s)) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
     if ((flags & MAMBA_SCAN_FORCE_LANES) && (flags & MAMBA_SCAN_FORCE_TILED)) return MAMBA_SCAN_ERR_ARGS;
+    // zero-order hold: the segment-tiled kernel, recomputing the states (no forward saves them)
+    if ((flags & MAMBA_SCAN_ZOH_B) && (flags & MAMBA_SCAN_SAVE_CHECKPOINTS)) return MAMBA_SCAN_ERR_UNSUPPORTED;
     if (s->batch * s->dim * s->len == 0) return 0;  // an empty call runs no scan
     const int pick = bwd_pick(*s, dtype == MAMBA_SCAN_BF16 ? 2 : 4, flags);
     if (pick < 0) return pick;
@@ -438,6 +441,7 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
         return rc;
     }
     const bool sp = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) != 0;
+    if (flags & MAMBA_SCAN_ZOH_B) return launch_bwd_tiled_zoh_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
     return lanes ? launch_bwd_ls_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs)
                  : launch_bwd_tiled_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
 }

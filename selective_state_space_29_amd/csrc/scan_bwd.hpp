@@ -10,6 +10,11 @@
 //   gp = dy g;  lam_t += gp C_t;  dC += gp h_t;  dB += lam dt u;  du = gp D + dt sum_n lam B
 //   ddt = sum_n lam (a h_{t-1} A + B u);  dA += lam a h_{t-1} dt;  ddelta = ddt softplus'(x)
 //   dz = dy p silu'(z);  dD += gp u;  dbias += ddelta;  then lam_{t-1} = a lam_t;  dh0 = lam.
+// With B discretised by zero-order hold ("手把手用PyTorch实现Mamba的SSM层…" §2.1, diagonal A) the
+// input term is c B u with c = (a - 1) / A (dt where A = 0) in place of dt B u. Then c replaces
+// dt in dB and du (du = gp D + sum_n lam c B), the term's derivative in dt is dc/ddt = a, so
+// ddt = sum_n lam a (h_{t-1} A + B u), and dA gains lam B u dc/dA (zoh_coef_dA_f); the adjoint
+// recurrence is unchanged.
 //
 // Decomposition (as the forward kernel): a workgroup owns 64 channels of one batch, one channel
 // per lane; wave w carries states w*S .. w*S+S-1 of the launch's block of at most 16 states
@@ -34,6 +39,7 @@
 #include "../../include/mamba_scan.h"
 #include "bwd_layout.hpp"
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace mscan {
 
@@ -76,7 +82,9 @@ __device__ __forceinline__ float load_el(const void* p, int64_t i) {
 
 // MULTI: one of several blocks of states (first / last read from the parameters); otherwise the
 // only block, with the sums over states finished in this launch.
-template <typename T, int S, bool SOFTPLUS, bool HAS_Z, bool EXACT, bool MULTI>
+// ZOH: B discretised by zero-order hold; the LDS factor F_DTU then holds u, the coefficient being
+// per state.
+template <typename T, int S, bool SOFTPLUS, bool HAS_Z, bool EXACT, bool MULTI, bool ZOH>
 __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
     constexpr int W = kBwdW, SEG = kBwdSeg, SUB = kBwdSub;
     constexpr int QS = SEG / W;      // prologue steps per thread
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
     // main role: this lane's channel, this wave's states
     const int64_t dm = d0 + lane;
     const bool mvalid = dm < p.dim;
-    float a2[S], Av[S], h[S], lam[S], gA[S];
+    float a2[S], Av[S], ian[S], h[S], lam[S], gA[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         Av[s] = 0.0f;
@@ -131,7 +139,14 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
             if (p.dlast) lam[s] = p.dlast[(b * p.dim + dm) * N + nbase + s];
         }
         a2[s] = Av[s] * kLog2e;
+        ian[s] = Av[s] != 0.0f ? 1.0f / Av[s] : 0.0f;
     }
+    // the input term of state s at step t: dt u B (Euler), or c u B with c the zero-order-hold
+    // coefficient (cu = u then); the forward tiled kernel's arithmetic
+    auto input_term = [&](int s, float dt, float cu, float a, float bb) __attribute__((always_inline)) {
+        if constexpr (ZOH) return zoh_coef_f(dt, dt * Av[s], a, ian[s]) * cu * bb;
+        return cu * bb;
+    };
     const float* Brow = p.bc + (b * N + nbase) * p.lp;              // state nbase + s at + s*lp
     const float* Crow = p.bc + ((p.batch + b) * N + nbase) * p.lp;
     const int64_t ckn = p.ckn;
@@ -172,7 +187,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
             if (t < L) {
                 const float x = r1.x[j] + pbias;
                 dt = SOFTPLUS ? softplus_f(x) : hw_exp2(x * kLog2e);
-                dtu = dt * r1.u[j];
+                dtu = ZOH ? r1.u[j] : dt * r1.u[j];
             }
             s_seg[F_DT][r * ROWP + QS * k8 + j] = dt;
             s_seg[F_DTU][r * ROWP + QS * k8 + j] = dtu;
@@ -194,7 +209,10 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                 const float dt = s_seg[F_DT][lane * ROWP + t];
                 const float dtu = s_seg[F_DTU][lane * ROWP + t];
 #pragma unroll
-                for (int s = 0; s < S; ++s) h[s] = __builtin_fmaf(hw_exp2(dt * a2[s]), h[s], dtu * bv[s][t]);
+                for (int s = 0; s < S; ++s) {
+                    const float a = hw_exp2(dt * a2[s]);
+                    h[s] = __builtin_fmaf(a, h[s], input_term(s, dt, dtu, a, bv[s][t]));
+                }
             }
         }
     }
@@ -234,7 +252,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                 } else {
                     dt = hw_exp2(x * kLog2e);
                 }
-                dtu = dt * uu;
+                dtu = ZOH ? uu : dt * uu;
                 if constexpr (HAS_Z) {
                     const float zz = r2.z[j];
                     const float sz = hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
@@ -284,7 +302,7 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
                 for (int t = 0; t < SEG; ++t) {
                     aseg[s][t] = hw_exp2(dtv[t] * a2[s]);
-                    hh = __builtin_fmaf(aseg[s][t], hh, dtuv[t] * bv[s][t]);
+                    hh = __builtin_fmaf(aseg[s][t], hh, input_term(s, dtv[t], dtuv[t], aseg[s][t], bv[s][t]));
                     hseg[s][t] = hh;
                 }
             }
@@ -308,12 +326,25 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                     for (int s = 0; s < S; ++s) {
                         lam[s] = __builtin_fmaf(gpv[t], cv[s][t], lam[s]);
                         gCc[s][tt] = gpv[t] * hseg[s][t];
-                        gBc[s][tt] = lam[s] * dtuv[t];
-                        P1 = __builtin_fmaf(lam[s], bv[s][t], P1);
                         const float hp = t > 0 ? hseg[s][t - 1] : hs[s];
-                        const float q = lam[s] * aseg[s][t] * hp;
-                        P2 = __builtin_fmaf(q, Av[s], P2);
-                        gA[s] = __builtin_fmaf(q, dtv[t], gA[s]);
+                        if constexpr (ZOH) {
+                            // P1 = sum lam c B (du), P2 = sum lam a (h_{t-1} A + B u) (ddt)
+                            const float x = dtv[t] * Av[s];
+                            const float cf = zoh_coef_f(dtv[t], x, aseg[s][t], ian[s]);
+                            const float lb = lam[s] * bv[s][t];
+                            gBc[s][tt] = lam[s] * (cf * dtuv[t]);
+                            P1 = __builtin_fmaf(lb, cf, P1);
+                            const float la = lam[s] * aseg[s][t];
+                            P2 = __builtin_fmaf(la, __builtin_fmaf(hp, Av[s], bv[s][t] * dtuv[t]), P2);
+                            gA[s] = __builtin_fmaf(la * hp, dtv[t], gA[s]);
+                            gA[s] = __builtin_fmaf(lb * dtuv[t], zoh_coef_dA_f(dtv[t], x, aseg[s][t], cf, ian[s]), gA[s]);
+                        } else {
+                            gBc[s][tt] = lam[s] * dtuv[t];
+                            P1 = __builtin_fmaf(lam[s], bv[s][t], P1);
+                            const float q = lam[s] * aseg[s][t] * hp;
+                            P2 = __builtin_fmaf(q, Av[s], P2);
+                            gA[s] = __builtin_fmaf(q, dtv[t], gA[s]);
+                        }
                         Y = __builtin_fmaf(cv[s][t], hseg[s][t], Y);
                         lam[s] *= aseg[s][t];
                     }
@@ -345,11 +376,11 @@ __global__ __launch_bounds__(64 * kBwdW) void scan_bwd_kernel(BwdParams p) {
                 }
                 const int o = r * ROWP + half * SUB + tt;
                 const float dt = s_seg[F_DT][o], gp = s_seg[F_GP][o], uu = s_seg[F_U][o];
-                const float gdt = __builtin_fmaf(uu, P1, P2);
+                const float gdt = ZOH ? P2 : __builtin_fmaf(uu, P1, P2);
                 const float gx = SOFTPLUS ? gdt * s_seg[F_SG][o] : gdt * dt;
                 if (pvalid && t < L) {
                     // this block's share; earlier blocks' shares are already in the outputs
-                    float gu = dt * P1, gxs = gx, ys = Y;
+                    float gu = ZOH ? P1 : dt * P1, gxs = gx, ys = Y;
                     if (first) {
                         gu = __builtin_fmaf(gp, pskip, gu);
                         gDacc = __builtin_fmaf(gp, uu, gDacc);
@@ -439,102 +470,37 @@ __global__ __launch_bounds__(256) void bwd_bc_widen_kernel(const void* B, const 
     out[i] = t < len ? load_el<T>(q ? C : B, rr * len + t) : 0.0f;
 }
 
-// Fixed-order sums of the partials: dB, dC over channel groups (4 steps per thread, 16-byte loads
-// of the partials, groups added in order); dA, dD, dbias over the batch.
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdReduceParams p) {
-    const int64_t lp4 = p.lp / 4;
-    const int64_t nbc4 = p.batch * p.dstate * lp4;  // 4-step columns per output tensor
-    const int64_t na = p.dim * p.dstate;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < 2 * nbc4) {
-        const int64_t q = i / nbc4, j = i - q * nbc4;
-        const int64_t row = j / lp4;  // b * dstate + n
-        const int64_t t = (j - row * lp4) * 4;
-        const int64_t b = row / p.dstate, n = row - b * p.dstate;
-        const float* src = p.bcpart + ((b * 2 + q) * p.dstate + n) * p.lp + t;
-        const int64_t gs = p.batch * 2 * p.dstate * p.lp;  // floats between channel groups
-        // the partials are read once: nontemporal loads (461 -> 455 us per backward call at the
-        // Mamba-130m shape, with the full-row float4 stores below)
-        typedef float nt_f4 __attribute__((ext_vector_type(4)));
-        const nt_f4 a0 = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(src));
-        float4 acc = make_float4(a0.x, a0.y, a0.z, a0.w);
-#pragma unroll 8
-        for (int64_t g = 1; g < p.groups; ++g) {
-            const nt_f4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(src + g * gs));
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
-        }
-        float* dst = (q ? p.dC : p.dB) + row * p.len + t;
-        const float a[4] = {acc.x, acc.y, acc.z, acc.w};
-        if (t + 4 <= p.len && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-            *reinterpret_cast<float4*>(dst) = acc;
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (t + k < p.len) dst[k] = a[k];
-        }
-    } else if (i < 2 * nbc4 + na) {
-        // over the batch, and within a batch over the sequence parts in order
-        const int64_t j = i - 2 * nbc4;
-        float acc = 0.0f;
-        for (int64_t b = 0; b < p.batch; ++b)
-            for (int64_t q = 0; q < p.parts; ++q) acc += p.apart[(q * p.batch + b) * na + j];
-        p.dA[j] = acc;
-    } else if (i < 2 * nbc4 + na + p.dim) {
-        const int64_t d = i - 2 * nbc4 - na;
-        float accd = 0.0f, accb = 0.0f;
-        for (int64_t b = 0; b < p.batch; ++b)
-            for (int64_t q = 0; q < p.parts; ++q) {
-                accd += p.dpart[(q * p.batch + b) * p.dim + d];
-                accb += p.bpart[(q * p.batch + b) * p.dim + d];
-            }
-        if (p.dD) p.dD[d] = accd;
-        if (p.dbias) p.dbias[d] = accb;
-    }
-}
-
 // ---------------------------------------------------------------------------------------------
 // host side
 
-inline int launch_bwd_reduce(const BwdReduceParams& r, hipStream_t stream) {
-    const int64_t nred = 2 * r.batch * r.dstate * (r.lp / 4) + r.dim * r.dstate + r.dim;
-    void* rargs[] = {const_cast<BwdReduceParams*>(&r)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_reduce_kernel), dim3((unsigned)((nred + 255) / 256)),
-                           dim3(256), rargs, 0, stream) == hipSuccess
-               ? MAMBA_SCAN_OK
-               : MAMBA_SCAN_ERR_LAUNCH;
-}
-
 inline int bwd_states_per_wave(int64_t nb) { return nb <= 8 ? 1 : 2; }
 
-template <typename T, int S, bool SP, bool HZ>
+template <typename T, int S, bool SP, bool HZ, bool ZOH>
 int launch_bwd_cfg(const BwdParams& q, hipStream_t stream) {
     void* args[] = {const_cast<BwdParams*>(&q)};
     const bool exact = q.nb == (int64_t)S * kBwdW;
     const bool multi = !(q.first && q.last);
     const void* fn =
-        multi ? (exact ? reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, true, true>)
-                       : reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, false, true>))
-              : (exact ? reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, true, false>)
-                       : reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, false, false>));
+        multi ? (exact ? reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, true, true, ZOH>)
+                       : reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, false, true, ZOH>))
+              : (exact ? reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, true, false, ZOH>)
+                       : reinterpret_cast<const void*>(&scan_bwd_kernel<T, S, SP, HZ, false, false, ZOH>));
     return hipLaunchKernel(fn, dim3((unsigned)(q.batch * q.groups)), dim3(64 * kBwdW), args, 0, stream) ==
                    hipSuccess
                ? MAMBA_SCAN_OK
                : MAMBA_SCAN_ERR_LAUNCH;
 }
 
-template <typename T, int S>
+template <typename T, int S, bool ZOH>
 int launch_bwd_s(const BwdParams& q, bool softplus, hipStream_t stream) {
     const bool hz = q.z != nullptr;
-    if (softplus && hz) return launch_bwd_cfg<T, S, true, true>(q, stream);
-    if (softplus) return launch_bwd_cfg<T, S, true, false>(q, stream);
-    if (hz) return launch_bwd_cfg<T, S, false, true>(q, stream);
-    return launch_bwd_cfg<T, S, false, false>(q, stream);
+    if (softplus && hz) return launch_bwd_cfg<T, S, true, true, ZOH>(q, stream);
+    if (softplus) return launch_bwd_cfg<T, S, true, false, ZOH>(q, stream);
+    if (hz) return launch_bwd_cfg<T, S, false, true, ZOH>(q, stream);
+    return launch_bwd_cfg<T, S, false, false, ZOH>(q, stream);
 }
 
-template <typename T>
+template <typename T, bool ZOH>
 int launch_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool softplus, hipStream_t stream) {
     const BwdLayout l = bwd_layout(s, p->checkpoints != nullptr);
     char* ws = static_cast<char*>(p->workspace);
@@ -586,8 +552,8 @@ int launch_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool sof
         q.nb = bwd_next_block(s.dstate - n0);
         q.first = n0 == 0;
         q.last = n0 + q.nb == s.dstate;
-        const int rc = bwd_states_per_wave(q.nb) == 1 ? launch_bwd_s<T, 1>(q, softplus, stream)
-                                                       : launch_bwd_s<T, 2>(q, softplus, stream);
+        const int rc = bwd_states_per_wave(q.nb) == 1 ? launch_bwd_s<T, 1, ZOH>(q, softplus, stream)
+                                                       : launch_bwd_s<T, 2, ZOH>(q, softplus, stream);
         if (rc != MAMBA_SCAN_OK) return rc;
     }
     BwdReduceParams r;
@@ -606,7 +572,7 @@ int launch_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool sof
     r.dstate = s.dstate;
     r.lp = l.lp;
     r.groups = l.groups;
-    return launch_bwd_reduce(r, stream);
+    return launch_bwd_reduce_any(r, stream);
 }
 
 }  // namespace mscan

@@ -299,7 +299,7 @@ def _check_checkpoints(ck, batch, dim, L, N, dev):
 
 def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False,
                        h0=None, dlast_state=None, want_dh0=True, checkpoints=None, static_scratch=False,
-                       kernel=None):
+                       kernel=None, zoh_b=False):
     """Gradients of the scan (``mamba_scan_bwd``) for incoming gradients dy (batch, dim, L) and,
     optionally, dlast_state (batch, dim, N). Inputs as for ``selective_scan_fn``; all tensors are
     made contiguous first. Returns a dict of fp32 gradients: u, delta, B, C, A, and z, D,
@@ -310,6 +310,8 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     workspace is allocated here; calls overlapping in time on one GPU must not be made).
     ``kernel``: None (the library's choice: the lane-per-state kernel at 16, 32 and 64 states,
     else the segment-tiled one), "lanes" or "tiled" (forced; an error where it cannot run).
+    ``zoh_b``: the gradients of the forward with B discretised by zero-order hold (the
+    segment-tiled kernel, recomputing the states: no ``checkpoints``, no ``kernel="lanes"``).
     """
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):
@@ -352,7 +354,7 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
         g["h0"] = torch.empty((batch, dim, N), **f32)
     shape = Shape(batch, dim, L, N)
     dtype = BF16 if u.dtype == torch.bfloat16 else F32
-    flags = DELTA_SOFTPLUS if delta_softplus else 0
+    flags = (DELTA_SOFTPLUS if delta_softplus else 0) | (ZOH_B if zoh_b else 0)
     if kernel not in (None, "lanes", "tiled"):
         raise ValueError(f"unknown backward kernel {kernel!r}: None, 'lanes' or 'tiled'")
     flags |= {None: 0, "lanes": FORCE_LANES, "tiled": FORCE_TILED}[kernel]
@@ -392,10 +394,12 @@ class SelectiveScan(torch.autograd.Function):
     """
 
     @staticmethod
-    def forward(ctx, u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus):
-        kw = dict(D=D, z=z, delta_bias=delta_bias, delta_softplus=delta_softplus, return_last_state=True, h0=h0)
+    def forward(ctx, u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, zoh_b):
+        kw = dict(D=D, z=z, delta_bias=delta_bias, delta_softplus=delta_softplus, return_last_state=True, h0=h0,
+                  zoh_b=zoh_b)
         ck = None
-        if A.shape[1] in (16, 32, 64) and u.dtype in (torch.float32, torch.bfloat16):
+        # the zero-order-hold backward recomputes the states: none are saved for it
+        if not zoh_b and A.shape[1] in (16, 32, 64) and u.dtype in (torch.float32, torch.bfloat16):
             ck = torch.empty(checkpoint_shape(*u.shape, A.shape[1]), dtype=torch.float32, device=u.device)
             try:
                 y, ls = selective_scan_fn(u, delta, A, B, C, checkpoints_out=ck, **kw)
@@ -407,6 +411,7 @@ class SelectiveScan(torch.autograd.Function):
             y, ls = selective_scan_fn(u, delta, A, B, C, **kw)
         ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0, ck)
         ctx.delta_softplus = delta_softplus
+        ctx.zoh_b = zoh_b
         return y, ls
 
     @staticmethod
@@ -416,17 +421,18 @@ class SelectiveScan(torch.autograd.Function):
             gy = torch.zeros(u.shape, dtype=torch.float32, device=u.device)
         g = selective_scan_bwd(u, delta, A, B, C, gy, D=D, z=z, delta_bias=delta_bias,
                                delta_softplus=ctx.delta_softplus, h0=h0, dlast_state=gls,
-                               want_dh0=h0 is not None and ctx.needs_input_grad[8], checkpoints=ck)
+                               want_dh0=h0 is not None and ctx.needs_input_grad[8], checkpoints=ck,
+                               zoh_b=ctx.zoh_b)
 
         def cast(name, like):
             return None if like is None or name not in g else g[name].to(like.dtype)
 
         return (cast("u", u), cast("delta", delta), cast("A", A), cast("B", B), cast("C", C),
-                cast("D", D), cast("z", z), cast("delta_bias", delta_bias), cast("h0", h0), None)
+                cast("D", D), cast("z", z), cast("delta_bias", delta_bias), cast("h0", h0), None, None)
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
-                   return_last_state=False, h0=None):
+                   return_last_state=False, h0=None, zoh_b=False):
     """Differentiable form of ``selective_scan_fn`` (torch autograd through the HIP backward).
     When no gradient can flow (grad mode off, or no input requires one) it is the plain forward:
     no states are saved for a backward that will not run."""
@@ -434,8 +440,8 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     if not (torch.is_grad_enabled() and any(t is not None and t.requires_grad for t in inputs)):
         return selective_scan_fn(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
                                  delta_softplus=delta_softplus, return_last_state=return_last_state,
-                                 h0=h0)
-    y, ls = SelectiveScan.apply(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus)
+                                 h0=h0, zoh_b=zoh_b)
+    y, ls = SelectiveScan.apply(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, zoh_b)
     return (y, ls) if return_last_state else y
 
 

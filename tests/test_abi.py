@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 13
+    assert scan.load_library().mamba_scan_abi_version() == 14
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -274,7 +274,12 @@ BWD_CASES = [
     ("both_kernels_forced", lambda c: c.__setitem__("flags", scan.FORCE_TILED | scan.FORCE_LANES), -6),
     ("lanes_forced_at_8_states",
      lambda c: (c.__setitem__("flags", scan.FORCE_LANES), setattr(c["shape"], "dstate", 8)), -8),
-    ("zoh_not_in_backward", lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.ZOH_B), -6),
+    # zero-order hold: the segment-tiled kernel only, which recomputes the states
+    ("zoh_with_checkpoints", lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.ZOH_B), -8),
+    ("zoh_with_lanes_forced", lambda c: (c.__setitem__("flags", scan.ZOH_B | scan.FORCE_LANES),
+                                         setattr(c["ptrs"], "checkpoints", None)), -8),
+    ("zoh_unknown_flag", lambda c: (c.__setitem__("flags", scan.ZOH_B | (1 << 13)),
+                                    setattr(c["ptrs"], "checkpoints", None)), -6),
     ("bad_dtype", lambda c: c.__setitem__("dtype", 7), -4),
     ("negative_len", _set("shape", "len", -1), -2),
     ("zero_dstate", _set("shape", "dstate", 0), -2),

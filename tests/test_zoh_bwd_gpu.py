@@ -1,0 +1,171 @@
+"""GPU parity of the backward pass with zero-order-hold B (``mamba_scan_bwd`` with
+MAMBA_SCAN_ZOH_B, the segment-tiled kernel) against the fp64 backward oracle with ``zoh_b=True``
+on identical inputs.
+
+Bars as for the Euler backward: max|g - r| / (1 + |r|) <= 1e-4 for fp32 inputs, <= 2e-3 for
+bf16 inputs. The coefficient c = (e^{dt A} - 1) / A is within 2^-20 relative of the exact one
+(zoh_coef_f) and its derivative in A within about 2^-19 (zoh_coef_dA_f: a series below
+|dt A| = 1/4, the closed form with a cancellation factor of at most 8 above), far inside the
+bars; the rest is the Euler backward's fp32 accumulation.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+import oracle
+from selective_state_space_29_amd import scan, workloads
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("u", "delta", "z", "B", "C", "A", "D", "delta_bias", "h0")
+
+
+def _grads_gpu(x, dy, dlast, softplus, h0, kernel=None):
+    g = {k: gu.to_dev(v) if isinstance(v, np.ndarray) else v for k, v in x.items()}
+    out = scan.selective_scan_bwd(
+        g["u"], g["delta"], g["A"], g["B"], g["C"], gu.to_dev(dy), D=g.get("D"), z=g.get("z"),
+        delta_bias=g.get("delta_bias"), delta_softplus=softplus,
+        h0=None if h0 is None else gu.to_dev(h0), dlast_state=None if dlast is None else gu.to_dev(dlast),
+        want_dh0=True, kernel=kernel, zoh_b=True)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def _check(x, tol, softplus=True, with_h0=False, with_dlast=True, seed=0, kernel=None):
+    batch, dim, L = x["u"].shape
+    N = x["A"].shape[1]
+    rng = np.random.default_rng(seed)
+    dy = rng.standard_normal((batch, dim, L)).astype(np.float32)
+    dlast = rng.standard_normal((batch, dim, N)).astype(np.float32) if with_dlast else None
+    h0 = rng.standard_normal((batch, dim, N)).astype(np.float32) if with_h0 else None
+    gg = _grads_gpu(x, dy, dlast, softplus, h0, kernel)
+    gr = oracle.selective_scan_bwd(
+        x["u"], x["delta"], x["A"], x["B"], x["C"], dy.astype(np.float64), D=x.get("D"), z=x.get("z"),
+        delta_bias=x.get("delta_bias"), delta_softplus=softplus,
+        h0=None if h0 is None else h0.astype(np.float64),
+        glast=None if dlast is None else dlast.astype(np.float64), zoh_b=True)
+    for k in NAMES:
+        if k not in gr or (k != "h0" and x.get(k) is None):
+            continue
+        assert np.all(np.isfinite(gg[k])), k
+        err = gu.rel_err(gg[k], gr[k])
+        print(f"  d{k}: max rel err {err:.3e} (bar {tol:g})", flush=True)
+        assert err <= tol, f"d{k}: max rel err {err:.3g}"
+    return gg
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_zoh_backward_workload_parity(wid):
+    """Workloads 1-3 in full (workload 1: 32 states, two blocks of 16)."""
+    w = workloads.WORKLOADS[wid]
+    print(f"zoh backward parity, workload {wid}: {w.name}", flush=True)
+    _check(workloads.make_inputs(w), 1e-4 if w.dtype == "f32" else 2e-3, softplus=w.softplus,
+           with_dlast=w.last_state, seed=wid)
+
+
+def _a(kind, dim, N, rng):
+    if kind == "zeros_mixed":  # every third state has A = 0 (pure integration)
+        A = (-rng.uniform(0.05, 4.0, (dim, N))).astype(np.float32)
+        A[:, ::3] = 0.0
+        return A
+    if kind == "tiny":  # |dt A| far below both series thresholds
+        return (-rng.uniform(1e-5, 1e-3, (dim, N))).astype(np.float32)
+    if kind == "straddle":  # |dt A| on both sides of 1/16 and 1/4 for the workloads' dt
+        return (-np.exp(rng.uniform(np.log(0.05), np.log(30.0), (dim, N)))).astype(np.float32)
+    if kind == "positive":
+        # growing states: A > 0 on every fourth state, small enough that over the case's steps
+        # (with the bias, sum dt ~ 20) they grow by e^2 at most. Growth of e^30 (no bias, A up to
+        # 0.3) makes the sums over states ill-conditioned: a few huge terms of random sign that
+        # cancel to well below their size, where fp32 terms leave errors of 7e-4 of the result
+        # in either discretisation.
+        A = (-rng.uniform(0.05, 4.0, (dim, N))).astype(np.float32)
+        A[:, 1::4] = rng.uniform(0.01, 0.1, A[:, 1::4].shape).astype(np.float32)
+        return A
+    return None
+
+
+EDGE = [
+    # (batch, dim, N, L, dtype, a_kind, h0, softplus, z, D, bias)
+    (2, 64, 16, 64, "f32", "mamba", False, True, True, True, True),
+    (2, 80, 16, 37, "bf16", "rand", True, True, True, True, True),
+    (1, 70, 4, 40, "f32", "zeros_mixed", False, True, True, True, True),
+    (2, 64, 12, 100, "f32", "tiny", True, True, True, True, True),
+    (1, 64, 32, 48, "bf16", "straddle", False, True, True, True, True),
+    (1, 33, 64, 33, "f32", "rand", True, True, False, True, True),
+    (1, 40, 100, 23, "f32", "zeros_mixed", False, True, True, False, True),
+    (2, 64, 16, 17, "f32", "straddle", True, False, True, True, True),   # exp mode
+    (2, 65, 16, 130, "f32", "positive", False, True, True, True, True),
+    (1, 8, 16, 1, "f32", "rand", True, True, True, True, True),
+    (3, 130, 24, 50, "bf16", "mamba", False, True, False, False, False),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(EDGE)))
+def test_zoh_backward_edge_cases(idx):
+    """N from 4 to 100 (one to seven blocks of 16), L from 1 to 130 across segment boundaries,
+    channels leaving the 64-channel groups partly empty, A with zero states, tiny |dt A|, |dt A|
+    on both sides of the series thresholds, A > 0 on some states, h0, exp mode, and each optional
+    input (z, D, bias) off."""
+    batch, dim, N, L, dtype, a_kind, with_h0, softplus, hz, hd, hb = EDGE[idx]
+    print(f"zoh backward edge case {EDGE[idx]}", flush=True)
+    rng = np.random.default_rng(800 + idx)
+    x = gu.case(800 + idx, batch, dim, N, L, dtype=dtype, z=hz, D=hd, bias=hb,
+                a_kind="mamba" if a_kind == "mamba" else "rand")
+    A = _a(a_kind, dim, N, rng)
+    if A is not None:
+        x["A"] = A
+    _check(x, 1e-4 if dtype == "f32" else 2e-3, softplus=softplus, with_h0=with_h0, seed=idx,
+           kernel="tiled" if idx % 2 else None)
+
+
+def test_zoh_backward_refusals():
+    """The lane-per-state backward does not take the zero-order hold, nor do saved states."""
+    x = gu.case(830, 1, 16, 16, 32, dtype="f32")
+    g = {k: gu.to_dev(v) if isinstance(v, np.ndarray) else v for k, v in x.items()}
+    dy = torch.ones((1, 16, 32), device="cuda:0")
+    with pytest.raises(ValueError):
+        scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"], z=g["z"],
+                                delta_bias=g["delta_bias"], delta_softplus=True, kernel="lanes", zoh_b=True)
+    ck = torch.zeros(scan.checkpoint_shape(1, 16, 32, 16), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ValueError):
+        scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"], z=g["z"],
+                                delta_bias=g["delta_bias"], delta_softplus=True, checkpoints=ck, zoh_b=True)
+
+
+def test_zoh_backward_is_deterministic():
+    x = gu.case(840, 2, 96, 16, 200, dtype="bf16", a_kind="rand")
+    rng = np.random.default_rng(7)
+    dy = rng.standard_normal((2, 96, 200)).astype(np.float32)
+    dl = rng.standard_normal((2, 96, 16)).astype(np.float32)
+    a = _grads_gpu(x, dy, dl, True, None)
+    b = _grads_gpu(x, dy, dl, True, None)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_zoh_autograd_matches_the_backward_entry():
+    """torch autograd through selective_scan(zoh_b=True): the forward runs the zero-order-hold
+    scan, saves no states, and the gradients are the backward entry's bits."""
+    x = gu.case(850, 2, 64, 16, 80, dtype="f32", a_kind="rand")
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev).requires_grad_(True) for k, v in x.items() if v is not None}
+    h0 = torch.randn((2, 64, 16), device=dev, generator=torch.Generator(dev).manual_seed(3)).requires_grad_(True)
+    y, ls = scan.selective_scan(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                delta_bias=t["delta_bias"], delta_softplus=True, return_last_state=True,
+                                h0=h0, zoh_b=True)
+    yf, lf = scan.selective_scan_fn(*(t[k].detach() for k in ("u", "delta", "A", "B", "C")), D=t["D"].detach(),
+                                    z=t["z"].detach(), delta_bias=t["delta_bias"].detach(), delta_softplus=True,
+                                    return_last_state=True, h0=h0.detach(), zoh_b=True)
+    assert torch.equal(y.detach(), yf) and torch.equal(ls.detach(), lf)
+    gy = torch.randn_like(y)
+    gl = torch.randn_like(ls)
+    torch.autograd.backward((y, ls), (gy, gl))
+    ref = scan.selective_scan_bwd(*(t[k].detach() for k in ("u", "delta", "A", "B", "C")), gy, D=t["D"].detach(),
+                                  z=t["z"].detach(), delta_bias=t["delta_bias"].detach(), delta_softplus=True,
+                                  h0=h0.detach(), dlast_state=gl, want_dh0=True, zoh_b=True)
+    torch.cuda.synchronize()
+    for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias"):
+        assert torch.equal(t[k].grad, ref[k]), k
+    assert torch.equal(h0.grad, ref["h0"])
