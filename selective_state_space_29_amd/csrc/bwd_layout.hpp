@@ -87,7 +87,6 @@ inline bool bwd_ls_fits(const mamba_scan_shape& s, int64_t es) {
 inline int bwd_pick(const mamba_scan_shape& s, int64_t es, uint32_t flags) {
     const bool fl = (flags & MAMBA_SCAN_FORCE_LANES) != 0, ft = (flags & MAMBA_SCAN_FORCE_TILED) != 0;
     if (fl && ft) return MAMBA_SCAN_ERR_ARGS;
-    if (flags & MAMBA_SCAN_ZOH_B) return fl ? MAMBA_SCAN_ERR_UNSUPPORTED : 0;  // segment-tiled only
     if (ft) return 0;
     const bool ok = bwd_ls_fits(s, es);
     if (fl && !ok) return MAMBA_SCAN_ERR_UNSUPPORTED;

@@ -343,7 +343,8 @@ int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dty
     // zero-order hold: the segment-tiled kernel, recomputing the states (no forward saves them)
     if ((flags & MAMBA_SCAN_ZOH_B) && (flags & MAMBA_SCAN_SAVE_CHECKPOINTS)) return MAMBA_SCAN_ERR_UNSUPPORTED;
     if (s->batch * s->dim * s->len == 0) return 0;  // an empty call runs no scan
-    const int pick = bwd_pick(*s, dtype == MAMBA_SCAN_BF16 ? 2 : 4, flags);
+    if ((flags & MAMBA_SCAN_ZOH_B) && (flags & MAMBA_SCAN_FORCE_LANES)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+    const int pick = (flags & MAMBA_SCAN_ZOH_B) ? 0 : bwd_pick(*s, dtype == MAMBA_SCAN_BF16 ? 2 : 4, flags);
     if (pick < 0) return pick;
     const bool given_ck = (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) != 0;
     return pick ? bwd_ls_layout(*s, given_ck).total : bwd_layout(*s, given_ck).total;
@@ -397,7 +398,8 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     if (reinterpret_cast<uintptr_t>(p->workspace) % 256 != 0) return MAMBA_SCAN_ERR_ARGS;
     if (reinterpret_cast<uintptr_t>(p->checkpoints) % 4 != 0) return MAMBA_SCAN_ERR_ARGS;
     const int64_t es = dtype == MAMBA_SCAN_BF16 ? 2 : 4;
-    const bool lanes = bwd_pick(*s, es, flags) == 1;  // an error was returned by the size query
+    // (an error was returned by the size query)
+    const bool lanes = !(flags & MAMBA_SCAN_ZOH_B) && bwd_pick(*s, es, flags) == 1;
     if (!lanes && s->batch * ((s->dim + 63) / 64) > 0x7fffffff) return MAMBA_SCAN_ERR_UNSUPPORTED;
 
     const int64_t DL = s->batch * s->dim * s->len, NL = s->batch * s->dstate * s->len;

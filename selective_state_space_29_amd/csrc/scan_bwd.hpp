@@ -75,6 +75,23 @@ constexpr int kBwdSub = 8;   // steps per LDS exchange
 
 typedef const __attribute__((address_space(4))) float* bwd_cptrf;
 
+// Derivative of the zero-order-hold coefficient c = (e^{dt A} - 1) / A with respect to A, given
+// x = dt * A, dA = e^x, c (from zoh_coef_f) and invA = 1 / A (0 where A = 0): (dt dA - c) / A,
+// whose limit at A = 0 is dt^2 / 2. For |x| < 1/4 the Taylor series of the same function,
+// dt^2 (1/2 + x/3 + x^2/8 + x^3/30 + x^4/144 + x^5/840) (the first dropped term, x^6 / 5760, is
+// below 1e-7 of the sum there), so that two nearly equal terms are never subtracted; above it
+// the closed form, whose cancellation costs at most a factor 2/|x| = 8 on the rounding of its
+// terms. The derivative with respect to dt is dA itself.
+__device__ __forceinline__ float zoh_coef_dA_f(float dt, float x, float dA, float c, float invA) {
+    const float p = __builtin_fmaf(
+        x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 840.0f, 1.0f / 144.0f), 1.0f / 30.0f), 0.125f),
+                          1.0f / 3.0f),
+        0.5f);
+    const float small = dt * dt * p;
+    const float big = __builtin_fmaf(dt, dA, -c) * invA;
+    return __builtin_fabsf(x) < 0.25f ? small : big;
+}
+
 template <typename T>
 __device__ __forceinline__ float load_el(const void* p, int64_t i) {
     return to_f32(static_cast<const T*>(p)[i]);
