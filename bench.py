@@ -543,8 +543,11 @@ def backward_bench(args):
 
     bwd_kernel = None if args.bwd_kernel == "auto" else args.bwd_kernel
     # the kernel that runs: the library's default is the lane-per-state one at 16, 32 and 64
-    # states (every workload here is within its offset limits)
-    bwd_kname = bwd_kernel or ("lanes" if w.dstate in (16, 32, 64) else "tiled")
+    # states (every workload here is within its offset limits); with the zero-order hold the
+    # segment-tiled one, recomputing the states
+    bwd_kname = bwd_kernel or ("lanes" if w.dstate in (16, 32, 64) and not args.zoh else "tiled")
+    if args.zoh and (args.checkpoints or bwd_kname != "tiled"):
+        raise SystemExit("--backward --zoh runs the segment-tiled kernel without saved states")
     ck, fwd_ck = None, None
     if args.checkpoints:
         # the forward that saves the segment states, graph-timed like the forward bench, then
@@ -569,7 +572,7 @@ def backward_bench(args):
         return scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"],
                                        z=g["z"], delta_bias=g["delta_bias"],
                                        delta_softplus=w.softplus, dlast_state=dl, want_dh0=False,
-                                       checkpoints=ck, kernel=bwd_kernel)
+                                       checkpoints=ck, kernel=bwd_kernel, zoh_b=args.zoh)
 
     # warm-up: the given calls, then sustained calls for WARM_MS, as for the forward's timed
     # replays (the clocks settle under the backward's own load)
@@ -599,11 +602,11 @@ def backward_bench(args):
         ref = oracle.selective_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"],
                                         dy_np.astype(np.float64), D=x["D"], z=x["z"],
                                         delta_bias=x["delta_bias"], delta_softplus=w.softplus,
-                                        glast=dl_np.astype(np.float64))
+                                        glast=dl_np.astype(np.float64), zoh_b=args.zoh)
         for k, v in out.items():
             r = ref[k]
             errs[k] = float(np.max(np.abs(v.cpu().numpy() - r) / (1 + np.abs(r))))
-    else:
+    elif not args.zoh:
         errs = backward_sampled_parity(w, out, dy_np, dl_np)
 
     es = 2 if w.dtype == "bf16" else 4
@@ -645,10 +648,10 @@ def backward_bench(args):
         "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name + ("-backward-from-checkpoints" if ck is not None else "-backward"),
                    "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
-                   "seq_len": w.seqlen, "storage": w.dtype, "kernel": bwd_kname},
+                   "seq_len": w.seqlen, "storage": w.dtype, "kernel": bwd_kname, "zoh_b": bool(args.zoh)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": read + written,
-                     "traffic": measured_bwd_traffic(w, ck is not None, bwd_kname),
+                     "traffic": None if args.zoh else measured_bwd_traffic(w, ck is not None, bwd_kname),
                      "mean_call_us": round(mean_us, 2), "min_call_us": round(float(per_us.min()), 2),
                      "valu_issue_slots": {"per_call": bwd_slots, "slot_equivalent_TFLOP_s": round(bwd_tflops, 2),
                                           "peak_TFLOP_s": VALU_PEAK_TFLOPS,
@@ -657,6 +660,8 @@ def backward_bench(args):
     }
     if fwd_ck is not None:
         res["forward_saving_checkpoints"] = fwd_ck
+    if args.zoh:  # the slot model counts the Euler backward's operations
+        res["roofline"]["valu_issue_slots"] = None
     print(json.dumps(res), flush=True)
 
 

@@ -566,11 +566,22 @@ int launch_bwd(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool sof
     for (int64_t n0 = 0; n0 < s.dstate; n0 += q.nb) {
         q.n0 = n0;
         q.ck_n0 = q.have_ck ? n0 : 0;
-        q.nb = bwd_next_block(s.dstate - n0);
-        q.first = n0 == 0;
-        q.last = n0 + q.nb == s.dstate;
-        const int rc = bwd_states_per_wave(q.nb) == 1 ? launch_bwd_s<T, 1, ZOH>(q, softplus, stream)
-                                                       : launch_bwd_s<T, 2, ZOH>(q, softplus, stream);
+        int rc;
+        if constexpr (ZOH) {
+            // one state per wave, blocks of at most 8 states: with two, the coefficient and its
+            // derivatives push the kernel past 256 VGPRs and about 100 of them spill to scratch
+            // (3.8 ms per call at the Mamba-130m shape)
+            q.nb = s.dstate - n0 > 8 ? 8 : s.dstate - n0;
+            q.first = n0 == 0;
+            q.last = n0 + q.nb == s.dstate;
+            rc = launch_bwd_s<T, 1, true>(q, softplus, stream);
+        } else {
+            q.nb = bwd_next_block(s.dstate - n0);
+            q.first = n0 == 0;
+            q.last = n0 + q.nb == s.dstate;
+            rc = bwd_states_per_wave(q.nb) == 1 ? launch_bwd_s<T, 1, false>(q, softplus, stream)
+                                                : launch_bwd_s<T, 2, false>(q, softplus, stream);
+        }
         if (rc != MAMBA_SCAN_OK) return rc;
     }
     BwdReduceParams r;
