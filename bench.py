@@ -65,6 +65,8 @@ BWD_TRAFFIC_RECORDS = {
                       ("common.hpp", "scan_bwd.hpp")),
     ("lanes", False): _BWD_LS,
     ("lanes", True): _BWD_LS,
+    ("tiled-zoh", False): (os.path.join(ROOT, "profiles", "scan_bwd_zoh_mamba130m_traffic.json"),
+                           ("common.hpp", "scan_bwd.hpp")),
 }
 RATES_LIB = os.path.join(ROOT, "selective_state_space_29_amd", "probe", "libmscan_rates.so")
 # the sources each forward kernel is built from (a profile or counter record names their hash)
@@ -189,7 +191,8 @@ def measured_bwd_traffic(w, from_checkpoints, kernel="lanes"):
         return None
     if rec.get("source_sha256") != kernel_source_hash(key, BWD_TRAFFIC_RECORDS):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    # per call: the zero-order-hold backward launches its scan kernel once per block of 8 states
+    return rec.get("traffic_bytes_per_launch") * rec.get("launches_per_call", 1)
 
 
 def graph_timed(fn, steps, warmup, stream, reps=5, warm_reps=1, warm_ms=0.0):
@@ -651,7 +654,7 @@ def backward_bench(args):
                    "seq_len": w.seqlen, "storage": w.dtype, "kernel": bwd_kname, "zoh_b": bool(args.zoh)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": read + written,
-                     "traffic": None if args.zoh else measured_bwd_traffic(w, ck is not None, bwd_kname),
+                     "traffic": measured_bwd_traffic(w, ck is not None, "tiled-zoh" if args.zoh else bwd_kname),
                      "mean_call_us": round(mean_us, 2), "min_call_us": round(float(per_us.min()), 2),
                      "valu_issue_slots": {"per_call": bwd_slots, "slot_equivalent_TFLOP_s": round(bwd_tflops, 2),
                                           "peak_TFLOP_s": VALU_PEAK_TFLOPS,
