@@ -546,11 +546,8 @@ def backward_bench(args):
 
     bwd_kernel = None if args.bwd_kernel == "auto" else args.bwd_kernel
     # the kernel that runs: the library's default is the lane-per-state one at 16, 32 and 64
-    # states (every workload here is within its offset limits); with the zero-order hold the
-    # segment-tiled one, recomputing the states
-    bwd_kname = bwd_kernel or ("lanes" if w.dstate in (16, 32, 64) and not args.zoh else "tiled")
-    if args.zoh and (args.checkpoints or bwd_kname != "tiled"):
-        raise SystemExit("--backward --zoh runs the segment-tiled kernel without saved states")
+    # states (every workload here is within its offset limits)
+    bwd_kname = bwd_kernel or ("lanes" if w.dstate in (16, 32, 64) else "tiled")
     ck, fwd_ck = None, None
     if args.checkpoints:
         # the forward that saves the segment states, graph-timed like the forward bench, then
@@ -563,7 +560,8 @@ def backward_bench(args):
         def fwd(_i):
             scan.selective_scan_fn(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
                                    delta_bias=g["delta_bias"], delta_softplus=w.softplus,
-                                   return_last_state=True, out=y, last_state_out=ls, checkpoints_out=ck)
+                                   return_last_state=True, out=y, last_state_out=ls, checkpoints_out=ck,
+                                   zoh_b=args.zoh)
 
         fwd_us = graph_timed(fwd, 50, 5, torch.cuda.current_stream(dev), reps=7, warm_reps=3)
         fwd(0)
@@ -654,7 +652,9 @@ def backward_bench(args):
                    "seq_len": w.seqlen, "storage": w.dtype, "kernel": bwd_kname, "zoh_b": bool(args.zoh)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": read + written,
-                     "traffic": measured_bwd_traffic(w, ck is not None, "tiled-zoh" if args.zoh else bwd_kname),
+                     "traffic": (measured_bwd_traffic(w, ck is not None, "tiled-zoh")
+                                 if args.zoh and bwd_kname == "tiled" else
+                                 None if args.zoh else measured_bwd_traffic(w, ck is not None, bwd_kname)),
                      "mean_call_us": round(mean_us, 2), "min_call_us": round(float(per_us.min()), 2),
                      "valu_issue_slots": {"per_call": bwd_slots, "slot_equivalent_TFLOP_s": round(bwd_tflops, 2),
                                           "peak_TFLOP_s": VALU_PEAK_TFLOPS,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 14
+#define MAMBA_SCAN_ABI_VERSION 15
 
 /* Storage dtype of u, delta, z, B, C. Arithmetic is fp32 in every case. */
 typedef enum mamba_scan_dtype {
@@ -75,8 +75,8 @@ typedef enum mamba_scan_dtype {
  * flag), and mamba_scan_bwd, given them as `checkpoints`, skips recomputing them. The
  * lane-per-state kernels (dstate 16, 32 or 64) and, from ABI 10, the chunked kernel (dstate 16:
  * the default where it is the default without the flag; its states come from its combine, so they
- * agree with the sequential recurrence's to rounding); no ZOH_B: MAMBA_SCAN_ERR_UNSUPPORTED
- * otherwise. ABI version 6. */
+ * agree with the sequential recurrence's to rounding; not with ZOH_B); with ZOH_B the
+ * lane-per-state kernels (ABI 15); MAMBA_SCAN_ERR_UNSUPPORTED otherwise. ABI version 6. */
 #define MAMBA_SCAN_SAVE_CHECKPOINTS (1u << 3)
 /* Kernel selection, for testing and tuning; at most one of these bits (MAMBA_SCAN_ERR_ARGS
  * otherwise). Default (none): with 16 states, the short-call kernel for at most 4 steps and the
@@ -216,9 +216,9 @@ int64_t mamba_scan_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dtype d
  *  - Flags: MAMBA_SCAN_DELTA_SOFTPLUS, MAMBA_SCAN_ZOH_B (ABI 14: the gradients of the forward
  *    with zero-order-hold B, where the input term's coefficient c = (exp(dt*A) - 1) / A replaces
  *    dt in dB and du, its derivative exp(dt*A) enters ddelta, and dA gains
- *    sum lam*B*u*dc/dA; run by the segment-tiled kernel, which recomputes the states: with
- *    `checkpoints` or MAMBA_SCAN_FORCE_LANES, MAMBA_SCAN_ERR_UNSUPPORTED), and at most one of
- *    the kernel choices (ABI 8; MAMBA_SCAN_ERR_ARGS for both or any other flag):
+ *    sum lam*B*u*dc/dA; the segment-tiled kernel from ABI 14, the lane-per-state one and
+ *    `checkpoints` saved by a zero-order-hold forward from ABI 15), and at most one of the
+ *    kernel choices (ABI 8; MAMBA_SCAN_ERR_ARGS for both or any other flag):
  *      MAMBA_SCAN_FORCE_LANES: the lane-per-state backward, one lane per (channel, state) as in
  *        the forward lane-per-state kernel, 16-step segments walked in reverse from the states
  *        saved every 16 steps (given, or written first by the forward launch that a call with

@@ -41,6 +41,8 @@ int launch_bwd_tiled_zoh_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shap
                              hipStream_t stream);
 int launch_bwd_ls_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
                       hipStream_t stream);
+int launch_bwd_ls_zoh_any(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool bf16, bool softplus,
+                          hipStream_t stream);
 int launch_bwd_reduce_any(const BwdReduceParams& r, hipStream_t stream);
 // dst[i] = src ? src[i] : 0 for i < n, contiguous fp32 (the gradients of empty backward calls)
 int launch_bwd_fill(float* dst, const float* src, int64_t n, hipStream_t stream);

@@ -340,11 +340,8 @@ int64_t mamba_scan_bwd_workspace_bytes(const mamba_scan_shape* s, mamba_scan_dty
     if (bad_shape(*s)) return MAMBA_SCAN_ERR_SHAPE;
     if (s->dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_DSTATE;
     if ((flags & MAMBA_SCAN_FORCE_LANES) && (flags & MAMBA_SCAN_FORCE_TILED)) return MAMBA_SCAN_ERR_ARGS;
-    // zero-order hold: the segment-tiled kernel, recomputing the states (no forward saves them)
-    if ((flags & MAMBA_SCAN_ZOH_B) && (flags & MAMBA_SCAN_SAVE_CHECKPOINTS)) return MAMBA_SCAN_ERR_UNSUPPORTED;
     if (s->batch * s->dim * s->len == 0) return 0;  // an empty call runs no scan
-    if ((flags & MAMBA_SCAN_ZOH_B) && (flags & MAMBA_SCAN_FORCE_LANES)) return MAMBA_SCAN_ERR_UNSUPPORTED;
-    const int pick = (flags & MAMBA_SCAN_ZOH_B) ? 0 : bwd_pick(*s, dtype == MAMBA_SCAN_BF16 ? 2 : 4, flags);
+    const int pick = bwd_pick(*s, dtype == MAMBA_SCAN_BF16 ? 2 : 4, flags);
     if (pick < 0) return pick;
     const bool given_ck = (flags & MAMBA_SCAN_SAVE_CHECKPOINTS) != 0;
     return pick ? bwd_ls_layout(*s, given_ck).total : bwd_layout(*s, given_ck).total;
@@ -398,8 +395,7 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
     if (reinterpret_cast<uintptr_t>(p->workspace) % 256 != 0) return MAMBA_SCAN_ERR_ARGS;
     if (reinterpret_cast<uintptr_t>(p->checkpoints) % 4 != 0) return MAMBA_SCAN_ERR_ARGS;
     const int64_t es = dtype == MAMBA_SCAN_BF16 ? 2 : 4;
-    // (an error was returned by the size query)
-    const bool lanes = !(flags & MAMBA_SCAN_ZOH_B) && bwd_pick(*s, es, flags) == 1;
+    const bool lanes = bwd_pick(*s, es, flags) == 1;  // an error was returned by the size query
     if (!lanes && s->batch * ((s->dim + 63) / 64) > 0x7fffffff) return MAMBA_SCAN_ERR_UNSUPPORTED;
 
     const int64_t DL = s->batch * s->dim * s->len, NL = s->batch * s->dstate * s->len;
@@ -443,7 +439,9 @@ int backward_entry(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape* s, mamb
         return rc;
     }
     const bool sp = (flags & MAMBA_SCAN_DELTA_SOFTPLUS) != 0;
-    if (flags & MAMBA_SCAN_ZOH_B) return launch_bwd_tiled_zoh_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
+    if (flags & MAMBA_SCAN_ZOH_B)
+        return lanes ? launch_bwd_ls_zoh_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs)
+                     : launch_bwd_tiled_zoh_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
     return lanes ? launch_bwd_ls_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs)
                  : launch_bwd_tiled_any(p, *s, dtype == MAMBA_SCAN_BF16, sp, hs);
 }

@@ -41,6 +41,21 @@
 
 namespace mscan {
 
+// Derivative in A of the zero-order-hold coefficient c = (e^{dt A} - 1) / A, from x = dt A,
+// dA = e^x, c (zoh_coef2_f) and ia = 1 / A (0 where A = 0): (dt dA - c) / A, limit dt^2 / 2 at
+// A = 0. Below |x| = 1/4 the Taylor series dt^2 (1/2 + x/3 + x^2/8 + x^3/30 + x^4/144 + x^5/840)
+// (first dropped term under 1e-7 of the sum), above it the closed form (cancellation at most
+// 2/|x| = 8).
+__device__ __forceinline__ float zoh_coef_dA_x_f(float dt, float x, float dA, float c, float ia) {
+    const float p = __builtin_fmaf(
+        x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 840.0f, 1.0f / 144.0f), 1.0f / 30.0f), 0.125f),
+                          1.0f / 3.0f),
+        0.5f);
+    const float small = dt * dt * p;
+    const float big = __builtin_fmaf(dt, dA, -c) * ia;
+    return __builtin_fabsf(x) < 0.25f ? small : big;
+}
+
 constexpr int kBlRowP = 20;                  // LDS floats per (channel, state) row of a segment
 constexpr int kBlChanP = 16 * kBlRowP + 16;  // per channel: 16 rows, skewed by 16 banks
 constexpr int kBlArea = 4 * kBlChanP;        // one quantity of a wave's 4 channels
@@ -100,8 +115,15 @@ __device__ __forceinline__ void bl_for(F&& f) {
 // MULTI: one of several blocks of 16 states (32 or 64 states): du, ddelta and, with a gate, the
 // sum over states of C h are read back from the earlier blocks' launches and added to, in block
 // order; the first block adds the skip term, the last one finishes dz. Otherwise the only block.
-template <typename T, int W, bool SOFTPLUS, bool HAS_Z, bool MULTI>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3)))
+// ZOH: B discretised by zero-order hold. The input term is c u B with c = (e^{dt A} - 1) / A
+// (zoh_coef2_f, the forward kernel's arithmetic; the row broadcast carries u): c replaces dt in dB
+// and in the first sum over states (sum lam c B, du), the second becomes sum lam a (h A + B u)
+// (ddt: dc/ddt = a), and dA gains lam B u dc/dA; c is recomputed in the reverse from the decay.
+// With the zero-order hold the segment's coefficients are kept beside its states and decays and
+// the kernel takes 221-250 VGPRs (the Euler one 164): 2 waves per SIMD instead of 3 (under the
+// 168-VGPR cap of 3 about 100 of them spilled to scratch).
+template <typename T, int W, bool SOFTPLUS, bool HAS_Z, bool MULTI, bool ZOH>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(ZOH ? 2 : 3)))
 void scan_bwd_ls_kernel(BlsParams p) {
     __shared__ __align__(16) float s_w[W][2][kBlArea];    // per wave: two quantity areas
     __shared__ __align__(16) float s_bc[2][16 * kBlRowP];  // the segment's B | C: [state][step]
@@ -125,6 +147,7 @@ void scan_bwd_ls_kernel(BlsParams p) {
 
     const float Av = p.A[d * NS + n0 + n];
     const float a2 = Av * kLog2e;
+    const float ia = Av != 0.0f ? 1.0f / Av : 0.0f;  // zero-order hold only
     const float bias = p.bias ? p.bias[d] : 0.0f;
     const float Dv = p.D ? p.D[d] : 0.0f;
     const int64_t si = (b * p.dim + d) * NS + n0 + n;  // this lane's (b, d, state)
@@ -246,7 +269,7 @@ void scan_bwd_ls_kernel(BlsParams p) {
             f.dt = hw_exp2(x * kLog2e);
             f.sg = 0.0f;
         }
-        f.dtu = f.dt * f.uu;
+        f.dtu = ZOH ? f.uu : f.dt * f.uu;
         if constexpr (HAS_Z) {
             const float zz = widen(w.z);
             const float sz = hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
@@ -291,15 +314,23 @@ void scan_bwd_ls_kernel(BlsParams p) {
         }
 
         // forward over the segment from its saved state: hp[j] = state before step j
-        float hp[16], dA[16];
+        float hp[16], dA[16], cfs[ZOH ? 16 : 1];
         float h = cur.h;
         {
             float yv[4];
             bl_for<0, 16>([&](auto jc) __attribute__((always_inline)) {
                 constexpr int j = decltype(jc)::value;
                 hp[j] = h;
-                dA[j] = hw_exp2(row_bcast<j>(dt) * a2);
-                h = __builtin_fmaf(dA[j], h, row_bcast<j>(dtu) * Bv[j]);
+                if constexpr (ZOH) {
+                    const float dtb = row_bcast<j>(dt);
+                    const float x2 = dtb * a2;
+                    dA[j] = hw_exp2(x2);
+                    cfs[j] = zoh_coef2_f(dtb, x2, dA[j], ia);
+                    h = __builtin_fmaf(dA[j], h, cfs[j] * row_bcast<j>(dtu) * Bv[j]);
+                } else {
+                    dA[j] = hw_exp2(row_bcast<j>(dt) * a2);
+                    h = __builtin_fmaf(dA[j], h, row_bcast<j>(dtu) * Bv[j]);
+                }
                 yv[j % 4] = Cv[j] * h;
                 if constexpr (j % 4 == 3)
                     *reinterpret_cast<float4*>(row0p + (j - 3)) = float4{yv[0], yv[1], yv[2], yv[3]};
@@ -320,11 +351,23 @@ void scan_bwd_ls_kernel(BlsParams p) {
                 const float gpb = row_bcast<j>(gp);
                 lam = __builtin_fmaf(gpb, Cv[j], lam);
                 dCp[j] = gpb * hs;
-                dBp[j] = lam * row_bcast<j>(dtu);
-                p1[j % 4] = lam * Bv[j];
-                const float q = lam * dA[j] * hp[j];
-                p2[j % 4] = q * Av;
-                gA = __builtin_fmaf(q, row_bcast<j>(dt), gA);
+                if constexpr (ZOH) {
+                    const float dtb = row_bcast<j>(dt), ub = row_bcast<j>(dtu);
+                    const float cf = cfs[j];
+                    dBp[j] = lam * (cf * ub);
+                    const float lb = lam * Bv[j];
+                    p1[j % 4] = lb * cf;
+                    const float la = lam * dA[j];
+                    p2[j % 4] = la * __builtin_fmaf(hp[j], Av, Bv[j] * ub);
+                    gA = __builtin_fmaf(la * hp[j], dtb, gA);
+                    gA = __builtin_fmaf(lb * ub, zoh_coef_dA_x_f(dtb, dtb * Av, dA[j], cf, ia), gA);
+                } else {
+                    dBp[j] = lam * row_bcast<j>(dtu);
+                    p1[j % 4] = lam * Bv[j];
+                    const float q = lam * dA[j] * hp[j];
+                    p2[j % 4] = q * Av;
+                    gA = __builtin_fmaf(q, row_bcast<j>(dt), gA);
+                }
                 lam *= dA[j];
                 if constexpr (j % 4 == 0) {
                     *reinterpret_cast<float4*>(row0p + j) = float4{p1[0], p1[1], p1[2], p1[3]};
@@ -333,8 +376,8 @@ void scan_bwd_ls_kernel(BlsParams p) {
             });
         }
         __builtin_amdgcn_wave_barrier();
-        const float P1 = col_sum(col0);  // sum_n lam B
-        const float P2 = col_sum(col1);  // sum_n lam a h_{t-1} A
+        const float P1 = col_sum(col0);  // sum_n lam B (zero-order hold: sum_n lam c B)
+        const float P2 = col_sum(col1);  // sum_n lam a h_{t-1} A (zero-order hold: + lam a B u)
         __builtin_amdgcn_wave_barrier();
 
         // dB / dC over the wave's 4 channels (rows), reduce-scattered across the rows: rows r and
@@ -369,9 +412,10 @@ void scan_bwd_ls_kernel(BlsParams p) {
         // finish step n of channel c
         {
             const float uu = cur.uu;
-            const float gdt = __builtin_fmaf(uu, P1, P2);
+            const float gdt = ZOH ? P2 : __builtin_fmaf(uu, P1, P2);
+            const float gin = ZOH ? P1 : dt * P1;  // the input term's share of du
             float gx = SOFTPLUS ? gdt * cur.sg : gdt * dt;
-            float gu = first ? __builtin_fmaf(gp, Dv, dt * P1) : dt * P1 + cur.pu;
+            float gu = first ? __builtin_fmaf(gp, Dv, gin) : gin + cur.pu;
             float ys = Ys;
             if constexpr (MULTI) {
                 if (!first) {
@@ -558,7 +602,7 @@ __global__ __launch_bounds__(64) void scan_bwd_ls_carry_kernel(BlsParams p) {
 // ---------------------------------------------------------------------------------------------
 // host side
 
-template <typename T, bool SP, bool HZ>
+template <typename T, bool SP, bool HZ, bool ZOH>
 int launch_bwd_ls_cfg(const BlsParams& q, hipStream_t stream) {
     void* args[] = {const_cast<BlsParams*>(&q)};
     if (q.parts > 1) {
@@ -570,15 +614,15 @@ int launch_bwd_ls_cfg(const BlsParams& q, hipStream_t stream) {
             hipSuccess)
             return MAMBA_SCAN_ERR_LAUNCH;
     }
-    const void* fn = q.N > 16 ? reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ, true>)
-                              : reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ, false>);
+    const void* fn = q.N > 16 ? reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ, true, ZOH>)
+                              : reinterpret_cast<const void*>(&scan_bwd_ls_kernel<T, kBlsW, SP, HZ, false, ZOH>);
     return hipLaunchKernel(fn, dim3((unsigned)(q.parts * q.batch * q.groups)), dim3(64 * kBlsW), args, 0, stream) ==
                    hipSuccess
                ? MAMBA_SCAN_OK
                : MAMBA_SCAN_ERR_LAUNCH;
 }
 
-template <typename T>
+template <typename T, bool ZOH>
 int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool softplus, hipStream_t stream) {
     if (!bwd_ls_fits(s, sizeof(T))) return MAMBA_SCAN_ERR_UNSUPPORTED;
     const bool given = p->checkpoints != nullptr;
@@ -615,7 +659,7 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
         f.sA_d = N;
         f.sD = f.sbias = 1;
         f.softplus = softplus ? 1 : 0;
-        f.zoh_b = 0;
+        f.zoh_b = ZOH ? 1 : 0;
         f.ck = ck;
         f.ck_nseg = l.nseg;
         const int rc = launch_fwd_checkpoints(f, sizeof(T) == 2, stream);
@@ -659,8 +703,10 @@ int launch_bwd_ls(const mamba_scan_bwd_ptrs* p, const mamba_scan_shape& s, bool 
         q.n0 = n0;
         q.first = n0 == 0;
         q.last = n0 + 16 == N;
-        const int rc = softplus ? (hz ? launch_bwd_ls_cfg<T, true, true>(q, stream) : launch_bwd_ls_cfg<T, true, false>(q, stream))
-                                : (hz ? launch_bwd_ls_cfg<T, false, true>(q, stream) : launch_bwd_ls_cfg<T, false, false>(q, stream));
+        const int rc = softplus ? (hz ? launch_bwd_ls_cfg<T, true, true, ZOH>(q, stream)
+                                      : launch_bwd_ls_cfg<T, true, false, ZOH>(q, stream))
+                                : (hz ? launch_bwd_ls_cfg<T, false, true, ZOH>(q, stream)
+                                      : launch_bwd_ls_cfg<T, false, false, ZOH>(q, stream));
         if (rc != MAMBA_SCAN_OK) return rc;
     }
     BwdReduceParams r;

@@ -612,11 +612,10 @@ void scan_ls_wide_kernel(ScanParams p) {
 // ---------------------------------------------------------------------------------------------
 // host side
 
-// The lane-per-state kernels take dstate 16, 32 or 64 (the zero-order hold without saved states,
-// which only the Euler backward reads), and shapes whose byte offsets within a wave's rows (u,
-// delta, z, y) and within a batch's B / C fit 31 bits.
+// The lane-per-state kernels take dstate 16, 32 or 64, and shapes whose byte offsets within a
+// wave's rows (u, delta, z, y) and within a batch's B / C fit 31 bits.
 inline bool ls_eligible(const ScanParams& q, int64_t es) {
-    if ((q.dstate != 16 && q.dstate != 32 && q.dstate != 64) || (q.zoh_b && q.ck)) return false;
+    if (q.dstate != 16 && q.dstate != 32 && q.dstate != 64) return false;
     const int64_t lim = (int64_t)1 << 31;
     const auto rows_ok = [&](const void* ptr, int64_t sd, int64_t e) {
         return ptr == nullptr || (3 * sd + q.len) * e < lim;
@@ -648,8 +647,10 @@ int launch_ls_cfg(const ScanParams& q, hipStream_t stream) {
 template <typename T, bool SP, bool HZ, bool VEC>
 int launch_ls_ck(const ScanParams& q, hipStream_t stream) {
     // saving the segment states is a separate instantiation: the plain forward issues no stores
-    // for it; so is the zero-order hold (never with saved states)
-    if (q.zoh_b) return launch_ls_cfg<T, SP, HZ, VEC, false, true>(q, stream);
+    // for it; so is the zero-order hold
+    if (q.zoh_b)
+        return q.ck ? launch_ls_cfg<T, SP, HZ, VEC, true, true>(q, stream)
+                    : launch_ls_cfg<T, SP, HZ, VEC, false, true>(q, stream);
     return q.ck ? launch_ls_cfg<T, SP, HZ, VEC, true, false>(q, stream)
                 : launch_ls_cfg<T, SP, HZ, VEC, false, false>(q, stream);
 }

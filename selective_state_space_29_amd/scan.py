@@ -310,8 +310,8 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     workspace is allocated here; calls overlapping in time on one GPU must not be made).
     ``kernel``: None (the library's choice: the lane-per-state kernel at 16, 32 and 64 states,
     else the segment-tiled one), "lanes" or "tiled" (forced; an error where it cannot run).
-    ``zoh_b``: the gradients of the forward with B discretised by zero-order hold (the
-    segment-tiled kernel, recomputing the states: no ``checkpoints``, no ``kernel="lanes"``).
+    ``zoh_b``: the gradients of the forward with B discretised by zero-order hold (either
+    kernel; ``checkpoints`` then come from a zero-order-hold forward).
     """
     lib = load_library()
     if u.dtype not in (torch.float32, torch.bfloat16):
@@ -398,8 +398,7 @@ class SelectiveScan(torch.autograd.Function):
         kw = dict(D=D, z=z, delta_bias=delta_bias, delta_softplus=delta_softplus, return_last_state=True, h0=h0,
                   zoh_b=zoh_b)
         ck = None
-        # the zero-order-hold backward recomputes the states: none are saved for it
-        if not zoh_b and A.shape[1] in (16, 32, 64) and u.dtype in (torch.float32, torch.bfloat16):
+        if A.shape[1] in (16, 32, 64) and u.dtype in (torch.float32, torch.bfloat16):
             ck = torch.empty(checkpoint_shape(*u.shape, A.shape[1]), dtype=torch.float32, device=u.device)
             try:
                 y, ls = selective_scan_fn(u, delta, A, B, C, checkpoints_out=ck, **kw)

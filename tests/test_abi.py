@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(scan.LIB_PATH)
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert scan.load_library().mamba_scan_abi_version() == 14
+    assert scan.load_library().mamba_scan_abi_version() == 15
 
 
 def fake_call(mutate=None, flags=scan.DELTA_SOFTPLUS, dtype=scan.BF16, shape=(2, 3, 40, 16),
@@ -147,7 +147,7 @@ CASES = [
     ("checkpoints_with_tiled", lambda c: _ck_ws(c, 1 << 20, extra=scan.FORCE_TILED), -8),
     ("checkpoints_with_generic", lambda c: _ck_ws(c, 1 << 20, extra=scan.FORCE_GENERIC), -8),
     ("checkpoints_24_states", lambda c: (_ck_ws(c, 1 << 20), setattr(c["shape"], "dstate", 24)), -8),
-    ("checkpoints_with_zoh", lambda c: _ck_ws(c, 1 << 20, extra=scan.ZOH_B), -8),
+    ("checkpoints_with_zoh_chunked", lambda c: _ck_ws(c, 1 << 20, extra=scan.ZOH_B | scan.FORCE_CHUNKED), -8),
     ("checkpoints_alias_y", lambda c: (_ck_ws(c, 1 << 20), setattr(c["ptrs"], "workspace", c["ptrs"].y)), -6),
     # with SAVE_CHECKPOINTS the workspace is an output: it may not overlap an input either
     ("checkpoints_alias_u", lambda c: (_ck_ws(c, 1 << 20), setattr(c["ptrs"], "workspace", c["ptrs"].u + 8)), -6),
@@ -274,10 +274,6 @@ BWD_CASES = [
     ("both_kernels_forced", lambda c: c.__setitem__("flags", scan.FORCE_TILED | scan.FORCE_LANES), -6),
     ("lanes_forced_at_8_states",
      lambda c: (c.__setitem__("flags", scan.FORCE_LANES), setattr(c["shape"], "dstate", 8)), -8),
-    # zero-order hold: the segment-tiled kernel only, which recomputes the states
-    ("zoh_with_checkpoints", lambda c: c.__setitem__("flags", scan.DELTA_SOFTPLUS | scan.ZOH_B), -8),
-    ("zoh_with_lanes_forced", lambda c: (c.__setitem__("flags", scan.ZOH_B | scan.FORCE_LANES),
-                                         setattr(c["ptrs"], "checkpoints", None)), -8),
     ("zoh_unknown_flag", lambda c: (c.__setitem__("flags", scan.ZOH_B | (1 << 13)),
                                     setattr(c["ptrs"], "checkpoints", None)), -6),
     ("bad_dtype", lambda c: c.__setitem__("dtype", 7), -4),

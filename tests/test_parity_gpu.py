@@ -43,7 +43,7 @@ def tol_for(dtype):
 def test_library_is_the_in_tree_build():
     lib = scan.load_library()
     assert os.path.dirname(scan.LIB_PATH).endswith("selective_state_space_29_amd")
-    assert lib.mamba_scan_abi_version() == 14
+    assert lib.mamba_scan_abi_version() == 15
     maps = open("/proc/self/maps").read()
     assert scan.LIB_PATH in maps
 

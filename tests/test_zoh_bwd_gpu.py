@@ -1,6 +1,7 @@
 """GPU parity of the backward pass with zero-order-hold B (``mamba_scan_bwd`` with
-MAMBA_SCAN_ZOH_B, the segment-tiled kernel) against the fp64 backward oracle with ``zoh_b=True``
-on identical inputs.
+MAMBA_SCAN_ZOH_B, on the lane-per-state and segment-tiled kernels, recomputing the states or from
+a zero-order-hold forward's saved states) against the fp64 backward oracle with ``zoh_b=True`` on
+identical inputs.
 
 Bars as for the Euler backward: max|g - r| / (1 + |r|) <= 1e-4 for fp32 inputs, <= 2e-3 for
 bf16 inputs. The coefficient c = (e^{dt A} - 1) / A is within 2^-20 relative of the exact one
@@ -58,7 +59,8 @@ def _check(x, tol, softplus=True, with_h0=False, with_dlast=True, seed=0, kernel
 
 @pytest.mark.parametrize("wid", [1, 2, 3])
 def test_zoh_backward_workload_parity(wid):
-    """Workloads 1-3 in full (workload 1: 32 states, two blocks of 16)."""
+    """Workloads 1-3 in full on the default kernel (the lane-per-state one: workload 1 has 32
+    states, two blocks of 16)."""
     w = workloads.WORKLOADS[wid]
     print(f"zoh backward parity, workload {wid}: {w.name}", flush=True)
     _check(workloads.make_inputs(w), 1e-4 if w.dtype == "f32" else 2e-3, softplus=w.softplus,
@@ -120,18 +122,62 @@ def test_zoh_backward_edge_cases(idx):
            kernel="tiled" if idx % 2 else None)
 
 
-def test_zoh_backward_refusals():
-    """The lane-per-state backward does not take the zero-order hold, nor do saved states."""
-    x = gu.case(830, 1, 16, 16, 32, dtype="f32")
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_zoh_backward_workload_parity_segment_tiled(wid):
+    """The segment-tiled kernel forced (the default at 16, 32 and 64 states is the lane-per-state
+    one)."""
+    w = workloads.WORKLOADS[wid]
+    print(f"zoh backward parity, workload {wid}: {w.name}, segment-tiled", flush=True)
+    _check(workloads.make_inputs(w), 1e-4 if w.dtype == "f32" else 2e-3, softplus=w.softplus,
+           with_dlast=w.last_state, seed=wid, kernel="tiled")
+
+
+LANES = [
+    # (batch, dim, N, L, dtype, a_kind, h0): the lane-per-state kernel forced; L across segment
+    # boundaries, dim leaving waves and workgroups partly empty, 32 / 64 states in blocks of 16
+    (2, 37, 16, 45, "bf16", "rand", True),
+    (1, 70, 16, 40, "f32", "zeros_mixed", False),
+    (2, 64, 16, 100, "f32", "tiny", True),
+    (1, 50, 32, 33, "bf16", "straddle", False),
+    (2, 19, 32, 70, "f32", "positive", True),
+    (1, 33, 64, 50, "f32", "rand", True),
+    (1, 16, 16, 1, "f32", "straddle", False),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(LANES)))
+def test_zoh_backward_lanes(idx):
+    batch, dim, N, L, dtype, a_kind, with_h0 = LANES[idx]
+    print(f"zoh backward, lane-per-state kernel: {LANES[idx]}", flush=True)
+    rng = np.random.default_rng(860 + idx)
+    x = gu.case(860 + idx, batch, dim, N, L, dtype=dtype, a_kind="rand")
+    x["A"] = _a(a_kind, dim, N, rng) if a_kind != "rand" else x["A"]
+    _check(x, 1e-4 if dtype == "f32" else 2e-3, with_h0=with_h0, seed=idx, kernel="lanes")
+
+
+@pytest.mark.parametrize("kernel,N", [("lanes", 16), ("lanes", 64), ("tiled", 16), ("tiled", 32)])
+def test_zoh_backward_from_saved_states(kernel, N):
+    """The zero-order-hold forward saving its segment states (lane-per-state kernel), then the
+    backward from them: the lane-per-state backward's gradients are its recomputing run's bits
+    (the recompute writes them with the same forward kernel); the segment-tiled one's agree to
+    rounding (it recomputes with the tiled kernel's arithmetic) and both meet the oracle's bar."""
+    x = gu.case(880 + N, 2, 80, N, 150, dtype="bf16", a_kind="rand")
     g = {k: gu.to_dev(v) if isinstance(v, np.ndarray) else v for k, v in x.items()}
-    dy = torch.ones((1, 16, 32), device="cuda:0")
-    with pytest.raises(ValueError):
-        scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"], z=g["z"],
-                                delta_bias=g["delta_bias"], delta_softplus=True, kernel="lanes", zoh_b=True)
-    ck = torch.zeros(scan.checkpoint_shape(1, 16, 32, 16), dtype=torch.float32, device="cuda:0")
-    with pytest.raises(ValueError):
-        scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"], z=g["z"],
-                                delta_bias=g["delta_bias"], delta_softplus=True, checkpoints=ck, zoh_b=True)
+    ck = torch.empty(scan.checkpoint_shape(2, 80, 150, N), dtype=torch.float32, device="cuda:0")
+    scan.selective_scan_fn(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                           delta_bias=g["delta_bias"], delta_softplus=True, checkpoints_out=ck, zoh_b=True)
+    rng = np.random.default_rng(N)
+    dy = torch.from_numpy(rng.standard_normal((2, 80, 150)).astype(np.float32)).to("cuda:0")
+    kw = dict(D=g["D"], z=g["z"], delta_bias=g["delta_bias"], delta_softplus=True, kernel=kernel, zoh_b=True)
+    a = scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, checkpoints=ck, **kw)
+    b = scan.selective_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, **kw)
+    torch.cuda.synchronize()
+    r = oracle.selective_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy.cpu().numpy().astype(np.float64),
+                                  D=x["D"], z=x["z"], delta_bias=x["delta_bias"], delta_softplus=True, zoh_b=True)
+    for k in ("u", "delta", "z", "B", "C", "A", "D", "delta_bias"):
+        if kernel == "lanes":
+            assert torch.equal(a[k], b[k]), k
+        assert gu.rel_err(a[k].cpu().numpy(), r[k]) <= 2e-3, k
 
 
 def test_zoh_backward_is_deterministic():
